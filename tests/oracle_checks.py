@@ -1,0 +1,326 @@
+"""Pins of the fp64 oracle to facts fixed independently of it.
+
+Each check raises AssertionError on failure.  They are run against the real
+oracle (tests/test_oracle_pins.py) and against copies of oracle.c with planted
+mistakes (tests/test_oracle_mutants.py), where at least one must fail.
+
+Independent references used here: scipy's ndtri (Cephes algorithm, not
+AS 241) and Python's NormalDist for the quantile; numpy mean/std/matmul/
+argsort; torch fp64 gelu(tanh), softmax and softplus; scipy's Student-t
+survival function; closed forms (quantile grid, power-of-two scaling,
+constant rows); and the O(sqrt(log d / d)) count concentration the pages state
+for Gaussian scores.
+"""
+from __future__ import annotations
+
+import math
+import os
+from statistics import NormalDist
+
+import numpy as np
+import torch
+from scipy import stats
+from scipy.special import ndtri
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+def np_stat_topk(x: np.ndarray, k: int):
+    """Statistical top-k of one row with numpy's population mean/std and scipy's ndtri."""
+    x = np.asarray(x, np.float64)
+    th = x.mean() + x.std() * ndtri(1.0 - k / x.size)
+    return th, np.nonzero(x > th)[0]
+
+
+def gelu_t(v: np.ndarray) -> np.ndarray:
+    return torch.nn.functional.gelu(torch.from_numpy(np.asarray(v, np.float64)), approximate="tanh").numpy()
+
+
+def softplus_t(v: np.ndarray) -> np.ndarray:
+    return torch.nn.functional.softplus(torch.from_numpy(np.asarray(v, np.float64))).numpy()
+
+
+def dense_masked_ffn(q, k1t, k2t, v, r, k):
+    """The Spark FFN written densely: every neuron is computed and the
+    unselected ones are multiplied by GELU(0) = 0.  No index list, no gather."""
+    q = np.asarray(q, np.float64)
+    W1, W2, V = (np.asarray(a, np.float64) for a in (k1t, k2t, v))
+    h = W1 @ q[:r]
+    th, S = np_stat_topk(h, k)
+    a = gelu_t(np.maximum(h - th, 0.0))
+    g = W2 @ q[r:]
+    return V.T @ (a * g), h, th, S
+
+
+def rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# ---------------------------------------------------------------- P1 quantile
+def check_quantile():
+    ps = np.concatenate([np.linspace(1e-6, 1 - 1e-6, 1001), np.logspace(-300, -1, 61),
+                         1 - np.logspace(-15, -1, 29), [0.5, 0.425, 0.075, 0.925, 1 - 737 / 9216]])
+    nd = NormalDist()
+    for p in ps:
+        a, b = oracle.norm_quantile(p), float(ndtri(p))
+        assert abs(a - b) <= 4e-15 * max(1.0, abs(b)), (p, a, b)
+        if 1e-300 < p < 1 - 1e-15:
+            c = nd.inv_cdf(p)
+            assert abs(a - c) <= 4e-15 * max(1.0, abs(c)), (p, a, c)
+    assert oracle.norm_quantile(0.5) == 0.0
+    for d, k in [(9216, 737), (1024, 82), (4096, 256), (32768, 256)]:
+        assert abs(oracle.threshold_z(k, d) - ndtri(1 - k / d)) < 4e-15
+
+
+# ---------------------------------------------------------------- P2 closed form
+def check_threshold_closed_form():
+    g = np.random.default_rng(7)
+    x = (g.standard_normal((32, 777)) * g.uniform(0.1, 3, (32, 1)) + g.uniform(-2, 2, (32, 1))).astype(np.float32)
+    for k in (1, 62, 388, 700, 776):
+        res = oracle.stat_topk(x, k)
+        xd = x.astype(np.float64)
+        mu, sd = xd.mean(axis=1), xd.std(axis=1)
+        assert np.allclose(res["mean"], mu, rtol=1e-13, atol=1e-13)
+        assert np.allclose(res["std"], sd, rtol=1e-13, atol=0)
+        th = mu + sd * ndtri(1 - k / 777)
+        assert np.allclose(res["theta"], th, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- P3 / R9 special cases
+def check_special_rows():
+    g = np.random.default_rng(3)
+    x = g.standard_normal((8, 1000)).astype(np.float32)
+    res = oracle.stat_topk(x, 500)  # k = d/2: z = 0, theta = mean
+    assert np.array_equal(res["theta"], res["mean"])
+    for i in range(8):
+        assert res["counts"][i] == int((x[i].astype(np.float64) > res["mean"][i]).sum())
+    c = np.full((3, 64), 0.75, np.float32)  # constant row: std 0, theta = mean, nothing strictly above
+    res = oracle.stat_topk(c, 5)
+    assert np.all(res["counts"] == 0) and np.all(res["theta"] == 0.75)
+
+
+# ---------------------------------------------------------------- P4 worked example (golden)
+def check_quantile_grid():
+    rows = [list(map(int, l.split())) for l in open(os.path.join(GOLDEN, "quantile_grid.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) >= 4
+    for d, k, expected in rows:
+        x = ndtri((np.arange(d) + 0.5) / d).astype(np.float32)
+        res = oracle.stat_topk(x[None, :], k)
+        n = int(res["counts"][0])
+        assert n == expected, (d, k, n)
+        assert np.array_equal(res["idx"][0, :n], np.arange(d - k, d))
+        gap = np.min(np.abs(x.astype(np.float64) - res["theta"][0])) / res["std"][0]
+        assert gap > 1e-4, (d, k, gap)
+
+
+# ---------------------------------------------------------------- P5 invariants
+def check_invariants():
+    x = synth.stat_rows(11, 64, 2000)
+    k = 160
+    res = oracle.stat_topk(x, k, cap=2000)
+    for i in range(x.shape[0]):
+        xd = x[i].astype(np.float64)
+        n = int(res["counts"][i])
+        S = res["idx"][i, :n]
+        th = res["theta"][i]
+        assert n == int((xd > th).sum())
+        assert np.all(np.diff(S) > 0)
+        assert np.array_equal(res["vals"][i, :n], xd[S] - th)
+        assert np.all(res["vals"][i, :n] > 0)
+        mask = np.zeros(xd.size, bool)
+        mask[S] = True
+        assert xd[mask].min() > th >= xd[~mask].max()
+    # capacity: the first cap entries of the same ascending list, true count kept
+    res2 = oracle.stat_topk(x, k, cap=50)
+    assert np.array_equal(res2["counts"], res["counts"])
+    assert np.array_equal(res2["idx"], res["idx"][:, :50])
+
+
+# ---------------------------------------------------------------- P6 scale invariance
+def check_scale_invariance():
+    x = synth.stat_rows(5, 16, 3000)
+    a = oracle.stat_topk(x, 240)
+    for j in (-3, 5):
+        b = oracle.stat_topk(x * np.float32(2.0 ** j), 240)
+        assert np.array_equal(a["counts"], b["counts"]) and np.array_equal(a["idx"], b["idx"])
+        assert np.array_equal(a["theta"] * 2.0 ** j, b["theta"])
+        assert np.array_equal(a["vals"] * 2.0 ** j, b["vals"])
+
+
+# ---------------------------------------------------------------- P7 Theorem 3.1
+def check_theorem31(rows: int = 256):
+    for d, k in [(9216, 737), (1024, 82)]:
+        x = synth.stat_rows(17, rows, d, "gauss")
+        c = oracle.stat_topk(x, k, cap=1)["counts"].astype(np.float64)
+        bound = math.sqrt(math.log(d) / d)
+        assert np.all(np.abs(c - k) / d <= bound), (d, k, c.min(), c.max())
+        # binomial-like spread around k: the mean sits within 5 standard errors
+        se = math.sqrt(d * (k / d) * (1 - k / d)) / math.sqrt(rows)
+        assert abs(c.mean() - k) <= 5 * se + 0.5, (d, k, c.mean(), se)
+
+
+# ---------------------------------------------------------------- P8 Student-t rows
+def check_student_t(rows: int = 1500):
+    d, k = 9216, 737
+    x = synth.stat_rows(19, rows, d, "t4")
+    c = oracle.stat_topk(x, k, cap=1)["counts"].astype(np.float64)
+    z = ndtri(1 - k / d)
+    expected = d * stats.t.sf(math.sqrt(2.0) * z, 4)  # population std of t(4) is sqrt(2)
+    assert abs(c.mean() - expected) <= 10.0, (c.mean(), expected)
+
+
+# ---------------------------------------------------------------- P9 sparse == dense-masked
+FFN_SHAPES = [(16, 64, 8, 6), (24, 40, 12, 3), (32, 96, 20, 9), (256, 1024, 128, 82)]
+
+
+def check_ffn_dense_masked(shapes=FFN_SHAPES, seeds=(0, 1, 2)):
+    for (dm, dff, r, k) in shapes:
+        for s in seeds:
+            k1t, k2t, v = synth.ffn_layer(s, 0, dm, dff, r, "f32")
+            q = synth.queries(s, 3, dm)
+            res = oracle.spark_ffn(q, k1t, k2t, v, r, k)
+            for t in range(3):
+                y, h, th, S = dense_masked_ffn(q[t], k1t, k2t, v, r, k)
+                n = int(res["counts"][t])
+                assert n == S.size and np.array_equal(res["idx"][t, :n], S), (dm, dff, s, t)
+                assert rel(res["h"][t], h) < 1e-13
+                assert abs(res["theta"][t] - th) <= 1e-13 * (1 + abs(th))
+                assert np.allclose(res["m"][t, :n], h[S] - th, rtol=1e-12, atol=1e-13)
+                assert rel(res["y"][t], y) < 1e-12, (dm, dff, s, t, rel(res["y"][t], y))
+
+
+def check_ffn_bf16_widening():
+    dm, dff, r, k = 48, 128, 16, 10
+    k1t, k2t, v = synth.ffn_layer(4, 0, dm, dff, r, "bf16")
+    qb = synth.queries(4, 2, dm, "bf16")
+    a = oracle.spark_ffn(qb, k1t, k2t, v, r, k)
+    w = synth.bf16_bits_to_f32
+    b = oracle.spark_ffn(w(qb), w(k1t), w(k2t), w(v), r, k)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["counts"], b["counts"])
+    # and the widened values drive the same result as the dense numpy form
+    y, _, _, _ = dense_masked_ffn(w(qb)[0], w(k1t), w(k2t), w(v), r, k)
+    assert rel(a["y"][0], y) < 1e-12
+
+
+# ---------------------------------------------------------------- P10 "top-k" = largest
+def check_topk_is_largest():
+    x = synth.stat_rows(23, 32, 4096)
+    res = oracle.stat_topk(x, 300)
+    for i in range(32):
+        n = int(res["counts"][i])
+        top = np.sort(np.argsort(-x[i].astype(np.float64), kind="stable")[:n])
+        assert np.array_equal(res["idx"][i, :n], top)
+
+
+# ---------------------------------------------------------------- P11 GELU / softplus
+def check_activations():
+    pts = np.array([0.0, 1e-8, 0.1, 0.5, 1.0, 1.4, 2.0, 3.7, 8.0, -0.5, -2.0, -6.0])
+    gt = gelu_t(pts)
+    for p, e in zip(pts, gt):
+        assert abs(oracle.gelu_tanh(p) - e) <= 4e-16 * max(1.0, abs(e)), (p, oracle.gelu_tanh(p), e)
+    assert oracle.gelu_tanh(0.0) == 0.0
+    sp_pts = np.array([-60.0, -5.0, -0.3, 0.0, 0.3, 5.0, 60.0, 700.0])
+    for p in sp_pts:
+        e = float(np.logaddexp(0.0, p))
+        assert abs(oracle.softplus(p) - e) <= 4e-16 * max(1.0, abs(e)), (p, oracle.softplus(p), e)
+    assert np.allclose([oracle.softplus(p) for p in sp_pts], softplus_t(sp_pts), rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------- P12 attention
+def _attn_ref(q, k1, k2, v, k_attn, sigma2=True):
+    """Masked softmax attention written with torch fp64 (dense over all tokens, mask from numpy stat top-k)."""
+    Hq, hd = q.shape
+    Hkv, n, r = k1.shape
+    grp = Hq // Hkv
+    out = np.zeros((Hq, hd))
+    cnt = np.zeros(Hq, int)
+    for h in range(Hq):
+        g = h // grp
+        s = k1[g] @ q[h, :r]
+        S = np.arange(n) if n <= k_attn else np_stat_topk(s, k_attn)[1]
+        cnt[h] = S.size
+        mask = torch.full((n,), -math.inf, dtype=torch.float64)
+        mask[torch.from_numpy(S)] = 0.0
+        w = torch.softmax(torch.from_numpy(s) + mask, dim=0).numpy()
+        u = softplus_t(k2[g] @ q[h, r:]) if sigma2 else np.ones(n)
+        out[h] = (w * u) @ v[g]
+    return out, cnt
+
+
+def check_attention():
+    w = synth.bf16_bits_to_f32
+    for (Hq, Hkv, n, hd, r, ka) in [(4, 2, 100, 32, 16, 256), (4, 2, 64, 32, 16, 64), (8, 4, 1500, 64, 32, 128),
+                                    (2, 1, 3000, 16, 8, 200)]:
+        qb, k1b, k2b, vb = synth.attn_inputs(31, Hq, Hkv, n, hd, r, scale=0.5)
+        res = oracle.spark_attn_decode(qb, k1b, k2b, vb, ka)
+        ref, cnt = _attn_ref(w(qb).astype(np.float64), w(k1b).astype(np.float64), w(k2b).astype(np.float64),
+                             w(vb).astype(np.float64), ka)
+        assert np.array_equal(res["counts"], cnt), (n, res["counts"], cnt)
+        assert rel(res["out"], ref) < 1e-12, (n, rel(res["out"], ref))
+        # with the compute-key half of q zeroed, sigma2 is the constant softplus(0) = ln 2
+        q0 = qb.copy()
+        q0[:, r:] = 0
+        res0 = oracle.spark_attn_decode(q0, k1b, k2b, vb, ka)
+        ref0, _ = _attn_ref(w(q0).astype(np.float64), w(k1b).astype(np.float64), w(k2b).astype(np.float64),
+                            w(vb).astype(np.float64), ka, sigma2=False)
+        assert rel(res0["out"], math.log(2.0) * ref0) < 1e-12
+    # GQA grouping: query head h reads KV head h // (Hq/Hkv)
+    qb, k1b, k2b, vb = synth.attn_inputs(37, 4, 2, 600, 32, 16)
+    a = oracle.spark_attn_decode(qb, k1b, k2b, vb, 64)
+    k1c, vc = k1b.copy(), vb.copy()
+    k1c[1] = k1c[1][::-1]
+    vc[1] = 0
+    b = oracle.spark_attn_decode(qb, k1c, k2b, vc, 64)
+    assert np.array_equal(a["out"][:2], b["out"][:2]) and not np.allclose(a["out"][2:], b["out"][2:])
+    # constant scores: std 0, nothing strictly above theta, zero output
+    k1z = np.zeros_like(k1b)
+    z = oracle.spark_attn_decode(qb, k1z, k2b, vb, 64)
+    assert np.all(z["counts"] == 0) and np.all(z["out"] == 0)
+
+
+# ---------------------------------------------------------------- P13 continuity at theta
+def check_continuity():
+    dm, dff, r, k = 16, 64, 8, 6
+    k1t, k2t, v = synth.ffn_layer(9, 0, dm, dff, r, "f32")
+    g = np.random.default_rng(1)
+    crossings = 0
+    for trial in range(400):
+        q = g.standard_normal(dm).astype(np.float32)
+        u = g.standard_normal(dm).astype(np.float32)
+        delta = 1e-2
+        a = oracle.spark_ffn(q[None], k1t, k2t, v, r, k)
+        b = oracle.spark_ffn((q + np.float32(delta) * u)[None], k1t, k2t, v, r, k)
+        if not np.array_equal(a["idx"], b["idx"]):
+            crossings += 1
+        dy = np.linalg.norm(a["y"] - b["y"])
+        assert dy <= 10.0 * delta, (trial, dy)
+    assert crossings >= 10, crossings  # the perturbations did move entries across theta
+
+
+# ---------------------------------------------------------------- P14 decode chain
+def check_decode_chain():
+    dm, dff, r, k, L = 32, 128, 16, 10, 4
+    layers = [synth.ffn_layer(2, l, dm, dff, r, "f32") for l in range(L)]
+    q0 = synth.queries(2, 2, dm)
+    eps = 1e-6
+    res = oracle.decode_stack(q0, layers, r, k, eps, trace=True)
+    for t in range(2):
+        q = q0[t].astype(np.float64)
+        for l in range(L):
+            assert np.allclose(res["q_trace"][t, l], q, rtol=1e-12, atol=1e-14)
+            y, _, _, S = dense_masked_ffn(q, *layers[l], r, k)
+            assert res["counts"][t, l] == S.size
+            q = y / np.sqrt(np.mean(y * y) + eps)
+        assert rel(res["y"][t], y) < 1e-12
+
+
+ALL_CHECKS = [check_quantile, check_threshold_closed_form, check_special_rows, check_quantile_grid,
+              check_invariants, check_scale_invariance, check_theorem31, check_student_t, check_ffn_dense_masked,
+              check_ffn_bf16_widening, check_topk_is_largest, check_activations, check_attention, check_continuity,
+              check_decode_chain]
