@@ -1,0 +1,278 @@
+"""Python binding of libspark_ffn.so, the MI355X (gfx950) Spark FFN library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/spark_ffn.h.  PyTorch supplies
+device memory (tensors' data pointers) and the current HIP stream.  There is no
+fallback: if the library is not built, or a call returns an error status, a
+RuntimeError is raised.
+
+Entry points (same names as the C ABI):
+  stat_topk(x, k, cap=None)                         -> (vals, idx, counts, theta)
+  spark_ffn_decode(q, layers, k, r, eps, ...)       -> y  (and a trace dict)
+  spark_ffn_prefill(Q, layer, k, r, ...)            -> Y  (and a trace dict)
+  spark_attn_decode(q, k1, k2, v, k_attn, cap=None) -> (out, counts, idx, theta)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspark_ffn.so")
+
+SPARK_OK, SPARK_EINVAL, SPARK_EUNSUPPORTED, SPARK_EHIP, SPARK_EWORKSPACE = 0, -1, -2, -3, -4
+SPARK_F32, SPARK_BF16 = 0, 1
+
+_vp, _i64, _ci, _f, _d, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double,
+                               ctypes.c_size_t)
+
+
+class ShapeC(ctypes.Structure):
+    _fields_ = [("d_model", _i64), ("d_ff", _i64), ("r", _i64), ("k", _i64), ("wdtype", _ci)]
+
+
+class WeightsC(ctypes.Structure):
+    _fields_ = [("k1t", _vp), ("k2t", _vp), ("v", _vp)]
+
+
+class TraceC(ctypes.Structure):
+    _fields_ = [("counts", _vp), ("idx", _vp), ("theta", _vp), ("q_in", _vp), ("cap", _i64)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspark_ffn.so (after torch, so that it binds to torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(f"{LIB_PATH} is not built: run `python -m attention_spark_ffn_amd.build`")
+                L = ctypes.CDLL(LIB_PATH)
+                L.spark_status_string.restype = ctypes.c_char_p
+                L.spark_status_string.argtypes = [_ci]
+                L.spark_threshold_z.restype = _d
+                L.spark_threshold_z.argtypes = [_i64, _i64]
+                L.stat_topk.restype = _ci
+                L.stat_topk.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp]
+                L.spark_ffn_decode.restype = _ci
+                L.spark_ffn_decode.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _ci, _vp, _i64, _vp,
+                                               _f, ctypes.POINTER(TraceC), _vp, _sz, _vp]
+                L.spark_ffn_prefill.restype = _ci
+                L.spark_ffn_prefill.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _vp, _i64, _vp,
+                                                ctypes.POINTER(TraceC), _vp, _sz, _vp]
+                L.spark_attn_decode.restype = _ci
+                L.spark_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
+                                                _vp, _i64, _vp, _vp, _sz, _vp]
+                L.spark_ffn_decode_workspace_size.restype = _ci
+                L.spark_ffn_decode_workspace_size.argtypes = [ctypes.POINTER(ShapeC), _ci, _i64,
+                                                              ctypes.POINTER(_sz)]
+                L.spark_ffn_prefill_workspace_size.restype = _ci
+                L.spark_ffn_prefill_workspace_size.argtypes = [ctypes.POINTER(ShapeC), _i64, ctypes.POINTER(_sz)]
+                L.spark_attn_workspace_size.restype = _ci
+                L.spark_attn_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_sz)]
+                _lib = L
+    return _lib
+
+
+def status_string(st: int) -> str:
+    return lib().spark_status_string(st).decode()
+
+
+def _check(st: int, what: str):
+    if st != SPARK_OK:
+        raise RuntimeError(f"{what}: {status_string(st)} (status {st})")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _wdtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SPARK_BF16
+    if t.dtype == torch.float32:
+        return SPARK_F32
+    raise TypeError(f"weights must be bf16 or fp32, got {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on a HIP device")
+
+
+def threshold_z(k: int, d: int) -> float:
+    """The library's Q(1 - k/d) (host fp64)."""
+    return lib().spark_threshold_z(int(k), int(d))
+
+
+# ---------------------------------------------------------------------------- stat_topk
+def stat_topk(x: torch.Tensor, k: int, cap: int | None = None):
+    """Statistical top-k of each row of fp32 x [rows][d] (row stride taken from x).
+
+    Returns vals [rows][cap] fp32, idx [rows][cap] int32 (first min(count, cap)
+    selected entries, ascending; the rest of each row untouched: zeros / -1),
+    counts [rows] int32 (true counts) and theta [rows] fp32.
+    """
+    if x.dim() != 2 or x.dtype != torch.float32 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D fp32 HIP tensor with unit column stride")
+    rows, d = x.shape
+    cap = d if cap is None else int(cap)
+    dev = x.device
+    vals = torch.zeros((rows, cap), dtype=torch.float32, device=dev)
+    idx = torch.full((rows, cap), -1, dtype=torch.int32, device=dev)
+    counts = torch.empty(rows, dtype=torch.int32, device=dev)
+    theta = torch.empty(rows, dtype=torch.float32, device=dev)
+    st = lib().stat_topk(_p(x), rows, d, x.stride(0) if rows > 0 else d, int(k), _p(vals), _p(idx), cap, _p(counts),
+                         _p(theta), _stream(dev))
+    _check(st, "stat_topk")
+    return vals, idx, counts, theta
+
+
+# ---------------------------------------------------------------------------- decode
+_ws_cache: dict = {}
+
+
+def _cached_workspace(kind: str, device, nbytes: int) -> torch.Tensor:
+    """Per-device workspace, zero-filled once when created and then carried
+    between calls (the decode kernel keeps a sequence counter in it)."""
+    key = (kind, device)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _shape(d_model, d_ff, r, k, wd) -> ShapeC:
+    return ShapeC(int(d_model), int(d_ff), int(r), int(k), int(wd))
+
+
+def spark_ffn_decode(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6, trace: bool = False,
+                     cap: int | None = None, ws: torch.Tensor | None = None):
+    """Run the stack of Spark FFN layers on T independent tokens.
+
+    q [T][d_model] fp32; layers: list of (k1t [d_ff][r], k2t [d_ff][d_model-r],
+    v [d_ff][d_model]) tensors, all bf16 or all fp32.  Returns y [T][d_model]
+    fp32 (last layer, before normalisation).  With trace=True also returns a
+    dict with counts [T][L], idx [T][L][cap], theta [T][L], q_in [T][L][d_model].
+    ws: optional zero-initialised uint8 workspace to use (and carry) instead of
+    the module's cached one.
+    """
+    _need_cuda(q)
+    T, d_model = q.shape
+    L = len(layers)
+    k1t0, k2t0, v0 = layers[0]
+    d_ff = v0.shape[0]
+    wd = _wdtype(k1t0)
+    for lw in layers:
+        _need_cuda(*lw)
+        if any(_wdtype(a) != wd for a in lw):
+            raise TypeError("all weights must share one dtype")
+        if lw[0].shape != (d_ff, r) or lw[1].shape != (d_ff, d_model - r) or lw[2].shape != (d_ff, d_model):
+            raise ValueError("weight shapes do not match q / r")
+    shape = _shape(d_model, d_ff, r, k, wd)
+    wts = (WeightsC * L)(*[WeightsC(a.data_ptr(), b.data_ptr(), c.data_ptr()) for (a, b, c) in layers])
+    need = ctypes.c_size_t(0)
+    _check(lib().spark_ffn_decode_workspace_size(ctypes.byref(shape), L, T, ctypes.byref(need)),
+           "spark_ffn_decode_workspace_size")
+    dev = q.device
+    if ws is None:
+        ws = _cached_workspace("decode", dev, need.value)
+    y = torch.empty((T, d_model), dtype=torch.float32, device=dev)
+    tr = None
+    trc = None
+    if trace:
+        cap = d_ff if cap is None else int(cap)
+        tr = dict(counts=torch.zeros((T, L), dtype=torch.int32, device=dev),
+                  idx=torch.full((T, L, cap), -1, dtype=torch.int32, device=dev),
+                  theta=torch.zeros((T, L), dtype=torch.float32, device=dev),
+                  q_in=torch.zeros((T, L, d_model), dtype=torch.float32, device=dev))
+        trc = TraceC(tr["counts"].data_ptr(), tr["idx"].data_ptr(), tr["theta"].data_ptr(), tr["q_in"].data_ptr(), cap)
+    st = lib().spark_ffn_decode(ctypes.byref(shape), wts, L, _p(q), T, _p(y), float(eps),
+                                ctypes.byref(trc) if trc is not None else None, _p(ws), ws.numel(), _stream(dev))
+    _check(st, "spark_ffn_decode")
+    return (y, tr) if trace else y
+
+
+def decode_workspace_failed(ws: torch.Tensor | None = None, device=None) -> bool:
+    """True if a decode kernel that used this workspace recorded a timeout
+    (reads the workspace header; synchronises)."""
+    if ws is None:
+        ws = _ws_cache.get(("decode", device or torch.device("cuda", torch.cuda.current_device())))
+        if ws is None:
+            return False
+    return int(ws[8:16].view(torch.int64).item()) != 0
+
+
+# ---------------------------------------------------------------------------- prefill
+def spark_ffn_prefill(Q: torch.Tensor, layer, k: int, r: int, trace: bool = False, cap: int | None = None):
+    """One Spark FFN layer on T tokens at once.  Q [T][d_model] bf16; layer =
+    (k1t, k2t, v) bf16.  Returns Y [T][d_model] fp32 (and with trace=True a dict
+    with counts [T], idx [T][cap], theta [T])."""
+    _need_cuda(Q, *layer)
+    T, d_model = Q.shape
+    k1t, k2t, v = layer
+    d_ff = v.shape[0]
+    wd = _wdtype(k1t)
+    if Q.dtype != k1t.dtype:
+        raise TypeError("Q must have the weights' dtype")
+    shape = _shape(d_model, d_ff, r, k, wd)
+    w = WeightsC(k1t.data_ptr(), k2t.data_ptr(), v.data_ptr())
+    need = ctypes.c_size_t(0)
+    _check(lib().spark_ffn_prefill_workspace_size(ctypes.byref(shape), T, ctypes.byref(need)),
+           "spark_ffn_prefill_workspace_size")
+    dev = Q.device
+    ws = _cached_workspace("prefill", dev, need.value)
+    Y = torch.empty((T, d_model), dtype=torch.float32, device=dev)
+    tr = None
+    trc = None
+    if trace:
+        cap = d_ff if cap is None else int(cap)
+        tr = dict(counts=torch.zeros((T, 1), dtype=torch.int32, device=dev),
+                  idx=torch.full((T, 1, cap), -1, dtype=torch.int32, device=dev),
+                  theta=torch.zeros((T, 1), dtype=torch.float32, device=dev))
+        trc = TraceC(tr["counts"].data_ptr(), tr["idx"].data_ptr(), tr["theta"].data_ptr(), None, cap)
+    st = lib().spark_ffn_prefill(ctypes.byref(shape), ctypes.byref(w), _p(Q), T, _p(Y),
+                                 ctypes.byref(trc) if trc is not None else None, _p(ws), ws.numel(), _stream(dev))
+    _check(st, "spark_ffn_prefill")
+    return (Y, tr) if trace else Y
+
+
+# ---------------------------------------------------------------------------- attention
+def spark_attn_decode(q: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor, v: torch.Tensor, k_attn: int,
+                      cap: int | None = None):
+    """Spark attention decode.  q [Hq][hd] bf16; k1 [Hkv][n][r], k2 [Hkv][n][hd-r],
+    v [Hkv][n][hd] bf16.  Returns out [Hq][hd] fp32, counts [Hq], idx [Hq][cap]
+    (ascending selected tokens; -1 padded) and theta [Hq] (NaN when dense)."""
+    _need_cuda(q, k1, k2, v)
+    for t in (q, k1, k2, v):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("attention inputs must be bf16")
+    Hq, hd = q.shape
+    Hkv, n, r = k1.shape
+    cap = min(n, 4096) if cap is None else int(cap)
+    need = ctypes.c_size_t(0)
+    _check(lib().spark_attn_workspace_size(Hq, Hkv, n, hd, r, int(k_attn), ctypes.byref(need)),
+           "spark_attn_workspace_size")
+    dev = q.device
+    ws = _cached_workspace("attn", dev, need.value)
+    out = torch.empty((Hq, hd), dtype=torch.float32, device=dev)
+    counts = torch.empty(Hq, dtype=torch.int32, device=dev)
+    idx = torch.full((Hq, max(cap, 1)), -1, dtype=torch.int32, device=dev)
+    theta = torch.empty(Hq, dtype=torch.float32, device=dev)
+    st = lib().spark_attn_decode(_p(q), _p(k1), _p(k2), _p(v), Hq, Hkv, n, hd, r, int(k_attn), _p(out), _p(counts),
+                                 _p(idx), cap, _p(theta), _p(ws), ws.numel(), _stream(dev))
+    _check(st, "spark_attn_decode")
+    return out, counts, idx, theta

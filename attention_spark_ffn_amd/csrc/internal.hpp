@@ -1,0 +1,44 @@
+// Launchers behind the C ABI (host side).  Arguments are validated by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "spark_ffn.h"
+
+namespace spark {
+
+// ---------------------------------------------------------------- stat_topk
+hipError_t launch_stat_topk(const float* x, int64_t rows, int64_t d, int64_t ldx, double z, float* vals, int32_t* idx,
+                            int64_t cap, int32_t* counts, float* theta, hipStream_t st);
+
+// ---------------------------------------------------------------- decode
+// Layers handled by one launch of the persistent decode kernel.
+constexpr int kDecodeMaxLayersPerLaunch = 32;
+constexpr int kDecodeThreads = 512;
+constexpr int kDecodeMaxDModel = 8192;
+constexpr int kDecodeMaxNeuronsPerWG = 256;
+constexpr int kDecodeMaxColsPerWG = 512;
+
+size_t decode_workspace_bytes(int64_t d_model, int64_t d_ff, int n_layers, int64_t T, int grid);
+int decode_grid(int64_t d_ff);  // workgroups of the persistent grid on the current device
+hipError_t launch_decode(const spark_ffn_shape& s, const spark_ffn_weights* layers, int n_layers, const float* q,
+                         int64_t T, float* y, float eps, double z, const spark_ffn_trace* trace, void* ws,
+                         hipStream_t st);
+
+// ---------------------------------------------------------------- prefill
+size_t prefill_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t T);
+hipError_t launch_prefill(const spark_ffn_shape& s, const spark_ffn_weights& w, const void* Q, int64_t T, float* Y,
+                          double z, const spark_ffn_trace* trace, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+size_t attn_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn);
+hipError_t launch_attn_decode(const void* q, const void* k1, const void* k2, const void* v, int64_t Hq, int64_t Hkv,
+                              int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn, double z, float* out,
+                              int32_t* counts, int32_t* idx, int64_t cap, float* theta, void* ws, hipStream_t st);
+
+// device properties (cached per device)
+int device_cu_count();
+
+}  // namespace spark

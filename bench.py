@@ -1,0 +1,176 @@
+"""Benchmark: Spark FFN decode on one MI355X.
+
+Workload: a stack of 26 independent Spark FFN layers (d_model 2304, d_ff 9216,
+r 1152, k 737 = 8% of d_ff), bf16 weights N(0, 1/fan_in), fp32 queries
+N(0, 1), RMS normalisation between layers; batch 1.  One step = one token
+through the whole stack (one spark_ffn_decode call with T = 1), inputs
+resident in HBM before the timed region.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+
+value = tokens/s.  roofline: the decode kernel's algorithmic HBM bytes per
+launch (K1 slab of every layer + the selected K2 and V rows, from the actual
+per-layer counts, + the small vectors) / its average launch time measured with
+HIP events on the launch stream.  cpu_baseline: the fp64 oracle on a bounded
+sample of tokens on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+D_MODEL, D_FF, R, K, LAYERS = 2304, 9216, 1152, 737, 26
+HBM_PEAK_GBS = 8000.0
+METRIC = "Spark-FFN decode tokens/s (2304×9216, k=8%) + achieved HBM GB/s vs peak"
+
+
+def algorithmic_bytes(counts: np.ndarray) -> float:
+    """Bytes one token must move from HBM: per layer the whole K1 (r x d_ff bf16),
+    the selected neurons' K2 rows ((d_model - r) bf16) and V rows (d_model bf16),
+    plus the fp32 input and output vectors."""
+    k1 = R * D_FF * 2
+    per_sel = (D_MODEL - R) * 2 + D_MODEL * 2
+    vecs = 2 * D_MODEL * 4
+    return float(LAYERS * (k1 + vecs) + per_sel * counts.sum())
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("ffn_decode.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "attention_spark_ffn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per decode launch from rocprofv3 counters (profiles/), only if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(layers_np, budget_s: float = 15.0):
+    import oracle
+
+    oracle.build()
+    q = np.random.default_rng(12345).standard_normal((1, D_MODEL)).astype(np.float32)
+    t0 = time.perf_counter()
+    oracle.decode_stack(q, layers_np, R, K, 1e-6)
+    one = time.perf_counter() - t0
+    n = int(max(3, min(400, budget_s / max(one, 1e-3))))
+    qs = np.random.default_rng(54321).standard_normal((n, D_MODEL)).astype(np.float32)
+    t0 = time.perf_counter()
+    oracle.decode_stack(qs, layers_np, R, K, 1e-6)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} tokens through the same 26-layer stack (fp64 C oracle, OpenMP), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the decode path is a single-GPU kernel); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_spark_ffn_amd as sf
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    layers_np = synth.ffn_stack(args.seed, LAYERS, D_MODEL, D_FF, R, "bf16", workers=16)
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    layers = [tuple(to_dev(a) for a in lw) for lw in layers_np]
+    nq = args.warmup + args.steps
+    qs = torch.from_numpy(synth.queries(args.seed, nq, D_MODEL)).to(dev)
+    print(f"# setup {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        sf.spark_ffn_decode(qs[i:i + 1], layers, K, R)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        sf.spark_ffn_decode(qs[args.warmup + i:args.warmup + i + 1], layers, K, R)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    failed = sf.decode_workspace_failed(device=dev)
+
+    # actual per-layer selected counts of the timed tokens (same inputs, deterministic)
+    _, tr = sf.spark_ffn_decode(qs[args.warmup:], layers, K, R, trace=True, cap=1)
+    counts = tr["counts"].cpu().numpy()
+    bytes_per_token = np.array([algorithmic_bytes(c) for c in counts])
+    avg_launch_s = per_launch_ms.mean() / 1e3
+    achieved_gbs = bytes_per_token.mean() / avg_launch_s / 1e9
+    traffic = load_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": args.steps / (total_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "spark_ffn_decode: 26 layers x (d_model 2304, d_ff 9216, r 1152, k 737), "
+                               "bf16 weights, fp32 q, batch 1",
+                   "weights_dtype": "bf16", "layers": LAYERS, "d_model": D_MODEL, "d_ff": D_FF, "r": R, "k": K,
+                   "global_batch": 1},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "spark::decode_kernel<bf16>",
+                     "algorithmic_bytes_per_launch": float(bytes_per_token.mean()),
+                     "avg_launch_us": avg_launch_s * 1e6,
+                     "p10_us": float(np.percentile(per_launch_ms, 10) * 1e3),
+                     "p90_us": float(np.percentile(per_launch_ms, 90) * 1e3),
+                     "mean_selected_per_layer": float(counts.mean())},
+        "cpu_baseline": None,
+        "kernel_failed": bool(failed),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(layers_np)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * spark_ffn.h -- C ABI of the MI355X (gfx950) Spark FFN library.
+ *
+ * The operations are those of the Spark Transformer (arXiv 2506.06644,
+ * "Spark Transformer: Reactivating Sparsity in FFN and Attention"); the
+ * statements of the method used here are in the reading notes of that paper,
+ * section "方法详解 / 关键设计" (method / key design), items "Spark FFN",
+ * "Spark Attention" and "Statistical Top-k".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Memory.  Every array argument is a DEVICE pointer (memory of the current
+ *    HIP device), except the shape/weight/trace structs themselves and the
+ *    `layers` array of spark_ffn_decode, which live in host memory.  The caller
+ *    owns all memory; the library never allocates or frees device memory.
+ *    Scratch memory is the caller's workspace `ws` of `ws_bytes` bytes, sized
+ *    with the matching *_workspace_size function (256-byte aligned base).
+ *  - Layout.  Row-major and contiguous.  Weights of one Spark FFN layer:
+ *      k1t [d_ff][r]          K1 transposed: row i is neuron i's predictor key
+ *      k2t [d_ff][d_model-r]  K2 transposed: row i is neuron i's compute key
+ *      v   [d_ff][d_model]    row i is neuron i's value row
+ *    Spark attention KV cache, split along the key dimension:
+ *      k1 [Hkv][n_ctx][r], k2 [Hkv][n_ctx][hd-r], v [Hkv][n_ctx][hd].
+ *  - Streams.  Work is enqueued on `stream` (NULL = the default stream) and
+ *    runs asynchronously; nothing synchronises the host.
+ *  - Errors.  Return SPARK_OK or a negative status.  All argument checks run
+ *    before the first device call, so a non-OK status means nothing was
+ *    enqueued -- except SPARK_EHIP, returned when the HIP runtime rejects a
+ *    launch (the error is the one hipGetLastError reported).  No C++
+ *    exception crosses this interface.  spark_status_string() names a status.
+ *  - Capacity.  Per-row index/value lists have `cap` slots.  `counts` always
+ *    receives the TRUE number of selected entries; when it exceeds `cap` only
+ *    the first `cap` (lowest indices) are stored.  cap = d never truncates.
+ *  - Determinism.  Every reduction runs in a fixed order: identical inputs
+ *    give bit-identical outputs.
+ */
+#ifndef SPARK_FFN_H
+#define SPARK_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SPARK_OK = 0,
+    SPARK_EINVAL = -1,       /* bad size, k, pointer, alignment or stride */
+    SPARK_EUNSUPPORTED = -2, /* a dtype or size outside what is built */
+    SPARK_EHIP = -3,         /* the HIP runtime failed a launch */
+    SPARK_EWORKSPACE = -4    /* ws is NULL, misaligned or smaller than required */
+};
+
+typedef enum { SPARK_F32 = 0, SPARK_BF16 = 1 } spark_dtype;
+
+/* One Spark FFN layer shape.  0 < r < d_model (q[:r] feeds the predictor,
+ * q[r:] the compute keys); 0 < k < d_ff (target number of active neurons). */
+typedef struct {
+    int64_t d_model, d_ff, r, k;
+    spark_dtype wdtype; /* dtype of k1t, k2t and v */
+} spark_ffn_shape;
+
+/* Device pointers to one layer's weights (layouts above). */
+typedef struct {
+    const void *k1t, *k2t, *v;
+} spark_ffn_weights;
+
+/* Optional per-layer outputs for inspection; every pointer may be NULL.
+ * For spark_ffn_prefill n_layers is 1. */
+typedef struct {
+    int32_t *counts; /* [T][n_layers] true number of selected neurons */
+    int32_t *idx;    /* [T][n_layers][cap] selected neurons, ascending */
+    float *theta;    /* [T][n_layers] threshold used */
+    float *q_in;     /* [T][n_layers][d_model] each layer's input q (decode only) */
+    int64_t cap;     /* slots per (token, layer) in idx */
+} spark_ffn_trace;
+
+/*
+ * Statistical top-k ("Statistical Top-k" item): for each of `rows` fp32 rows
+ * x[row*ldx + 0..d), theta = mean + std * Q(1 - k/d) with the population std
+ * (1/d) and Q the standard-normal quantile; the selected set is
+ * {i : x_i > theta} in ascending order, and the soft-threshold value of a
+ * selected entry is x_i - theta (the operator max{x - theta, 0} restricted to
+ * its nonzeros).
+ *   vals [rows][cap] fp32, idx [rows][cap] int32: first min(count, cap)
+ *       entries of each row (both may be NULL; then nothing is listed);
+ *   counts [rows] int32 (required);  theta [rows] fp32 (may be NULL).
+ * Requires 0 < k < d <= 65536, ldx >= d, rows >= 0, cap >= 0.  No workspace.
+ * Rows with zero spread select nothing.
+ */
+int stat_topk(const float *x, int64_t rows, int64_t d, int64_t ldx, int64_t k, float *vals, int32_t *idx,
+              int64_t cap, int32_t *counts, float *theta, hipStream_t stream);
+
+/*
+ * Spark FFN decode ("Spark FFN" item): for each of T independent tokens, run
+ * the stack of n_layers Spark FFN layers
+ *     y_l = V (GELU(StatTopk(K1^T q_l[:r])) (.) (K2^T q_l[r:]))
+ * where StatTopk is the statistical top-k above with k = s->k over the d_ff
+ * predictor scores, GELU is the tanh form, and only the selected K2 columns
+ * (k2t rows) and V rows are read.  Between layers
+ *     q_{l+1} = y_l / sqrt(mean(y_l^2) + rms_eps)      (unit gain, no residual).
+ *   q [T][d_model] fp32 input of layer 0;  y [T][d_model] fp32 output of the
+ *   last layer (before normalisation);  layers: host array of n_layers weight
+ *   sets; trace may be NULL.
+ * Weights fp32 or bf16; arithmetic fp32 with fp32 accumulation.
+ * Requires d_model <= 8192, d_ff <= 65536, 1 <= n_layers, T >= 0, rms_eps >= 0;
+ * weight rows 16-byte aligned (k1t, k2t, v base pointers 256-byte aligned and
+ * r, d_model - r, d_model multiples of 8 elements).
+ * The kernel is a cooperative (co-resident) grid; it returns SPARK_EHIP if the
+ * device cannot host it.
+ */
+int spark_ffn_decode(const spark_ffn_shape *s, const spark_ffn_weights *layers, int n_layers, const float *q,
+                     int64_t T, float *y, float rms_eps, const spark_ffn_trace *trace, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
+ * Spark FFN prefill: the same layer (one layer) applied to T tokens at once.
+ * The predictor K1^T Q[:, :r] runs as a dense GEMM on the matrix cores, the
+ * statistical top-k per token over its fp32 scores, then each token's
+ * selected K2 columns and V rows.
+ *   Q [T][d_model] of dtype s->wdtype; Y [T][d_model] fp32; trace may be NULL
+ *   (its q_in is ignored).
+ * Requires bf16 weights and Q, d_ff a multiple of 256, r a multiple of 64,
+ * d_model <= 8192, d_ff <= 65536.
+ */
+int spark_ffn_prefill(const spark_ffn_shape *s, const spark_ffn_weights *w, const void *Q, int64_t T, float *Y,
+                      const spark_ffn_trace *trace, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Spark attention decode ("Spark Attention" item): attention in the form of
+ * the Spark FFN, with the key dimension split into a predictor part (first r
+ * dims) and a compute part (last hd - r dims), sigma1 = softmax and
+ * sigma2 = softplus.  For query head h (KV head g = h / (Hq/Hkv)):
+ *     s_j = q_h[:r] . k1[g][j]                    (predictor scores, j < n_ctx)
+ *     S   = statistical top-k of s with k_attn    (all j when n_ctx <= k_attn)
+ *     w_j = softmax of s over S (unselected tokens get weight 0)
+ *     u_j = softplus(q_h[r:] . k2[g][j])
+ *     out_h = sum_{j in S} w_j u_j v[g][j]
+ * No 1/sqrt(hd) factor is applied (scale q or k beforehand).
+ *   q [Hq][hd] bf16; k1/k2/v bf16 as above; out [Hq][hd] fp32;
+ *   counts [Hq] (may be NULL), idx [Hq][cap] (may be NULL), theta [Hq] (may be
+ *   NULL; NaN when all tokens are attended).
+ * Requires Hq % Hkv == 0, hd <= 512, 0 < r < hd, r and hd - r multiples of 8,
+ * 1 <= n_ctx <= 1048576, k_attn >= 1.
+ */
+int spark_attn_decode(const void *q, const void *k1, const void *k2, const void *v, int64_t Hq, int64_t Hkv,
+                      int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn, float *out, int32_t *counts,
+                      int32_t *idx, int64_t cap, float *theta, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace sizes (bytes) for the calls above with the same arguments. */
+int spark_ffn_decode_workspace_size(const spark_ffn_shape *s, int n_layers, int64_t T, size_t *bytes);
+int spark_ffn_prefill_workspace_size(const spark_ffn_shape *s, int64_t T, size_t *bytes);
+int spark_attn_workspace_size(int64_t Hq, int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn,
+                              size_t *bytes);
+
+/* z = Q(1 - k/d), the standard-normal quantile the threshold uses (host fp64). */
+double spark_threshold_z(int64_t k, int64_t d);
+
+/* Text for a status code. */
+const char *spark_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARK_FFN_H */
