@@ -54,7 +54,9 @@ int decode_limits(const spark_ffn_shape* s) {
   const int grid = spark::decode_grid(s->d_ff);
   if (grid <= 0 || grid > 256) return SPARK_EUNSUPPORTED;
   if ((s->d_ff + grid - 1) / grid > spark::kDecodeMaxNeuronsPerWG) return SPARK_EUNSUPPORTED;
-  if ((s->d_model + grid - 1) / grid > spark::kDecodeMaxColsPerWG) return SPARK_EUNSUPPORTED;
+  // each workgroup owns at most two 16-byte chunks of a V row
+  const int64_t cn = s->wdtype == SPARK_BF16 ? 8 : 4;
+  if (s->d_model % cn != 0 || (s->d_model / cn + grid - 1) / grid > 2) return SPARK_EUNSUPPORTED;
   return SPARK_OK;
 }
 

@@ -50,6 +50,23 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
 }
 
 // ---------------------------------------------------------------- wave reductions
+// Sum over the 64 lanes with DPP row operations (VALU, no LDS traffic); the
+// total is read from lane 63 and returned to every lane.  The order of the
+// additions is fixed, so the result is bit-identical run to run and in every
+// workgroup that reduces the same values.
+#define SPARK_DPP_ADD(v, ctrl, rmask)                                                                          \
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, rmask, 0xf, true))
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  SPARK_DPP_ADD(v, 0xb1, 0xf);   // quad_perm [1,0,3,2]
+  SPARK_DPP_ADD(v, 0x4e, 0xf);   // quad_perm [2,3,0,1]
+  SPARK_DPP_ADD(v, 0x114, 0xf);  // row_shr:4
+  SPARK_DPP_ADD(v, 0x118, 0xf);  // row_shr:8   -> lane 15 of each row holds the row sum
+  SPARK_DPP_ADD(v, 0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+  SPARK_DPP_ADD(v, 0x143, 0xc);  // row_bcast:31 into rows 2 and 3 -> lane 63 holds the total
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+#undef SPARK_DPP_ADD
+
 // Butterfly reductions: every lane ends with the same value, bit for bit
 // (each step adds a and b in either order, and fp add is commutative).
 __device__ __forceinline__ float wave_sum(float v) {

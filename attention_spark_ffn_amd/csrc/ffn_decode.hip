@@ -32,11 +32,15 @@
 
 namespace spark {
 
-constexpr int kDecMaxC = 21;  // K1 chunks (16 B) held per streamer thread (a 36 x 1152 bf16 slab)
+constexpr int kDecMaxC = 21;   // K1 chunks (16 B) held per streamer thread (a 36 x 1152 bf16 slab)
 constexpr int kStreamers = 256;
 constexpr int kWorkers = 256;
-constexpr int kRep = 8;       // replicas of the broadcast exchanges (one per XCD)
-constexpr int kRedMax = kDecodeMaxDModel + 512;
+constexpr int kRep = 8;        // replicas of every broadcast record (one per XCD)
+constexpr int kCand = 16;      // owned neurons whose K2 dot is formed before theta is known
+constexpr int kRecWords = 16;  // selected-list record: 2 mask words + 14 entries
+constexpr int kRecEntries = kRecWords - 2;
+constexpr int kOvfWords = kDecodeMaxNeuronsPerWG - kRecEntries;
+constexpr int kListMax = kDecodeMaxNeuronsPerWG * 256;
 
 struct DecodeParams {
   const void* k1t[kDecodeMaxLayersPerLaunch];
@@ -53,11 +57,12 @@ struct DecodeParams {
   float* tr_theta;
   float* tr_q;
   int64_t tr_cap;
-  uint64_t* hdr;   // [0]: last tag used, [1]: failure flag
-  uint64_t* stats; // kRep x stats_stride
-  uint64_t* part;  // G x part_stride
-  uint64_t* ycol;  // kRep x ycol_stride
-  int stats_stride, part_stride, ycol_stride;
+  uint64_t* hdr;    // [0]: last tag used, [1]: failure flag
+  uint64_t* stats;  // kRep x stats_stride: (mean, M2) per workgroup
+  uint64_t* rec;    // kRep x rec_stride: selected-list record per workgroup
+  uint64_t* ovf;    // G x kOvfWords: list entries past the record
+  uint64_t* ycol;   // kRep x ycol_stride: owned columns of y
+  int stats_stride, rec_stride, ycol_stride, ycol_done;
   uint32_t spin_limit;
 };
 
@@ -90,6 +95,7 @@ __device__ __forceinline__ bool gather_tagged(const uint64_t* const (&ptrs)[K], 
     if (all) return true;
     if (spin > spin_limit) return false;
     if ((spin & 1023) == 1023 && get_word(hdr + 1) != 0) return false;
+    __builtin_amdgcn_s_sleep(1);
   }
 }
 
@@ -99,32 +105,84 @@ __device__ __forceinline__ void raise_failure(uint64_t* hdr) {
 
 // LDS of one decode workgroup.
 struct DecShared {
-  float q[kDecodeMaxDModel];               // current layer input
-  float part[kStreamers * kDecMaxC];       // per-chunk partial dot products
-  float h[kDecodeMaxNeuronsPerWG];         // predictor scores of the owned neurons
-  int sel[kDecodeMaxNeuronsPerWG];         // selected owned neurons, ascending
-  float m[kDecodeMaxNeuronsPerWG];         // their soft-threshold values
-  float c[kDecodeMaxNeuronsPerWG];         // their gated values GELU(m) * (K2^T q[r:])
-  float red[kRedMax];                      // partial y, then gathered column partials
-  float ycol[kDecodeMaxColsPerWG];         // owned columns of y
+  alignas(16) float q[kDecodeMaxDModel];  // current layer input
+  union {
+    float part[kStreamers * kDecMaxC + 64];  // per-chunk partial dot products (+ a dummy slot)
+    struct {
+      float c[kListMax];          // gated values of every selected neuron, ascending neuron order
+      uint16_t idx[kListMax];     // their neuron indices
+    } list;
+  } u;
+  float h[kDecodeMaxNeuronsPerWG];   // predictor scores of the owned neurons
+  float g[kDecodeMaxNeuronsPerWG];   // K2^T q[r:] of the owned neurons (candidates, then misses)
+  int cnt[256];                      // selected count of every workgroup
+  int off[256];                      // exclusive prefix of cnt
+  union {
+    float stage[256][kRecEntries];   // record entries as gathered, before placement
+  } t;
+  float colpart[4][16];              // per-wave sums of the owned columns
   float wred[8];
   float theta;
-  int nsel, fail;
+  uint64_t candmask;
+  int ntot, fail;
   uint32_t tag0;
 };
 
 // Shape of the work of one workgroup.
 struct DecGeo {
   int G, w, d_model, d_ff, r, L, T;
-  int n0, nown, c0, ncol;
-  int CK, K2C, VC, TC, ntile, rep;
+  int n0, nown, c0, ncol, ch0, nch;
+  int CK, K2C, TC, ntile, rep;
 };
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+
+__device__ __forceinline__ int own_first(int g, int d_ff, int G) { return (int)((int64_t)g * d_ff / G); }
 
 // Both roles execute exactly the same sequence of workgroup barriers:
 //   per token:  1 (input loaded) [+2 when the input needs normalising]
-//   per layer:  2 per K1 tile, then A, S, K, V, P, B, T, and either Y (last
-//               layer) or C, R1, R2; the failure flag is checked after A, B, T, C.
+//   per layer:  2 per K1 tile, then A, S, M, O, L, V, and either Y (last
+//               layer) or C, R1, R2; the failure flag is read after A, M, L and C.
 __device__ __forceinline__ void bar() { __syncthreads(); }
+
+
+
+// Per-neuron sums of one tile's chunk products.  Wave wv takes neurons
+// wv, wv + 8, ...; in the common case (one tile, rows of at most 192 chunks,
+// at most 64 neurons) all of a wave's LDS reads are issued before any sum.
+__device__ __forceinline__ void reduce_tile(const DecGeo& g, DecShared& S, int tile, int lane, int wv) {
+  const int TILE = kStreamers * kDecMaxC;
+  const int tb = tile * TILE, te = min(g.TC, tb + TILE);
+  if (g.ntile == 1 && g.CK <= 192) {
+    float v[8][3];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = wv + 8 * u;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int c = j * g.CK + lane + 64 * k;
+        const bool ok = j < g.nown && lane + 64 * k < g.CK;
+        v[u][k] = S.u.part[ok ? c : TILE];
+        v[u][k] = ok ? v[u][k] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = wv + 8 * u;
+      const float s = wave_sum_dpp(v[u][0] + v[u][1] + v[u][2]);
+      if (lane == 0 && j < g.nown) S.h[j] = s;
+    }
+    return;
+  }
+  for (int j = tb / g.CK + wv; j <= (te - 1) / g.CK; j += 8) {
+    const int a = max(j * g.CK, tb), b = min((j + 1) * g.CK, te);
+    float s = 0.f;
+    for (int c = a + lane; c < b; c += 64) s += S.u.part[c - tb];
+    s = wave_sum_dpp(s);
+    if (lane == 0) S.h[j] += s;
+  }
+}
 
 // ---------------------------------------------------------------- streamer role
 template <typename W>
@@ -133,9 +191,16 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
   const int sid = threadIdx.x - kWorkers, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int TILE = kStreamers * kDecMaxC;
   u32x4 pre[kDecMaxC];
+  // q offset of each register chunk of tile 0 (fixed for the whole kernel)
+  int qoff[kDecMaxC];
+#pragma unroll
+  for (int m = 0; m < kDecMaxC; ++m) {
+    const int c = sid + kStreamers * m;
+    qoff[m] = c < g.TC ? (c % g.CK) * CN : 0;
+  }
   // Branch-free: chunks past the slab end re-read its last chunk (in bounds) and
-  // are ignored by the dot products; with no branches the loads issue
-  // back to back instead of each waiting for the previous one.
+  // their products go to a dummy slot; with no branches the loads issue back to
+  // back and the LDS reads of consecutive chunks overlap.
   auto load_tile = [&](int layer, int tile) {
     const char* slab = (const char*)tab_k1[layer] + (size_t)g.n0 * g.r * sizeof(W);
 #pragma unroll
@@ -158,26 +223,25 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
 #pragma unroll
         for (int m = 0; m < kDecMaxC; ++m) {
           const int c = tile * TILE + sid + kStreamers * m;
-          if (c < g.TC) {
-            float wf[CN];
-            Chunk<W>::widen(pre[m], wf);
-            const float* qq = S.q + (c % g.CK) * CN;
-            float acc = 0.f;
+          const bool ok = c < g.TC;
+          const int qo = tile == 0 ? qoff[m] : (ok ? (c % g.CK) * CN : 0);
+          float wf[CN];
+          Chunk<W>::widen(pre[m], wf);
+          const f32x4* qq = reinterpret_cast<const f32x4*>(S.q + qo);  // 16-byte aligned
+          float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < CN; ++e) acc += wf[e] * qq[e];
-            S.part[c - tile * TILE] = acc;
+          for (int e4 = 0; e4 < CN / 4; ++e4) {
+            const f32x4 qv = qq[e4];
+            acc += wf[4 * e4] * qv.x + wf[4 * e4 + 1] * qv.y + wf[4 * e4 + 2] * qv.z + wf[4 * e4 + 3] * qv.w;
           }
+          S.u.part[ok ? c - tile * TILE : TILE] = acc;
+          // at most three chunks' q reads in flight: enough to cover the LDS
+          // latency without holding every chunk's q in registers
+          if (m % 3 == 2) __builtin_amdgcn_sched_barrier(0);
         }
         bar();
         // per-neuron sums of this tile's chunks (waves 4..7 take every other neuron)
-        const int tb = tile * TILE, te = min(g.TC, tb + TILE);
-        for (int j = tb / g.CK + wv; j <= (te - 1) / g.CK; j += 8) {
-          const int a = max(j * g.CK, tb), b = min((j + 1) * g.CK, te);
-          float s = 0.f;
-          for (int c = a + lane; c < b; c += 64) s += S.part[c - tb];
-          s = wave_sum(s);
-          if (lane == 0) S.h[j] += s;
-        }
+        reduce_tile(g, S, tile, lane, wv);
         bar();
       }
       // stream the next slab while the rest of this layer runs
@@ -186,23 +250,82 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
       bar();  // A
       if (S.fail) return;
       bar();  // S
-      bar();  // K
+      bar();  // M
+      if (S.fail) return;
+      bar();  // O
+      bar();  // L
+      if (S.fail) return;
       bar();  // V
-      bar();  // P
-      bar();  // B
-      if (S.fail) return;
-      bar();  // T
-      if (S.fail) return;
       if (last) {
         bar();  // Y
         continue;
       }
+      bar();  // C0
       bar();  // C
       if (S.fail) return;
       bar();  // R1
       bar();  // R2
     }
   }
+}
+
+// K2^T q[r:] for one owned neuron, by one wave (chunks strided over lanes).
+template <typename W>
+__device__ __forceinline__ float k2_dot(const char* row, const float* qr, int K2C, int lane) {
+  constexpr int CN = Chunk<W>::N;
+  float s = 0.f;
+  for (int c0 = 0; c0 < K2C; c0 += 192) {
+    u32x4 raw[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) raw[k] = load16(row + (size_t)min(c0 + lane + 64 * k, K2C - 1) * 16);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int cc = c0 + lane + 64 * k;
+      float wf[CN];
+      Chunk<W>::widen(raw[k], wf);
+      const float* qq = qr + (cc < K2C ? cc : 0) * CN;
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < CN; ++e) a += wf[e] * qq[e];
+      s += cc < K2C ? a : 0.f;
+    }
+  }
+  return wave_sum_dpp(s);
+}
+
+// K2^T q[r:] for up to three owned neurons at once (j0, j1, j2; -1 = none), by one
+// wave: every K2 load of the three rows is issued before any is used.
+template <typename W>
+__device__ __forceinline__ void k2_dot3(const char* k2base, size_t k2row, int j0, int j1, int j2, const float* qr,
+                                        int K2C, int lane, float* out) {
+  constexpr int CN = Chunk<W>::N;
+  float s[3] = {0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < K2C; c0 += 192) {
+    u32x4 raw[3][3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int ju = u == 0 ? j0 : (u == 1 ? (j1 >= 0 ? j1 : j0) : (j2 >= 0 ? j2 : j0));
+      const char* row = k2base + (size_t)ju * k2row;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) raw[u][k] = load16(row + (size_t)min(c0 + lane + 64 * k, K2C - 1) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int cc = c0 + lane + 64 * k;
+        float wf[CN];
+        Chunk<W>::widen(raw[u][k], wf);
+        const float* qq = qr + (cc < K2C ? cc : 0) * CN;
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < CN; ++e) a += wf[e] * qq[e];
+        s[u] += cc < K2C ? a : 0.f;
+        __builtin_amdgcn_sched_barrier(0);  // one chunk's q reads at a time
+      }
+  }
+#pragma unroll
+  for (int u = 0; u < 3; ++u) out[u] = wave_sum_dpp(s[u]);
 }
 
 // ---------------------------------------------------------------- worker role
@@ -213,6 +336,8 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int TILE = kStreamers * kDecMaxC;
   const int d_model = g.d_model, G = g.G, w = g.w;
+  const size_t k2row = (size_t)(d_model - g.r) * sizeof(W);
+  const size_t vrow = (size_t)d_model * sizeof(W);
   uint32_t tag = S.tag0;
 
   for (int t = 0; t < g.T; ++t) {
@@ -221,7 +346,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
     if (p.q_prenorm) {
       float ss = 0.f;
       for (int c = tid; c < d_model; c += kWorkers) ss += S.q[c] * S.q[c];
-      ss = wave_sum(ss);
+      ss = wave_sum_dpp(ss);
       if (lane == 0) S.wred[wv] = ss;
       bar();
       const float inv = 1.f / sqrtf((S.wred[0] + S.wred[1] + S.wred[2] + S.wred[3]) / (float)d_model + p.eps);
@@ -232,222 +357,305 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       const bool last = l == g.L - 1;
       const uint32_t tagA = ++tag, tagB = ++tag, tagC = last ? 0u : ++tag;
       const size_t trow = (size_t)t * p.total_layers + p.layer_offset + l;
+      const char* k2base = (const char*)tab_k2[l] + (size_t)g.n0 * k2row;
       if (p.tr_q && w == 0)
         for (int c = tid; c < d_model; c += kWorkers) p.tr_q[trow * d_model + c] = S.q[c];
-      for (int j = tid; j < g.nown; j += kWorkers) S.h[j] = 0.f;
+      if (tid < g.nown) S.h[tid] = 0.f;
 
       // ---------------- predictor: the streamers form chunk dots, all waves sum them
       for (int tile = 0; tile < g.ntile; ++tile) {
-        bar();
-        const int tb = tile * TILE, te = min(g.TC, tb + TILE);
-        for (int j = tb / g.CK + wv; j <= (te - 1) / g.CK; j += 8) {
-          const int a = max(j * g.CK, tb), b = min((j + 1) * g.CK, te);
-          float s = 0.f;
-          for (int c = a + lane; c < b; c += 64) s += S.part[c - tb];
-          s = wave_sum(s);
-          if (lane == 0) S.h[j] += s;
-        }
-        bar();
+        bar();  // G1
+        reduce_tile(g, S, tile, lane, wv);
+        bar();  // G2
       }
 
-      // ---------------- exchange A: moments of the predictor scores -> theta
+      const bool own = lane < g.nown;
+      const float hj = own ? S.h[lane] : 0.f;
       if (wv == 0) {
-        float s = 0.f;
-        for (int j = lane; j < g.nown; j += 64) s += S.h[j];
-        const float mean_w = wave_sum(s) / (float)g.nown;
-        float q2 = 0.f;
-        for (int j = lane; j < g.nown; j += 64) {
-          const float dv = S.h[j] - mean_w;
-          q2 += dv * dv;
-        }
-        const float m2_w = wave_sum(q2);
+        // ---------------- exchange A: per-workgroup (mean, M2) -> theta
+        const float mean_w = wave_sum_dpp(hj) / (float)g.nown;
+        const float dv = own ? hj - mean_w : 0.f;
+        const float m2_w = wave_sum_dpp(dv * dv);
         if (lane < kRep) {
           uint64_t* dst = p.stats + (size_t)lane * p.stats_stride + 2 * w;
           put_tagged(dst, mean_w, tagA);
           put_tagged(dst + 1, m2_w, tagA);
         }
+        // poll the 4 mean words of this lane's records first (few words per
+        // polling round), then read the M2 words, which are then normally there
         const uint64_t* src = p.stats + (size_t)g.rep * p.stats_stride;
         constexpr int KA = 8;  // 4 records (G <= 256) x 2 words per lane
-        const uint64_t* ptrs[KA];
+        const uint64_t* pm[KA / 2];
+        const uint64_t* pq[KA / 2];
 #pragma unroll
         for (int k = 0; k < KA / 2; ++k) {
           const int gg = lane + 64 * k;
-          ptrs[2 * k] = gg < G ? src + 2 * gg : nullptr;
-          ptrs[2 * k + 1] = gg < G ? src + 2 * gg + 1 : nullptr;
+          pm[k] = gg < G ? src + 2 * gg : nullptr;
+          pq[k] = gg < G ? src + 2 * gg + 1 : nullptr;
         }
-        float vals[KA];
-        const bool ok = gather_tagged<KA>(ptrs, tagA, vals, p.hdr, p.spin_limit);
-        Moments acc{0.f, 0.f, 0.f};
+        float vm[KA / 2], vq[KA / 2], vals[KA];
+        bool ok = gather_tagged<KA / 2>(pm, tagA, vm, p.hdr, p.spin_limit);
+        ok = ok && gather_tagged<KA / 2>(pq, tagA, vq, p.hdr, p.spin_limit);
+#pragma unroll
+        for (int k = 0; k < KA / 2; ++k) {
+          vals[2 * k] = vm[k];
+          vals[2 * k + 1] = vq[k];
+        }
+        // two passes over the records: the mean, then the squared deviations
+        // about it (Chan et al.'s combination, written as two plain sums)
+        float s1 = 0.f;
 #pragma unroll
         for (int k = 0; k < KA / 2; ++k) {
           const int gg = lane + 64 * k;
-          if (gg < G) {
-            const float ng = (float)((int)((int64_t)(gg + 1) * g.d_ff / G) - (int)((int64_t)gg * g.d_ff / G));
-            acc = merge(acc, Moments{ng, vals[2 * k], vals[2 * k + 1]});
-          }
+          const float ng = (float)(own_first(gg + 1, g.d_ff, G) - own_first(gg, g.d_ff, G));
+          s1 += gg < G ? ng * vals[2 * k] : 0.f;
         }
-        const Moments tot = wave_merge(acc);
-        if (lane == 0) S.theta = tot.mean + sqrtf(tot.m2 / (float)g.d_ff) * p.z;
+        const float mu = wave_sum_dpp(s1) / (float)g.d_ff;
+        float s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < KA / 2; ++k) {
+          const int gg = lane + 64 * k;
+          const float ng = (float)(own_first(gg + 1, g.d_ff, G) - own_first(gg, g.d_ff, G));
+          const float d = vals[2 * k] - mu;
+          s2 += gg < G ? vals[2 * k + 1] + ng * d * d : 0.f;
+        }
+        const float m2 = wave_sum_dpp(s2);
+        if (lane == 0) S.theta = mu + sqrtf(m2 / (float)g.d_ff) * p.z;
         if (__builtin_amdgcn_ballot_w64(!ok) != 0 && lane == 0) {
           S.fail = 1;
           raise_failure(p.hdr);
+        }
+      } else {
+        // ---------------- waves 1..3, meanwhile: K2 dots of the top candidates
+        int rank = 0;
+        for (int i = 0; i < g.nown; ++i) {
+          const float hi = S.h[i];
+          rank += (hi > hj || (hi == hj && i < lane)) ? 1 : 0;
+        }
+        const uint64_t cmask = __builtin_amdgcn_ballot_w64(own && rank < kCand);
+        if (wv == 1 && lane == 0) S.candmask = cmask;
+        // this wave's candidates: every third one (positions wv-1, wv+2, ...);
+        // their K2 rows are loaded three at a time, all loads issued first
+        const bool isc = own && rank < kCand;
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cmask, 0));
+        int jsel[6];
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          const uint64_t bb = __builtin_amdgcn_ballot_w64(isc && pos == (wv - 1) + 3 * u);
+          jsel[u] = bb ? __builtin_ctzll(bb) : -1;
+        }
+#pragma unroll
+        for (int b0 = 0; b0 < 6; b0 += 3) {
+          if (jsel[b0] >= 0) {
+            float d3[3];
+            k2_dot3<W>(k2base, k2row, jsel[b0], jsel[b0 + 1], jsel[b0 + 2], S.q + g.r, g.K2C, lane, d3);
+            if (lane == 0) {
+#pragma unroll
+              for (int u = 0; u < 3; ++u)
+                if (jsel[b0 + u] >= 0) S.g[jsel[b0 + u]] = d3[u];
+            }
+          }
         }
       }
       bar();  // A
       if (S.fail) return;
       const float theta = S.theta;
 
-      // ---------------- selection of the owned neurons (ascending)
+      // ---------------- selection, gated values, publish the record
       if (wv == 0) {
-        int base = 0;
-        for (int j0 = 0; j0 < g.nown; j0 += 64) {
-          const int j = j0 + lane;
-          const bool on = j < g.nown && S.h[j] > theta;
-          const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
-          const int pos =
-              base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-          if (on) {
-            S.sel[pos] = j;
-            S.m[pos] = S.h[j] - theta;
-          }
-          base += __builtin_popcountll(bal);
+        const bool on = own && hj > theta;
+        const uint64_t M = __builtin_amdgcn_ballot_w64(on);
+        uint64_t miss = M & ~S.candmask;
+        while (miss) {  // selected neurons outside the candidates (rare)
+          const int j = __builtin_ctzll(miss);
+          miss &= miss - 1;
+          const float d = k2_dot<W>(k2base + (size_t)j * k2row, S.q + g.r, g.K2C, lane);
+          if (lane == 0) S.g[j] = d;
         }
-        if (lane == 0) S.nsel = base;
+        const float cval = on ? gelu_tanh(hj - theta) * S.g[lane < 64 ? lane : 0] : 0.f;
+        const int e = __builtin_amdgcn_mbcnt_hi((uint32_t)(M >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)M, 0));
+        if (on) {
+          if (e < kRecEntries) {
+#pragma unroll
+            for (int rp = 0; rp < kRep; ++rp)
+              put_tagged(p.rec + (size_t)rp * p.rec_stride + (size_t)w * kRecWords + 2 + e, cval, tagB);
+          } else {
+            put_tagged(p.ovf + (size_t)w * kOvfWords + (e - kRecEntries), cval, tagB);
+          }
+        }
+        if (lane < 2 * kRep) {
+          const int rp = lane >> 1;
+          put_tagged_u32(p.rec + (size_t)rp * p.rec_stride + (size_t)w * kRecWords + (lane & 1),
+                         (lane & 1) ? (uint32_t)(M >> 32) : (uint32_t)M, tagB);
+        }
       }
       bar();  // S
-      const int nsel = S.nsel;
 
-      // ---------------- K2 gather-dot and gate: c = GELU(m) * (K2^T q[r:])
-      for (int e = wv; e < nsel; e += kWorkers / 64) {
-        const char* row = (const char*)tab_k2[l] + (size_t)(g.n0 + S.sel[e]) * (d_model - g.r) * sizeof(W);
-        float s = 0.f;
-        for (int cc = lane; cc < g.K2C; cc += 64) {
-          float wf[CN];
-          Chunk<W>::widen(load16(row + (size_t)cc * 16), wf);
-          const float* qq = S.q + g.r + cc * CN;
+      // ---------------- exchange B: every workgroup's record (one thread each)
+      bool okB = true;
+      uint64_t Mg = 0;
+      {
+        // one thread per record: poll its first mask word alone, then read the
+        // second mask word and the entries it announces (re-polling stragglers)
+        const int gg = tid;
+        const uint64_t* rp = p.rec + (size_t)g.rep * p.rec_stride + (size_t)(gg < G ? gg : 0) * kRecWords;
+        float m0[1];
+        const uint64_t* p0[1] = {gg < G ? rp : nullptr};
+        okB = gather_tagged<1>(p0, tagB, m0, p.hdr, p.spin_limit);
+        float m1[1];
+        const uint64_t* p1[1] = {gg < G ? rp + 1 : nullptr};
+        okB = okB && gather_tagged<1>(p1, tagB, m1, p.hdr, p.spin_limit);
+        if (gg < G && okB) Mg = ((uint64_t)__float_as_uint(m1[0]) << 32) | __float_as_uint(m0[0]);
+        const int n = __builtin_popcountll(Mg);
+#pragma unroll 1
+        for (int h0 = 0; h0 < kRecEntries; h0 += kRecEntries / 2) {
+          const uint64_t* pe[kRecEntries / 2];
 #pragma unroll
-          for (int e2 = 0; e2 < CN; ++e2) s += wf[e2] * qq[e2];
+          for (int k = 0; k < kRecEntries / 2; ++k) pe[k] = (gg < G && h0 + k < n) ? rp + 2 + h0 + k : nullptr;
+          float ev[kRecEntries / 2];
+          okB = okB && gather_tagged<kRecEntries / 2>(pe, tagB, ev, p.hdr, p.spin_limit);
+#pragma unroll
+          for (int k = 0; k < kRecEntries / 2; ++k)
+            if (gg < G && h0 + k < n) S.t.stage[gg][h0 + k] = ev[k];
         }
-        s = wave_sum(s);
-        if (lane == 0) S.c[e] = gelu_tanh(S.m[e]) * s;
+        if (gg < G) S.cnt[gg] = okB ? __builtin_popcountll(Mg) : 0;
       }
-      bar();  // K
-
-      // ---------------- V rows: partial y of this workgroup, staged in LDS
-      for (int vc = tid; vc < g.VC; vc += kWorkers) {
-        float acc[CN];
+      if (!okB) S.fail = 1;
+      bar();  // M
+      if (S.fail) {
+        if (tid == 0) raise_failure(p.hdr);
+        return;
+      }
+      if (wv == 0) {  // exclusive prefix of the counts, workgroup order
+        int c4[4], s4 = 0;
 #pragma unroll
-        for (int e2 = 0; e2 < CN; ++e2) acc[e2] = 0.f;
-        for (int e0 = 0; e0 < nsel; e0 += 4) {
-          u32x4 raw[4];
+        for (int k = 0; k < 4; ++k) {
+          const int gg = 4 * lane + k;
+          c4[k] = gg < G ? S.cnt[gg] : 0;
+          s4 += c4[k];
+        }
+        int run = wave_excl_scan(s4, lane);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (e0 + u < nsel)
-              raw[u] = load16((const char*)tab_v[l] + (size_t)(g.n0 + S.sel[e0 + u]) * d_model * sizeof(W) +
-                              (size_t)vc * 16);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (e0 + u < nsel) {
-              float wf[CN];
-              Chunk<W>::widen(raw[u], wf);
-              const float cf = S.c[e0 + u];
-#pragma unroll
-              for (int e2 = 0; e2 < CN; ++e2) acc[e2] += cf * wf[e2];
+        for (int k = 0; k < 4; ++k) {
+          const int gg = 4 * lane + k;
+          if (gg < G) S.off[gg] = run;
+          run += c4[k];
+        }
+        if (lane == 63) S.ntot = run;
+      }
+      bar();  // O
+      // place this record's entries into the list (ascending neuron order)
+      {
+        const int gg = tid;
+        if (gg < G) {
+          const int n = __builtin_popcountll(Mg), o = S.off[gg], nb = own_first(gg, g.d_ff, G);
+          uint64_t mm = Mg;
+          for (int e = 0; e < n; ++e) {
+            const int j = __builtin_ctzll(mm);
+            mm &= mm - 1;
+            float cv;
+            if (e < kRecEntries) {
+              cv = S.t.stage[gg][e];
+            } else {
+              const uint64_t* op[1] = {p.ovf + (size_t)gg * kOvfWords + (e - kRecEntries)};
+              float ov[1];
+              okB &= gather_tagged<1>(op, tagB, ov, p.hdr, p.spin_limit);
+              cv = ov[0];
             }
-          }
-        }
-#pragma unroll
-        for (int e2 = 0; e2 < CN; ++e2) S.red[vc * CN + e2] = acc[e2];
-      }
-      bar();  // V
-
-      // ---------------- exchange B: publish partial y (and the selected count)
-      {
-        uint64_t* mine = p.part + (size_t)w * p.part_stride;
-        for (int c = tid; c < d_model; c += kWorkers) put_tagged(mine + c, S.red[c], tagB);
-        if (tid == 0) put_tagged_u32(mine + d_model, (uint32_t)nsel, tagB);
-      }
-      bar();  // P
-      // gather the owned columns of every workgroup's partial
-      {
-        bool okB = true;
-        const int total = G * g.ncol;
-        constexpr int KB = 8;
-        for (int i0 = 0; i0 < total; i0 += kWorkers * KB) {
-          const uint64_t* ptrs[KB];
-#pragma unroll
-          for (int k = 0; k < KB; ++k) {
-            const int i = i0 + tid + kWorkers * k;
-            const int gg = i / g.ncol, cc = i - gg * g.ncol;
-            ptrs[k] = i < total ? p.part + (size_t)gg * p.part_stride + g.c0 + cc : nullptr;
-          }
-          float vals[KB];
-          okB &= gather_tagged<KB>(ptrs, tagB, vals, p.hdr, p.spin_limit);
-#pragma unroll
-          for (int k = 0; k < KB; ++k) {
-            const int i = i0 + tid + kWorkers * k;
-            if (i < total) S.red[i] = vals[k];
+            if (o + e < kListMax) {
+              S.u.list.c[o + e] = cv;
+              S.u.list.idx[o + e] = (uint16_t)(nb + j);
+            }
           }
         }
         if (!okB) S.fail = 1;
       }
-      bar();  // B
+      bar();  // L
       if (S.fail) {
         if (tid == 0) raise_failure(p.hdr);
         return;
       }
-      // fixed-order sum over the G partials of each owned column
-      for (int cc = wv; cc < g.ncol; cc += kWorkers / 64) {
-        float s = 0.f;
-        for (int gg = lane; gg < G; gg += 64) s += S.red[gg * g.ncol + cc];
-        s = wave_sum(s);
-        if (lane == 0) S.ycol[cc] = s;
+      const int ntot = S.ntot;
+      if (w == 0 && tid == 0) {
+        if (p.tr_counts) p.tr_counts[trow] = ntot;
+        if (p.tr_theta) p.tr_theta[trow] = theta;
       }
-      // trace: threshold, counts and indices of this layer
-      if ((p.tr_counts || p.tr_idx || p.tr_theta) && wv == 0) {
-        bool okT = true;
-        int before = 0, all = 0;
-        for (int g0 = 0; g0 < G; g0 += 64) {
-          const int gg = g0 + lane;
-          const uint64_t* ptr[1] = {gg < G ? p.part + (size_t)gg * p.part_stride + d_model : nullptr};
-          float v1[1] = {0.f};
-          okT &= gather_tagged<1>(ptr, tagB, v1, p.hdr, p.spin_limit);
-          const int cnt = gg < G ? (int)__float_as_uint(v1[0]) : 0;
-          before += wave_sum_int(gg < w ? cnt : 0);
-          all += wave_sum_int(cnt);
-        }
-        if (p.tr_idx)
-          for (int e = lane; e < nsel; e += 64) {
-            const int64_t pos = before + e;
-            if (pos < p.tr_cap) p.tr_idx[trow * p.tr_cap + pos] = g.n0 + S.sel[e];
+      if (w == 0 && p.tr_idx)
+        for (int e = tid; e < ntot && e < p.tr_cap; e += kWorkers) p.tr_idx[trow * p.tr_cap + e] = S.u.list.idx[e];
+
+      // ---------------- V: the owned columns of y over every selected neuron.
+      // Ownership is by 16-byte chunks of a V row (at most 2 per workgroup per
+      // pass); thread t takes entries t, t + 256, ... and loads each entry's
+      // owned chunks with 16-byte loads, three entries at a time.  Column sums
+      // then run over lanes (DPP) and waves in a fixed order.
+      {
+        const int n = min(ntot, kListMax);
+        const char* vbase = (const char*)tab_v[l] + (size_t)g.ch0 * 16;
+        float acc[2 * CN];
+#pragma unroll
+        for (int i = 0; i < 2 * CN; ++i) acc[i] = 0.f;
+        for (int e0 = tid; e0 < n; e0 += 3 * kWorkers) {
+          u32x4 raw[3][2];
+          float cv[3];
+#pragma unroll
+          for (int u = 0; u < 3; ++u) {
+            const int e = e0 + u * kWorkers;
+            const bool ok = e < n;
+            const char* row = vbase + (size_t)(ok ? S.u.list.idx[e] : 0) * vrow;
+            cv[u] = ok ? S.u.list.c[e] : 0.f;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) raw[u][hh] = load16(row + (size_t)(hh < g.nch ? hh : 0) * 16);
           }
-        if (w == 0 && lane == 0) {
-          if (p.tr_counts) p.tr_counts[trow] = all;
-          if (p.tr_theta) p.tr_theta[trow] = theta;
+#pragma unroll
+          for (int u = 0; u < 3; ++u) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              float wf[CN];
+              Chunk<W>::widen(raw[u][hh], wf);
+#pragma unroll
+              for (int i = 0; i < CN; ++i) acc[hh * CN + i] += cv[u] * wf[i];
+            }
+          }
         }
-        if (__builtin_amdgcn_ballot_w64(!okT) != 0 && lane == 0) S.fail = 1;
+#pragma unroll
+        for (int i = 0; i < 2 * CN; ++i) {
+          if (i < g.ncol) {
+            const float sum = wave_sum_dpp(acc[i]);
+            if (lane == 0) S.colpart[wv][i] = sum;
+          }
+        }
       }
-      bar();  // T
-      if (S.fail) {
-        if (tid == 0) raise_failure(p.hdr);
-        return;
-      }
+      bar();  // V
+      const float ymine =
+          tid < g.ncol ? ((S.colpart[0][tid] + S.colpart[1][tid]) + S.colpart[2][tid]) + S.colpart[3][tid] : 0.f;
       if (last) {
-        for (int cc = tid; cc < g.ncol; cc += kWorkers) p.y_out[(size_t)t * d_model + g.c0 + cc] = S.ycol[cc];
+        if (tid < g.ncol) p.y_out[(size_t)t * d_model + g.c0 + tid] = ymine;
         bar();  // Y
         continue;
       }
 
       // ---------------- exchange C: owned columns of y -> every workgroup
       {
-        for (int i = tid; i < kRep * g.ncol; i += kWorkers) {
-          const int rp = i / g.ncol, cc = i - rp * g.ncol;
-          put_tagged(p.ycol + (size_t)rp * p.ycol_stride + g.c0 + cc, S.ycol[cc], tagC);
-        }
+        if (tid < g.ncol)
+#pragma unroll
+          for (int rp = 0; rp < kRep; ++rp) put_tagged(p.ycol + (size_t)rp * p.ycol_stride + g.c0 + tid, ymine, tagC);
+        // then this owner's "done" word (one per replica)
+        if (tid < kRep) put_tagged_u32(p.ycol + (size_t)tid * p.ycol_stride + p.ycol_done + w, 1u, tagC);
         bool okC = true;
         const uint64_t* src = p.ycol + (size_t)g.rep * p.ycol_stride;
-        constexpr int KC = 8;
-        for (int c00 = 0; c00 < d_model; c00 += kWorkers * KC) {
+        {
+          float dn[1];
+          const uint64_t* pd[1] = {tid < G ? src + p.ycol_done + tid : nullptr};
+          okC = gather_tagged<1>(pd, tagC, dn, p.hdr, p.spin_limit);
+        }
+        if (!okC) S.fail = 1;
+      }
+      bar();  // C0
+      {
+        bool okC = S.fail == 0;
+        const uint64_t* src = p.ycol + (size_t)g.rep * p.ycol_stride;
+        constexpr int KC = 5;
+        for (int c00 = 0; okC && c00 < d_model; c00 += kWorkers * KC) {
           const uint64_t* ptrs[KC];
 #pragma unroll
           for (int k = 0; k < KC; ++k) {
@@ -472,13 +680,15 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       // RMS normalisation (identical order in every workgroup)
       {
         float ss = 0.f;
+#pragma unroll 4
         for (int c = tid; c < d_model; c += kWorkers) ss += S.q[c] * S.q[c];
-        ss = wave_sum(ss);
+        ss = wave_sum_dpp(ss);
         if (lane == 0) S.wred[wv] = ss;
       }
       bar();  // R1
       {
         const float inv = 1.f / sqrtf((S.wred[0] + S.wred[1] + S.wred[2] + S.wred[3]) / (float)d_model + p.eps);
+#pragma unroll 4
         for (int c = tid; c < d_model; c += kWorkers) S.q[c] *= inv;
       }
       bar();  // R2
@@ -502,13 +712,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
   g.r = p.r;
   g.L = p.n_layers;
   g.T = p.T;
-  g.n0 = (int)((int64_t)g.w * g.d_ff / g.G);
-  g.nown = (int)((int64_t)(g.w + 1) * g.d_ff / g.G) - g.n0;
-  g.c0 = (int)((int64_t)g.w * g.d_model / g.G);
-  g.ncol = (int)((int64_t)(g.w + 1) * g.d_model / g.G) - g.c0;
+  g.n0 = own_first(g.w, g.d_ff, g.G);
+  g.nown = own_first(g.w + 1, g.d_ff, g.G) - g.n0;
+  // column owner index: the workgroups of one XCD (w = x + 8j) own one
+  // contiguous range of columns, so each V row segment is read once per XCD
+  const int o = (g.G % 8 == 0) ? (g.w & 7) * (g.G / 8) + (g.w >> 3) : g.w;
+  const int vch = g.d_model / CN;  // 16-byte chunks per V row
+  g.ch0 = (int)((int64_t)o * vch / g.G);
+  g.nch = (int)((int64_t)(o + 1) * vch / g.G) - g.ch0;
+  g.c0 = g.ch0 * CN;
+  g.ncol = g.nch * CN;
   g.CK = g.r / CN;
   g.K2C = (g.d_model - g.r) / CN;
-  g.VC = g.d_model / CN;
   g.TC = g.nown * g.CK;
   g.ntile = (g.TC + kStreamers * kDecMaxC - 1) / (kStreamers * kDecMaxC);
   g.rep = xcc_id();
@@ -527,22 +742,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct DecodeLayout {
-  size_t hdr, stats, part, ycol, qbuf, total;
-  int stats_stride, part_stride, ycol_stride;
+  size_t hdr, stats, rec, ovf, ycol, qbuf, total;
+  int stats_stride, rec_stride, ycol_stride, ycol_done;
 };
 
 static DecodeLayout decode_layout(int64_t d_model, int64_t T, int grid, int n_layers) {
   DecodeLayout L;
-  L.stats_stride = (int)round_up((size_t)2 * grid + 64, 512);      // words; replicas 4 KB+ apart
-  L.part_stride = (int)round_up((size_t)d_model + 1, 16);           // words, 128-byte rows
-  L.ycol_stride = (int)round_up((size_t)d_model + 64, 512);
+  L.stats_stride = (int)round_up((size_t)2 * grid + 64, 512);  // words; replicas 4 KB+ apart
+  L.rec_stride = (int)round_up((size_t)kRecWords * grid + 64, 512);
+  L.ycol_done = (int)round_up((size_t)d_model, 64);  // words: owners' "done" flags follow the columns
+  L.ycol_stride = (int)round_up((size_t)L.ycol_done + grid + 64, 512);
   size_t off = 0;
   L.hdr = off;
   off += 256;
   L.stats = off;
   off += round_up((size_t)kRep * L.stats_stride * 8, 256);
-  L.part = off;
-  off += round_up((size_t)grid * L.part_stride * 8, 256);
+  L.rec = off;
+  off += round_up((size_t)kRep * L.rec_stride * 8, 256);
+  L.ovf = off;
+  off += round_up((size_t)grid * kOvfWords * 8, 256);
   L.ycol = off;
   off += round_up((size_t)kRep * L.ycol_stride * 8, 256);
   L.qbuf = off;
@@ -602,11 +820,13 @@ static hipError_t launch_decode_t(const spark_ffn_shape& s, const spark_ffn_weig
     p.tr_cap = trace ? trace->cap : 0;
     p.hdr = (uint64_t*)(base + Lo.hdr);
     p.stats = (uint64_t*)(base + Lo.stats);
-    p.part = (uint64_t*)(base + Lo.part);
+    p.rec = (uint64_t*)(base + Lo.rec);
+    p.ovf = (uint64_t*)(base + Lo.ovf);
     p.ycol = (uint64_t*)(base + Lo.ycol);
     p.stats_stride = Lo.stats_stride;
-    p.part_stride = Lo.part_stride;
+    p.rec_stride = Lo.rec_stride;
     p.ycol_stride = Lo.ycol_stride;
+    p.ycol_done = Lo.ycol_done;
     p.spin_limit = 1u << 22;
     void* args[] = {&p};
     e = hipLaunchCooperativeKernel((const void*)decode_kernel<W>, dim3(grid), dim3(kDecodeThreads), args, 0, st);

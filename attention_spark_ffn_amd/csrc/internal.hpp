@@ -18,8 +18,8 @@ hipError_t launch_stat_topk(const float* x, int64_t rows, int64_t d, int64_t ldx
 constexpr int kDecodeMaxLayersPerLaunch = 32;
 constexpr int kDecodeThreads = 512;
 constexpr int kDecodeMaxDModel = 8192;
-constexpr int kDecodeMaxNeuronsPerWG = 256;
-constexpr int kDecodeMaxColsPerWG = 512;
+constexpr int kDecodeMaxNeuronsPerWG = 64;  // one 64-bit selection mask per workgroup
+constexpr int kDecodeMaxColsPerWG = 32;
 
 size_t decode_workspace_bytes(int64_t d_model, int64_t d_ff, int n_layers, int64_t T, int grid);
 int decode_grid(int64_t d_ff);  // workgroups of the persistent grid on the current device
