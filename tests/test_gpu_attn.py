@@ -1,0 +1,67 @@
+"""Spark attention decode on the GPU against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import attention_spark_ffn_amd as sf
+import oracle
+import synth
+from parity import check_index_set, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def run_attn(Hq, Hkv, n, hd, r, ka, seed, tol=2e-2, scale=None):
+    qb, k1b, k2b, vb = synth.attn_inputs(seed, Hq, Hkv, n, hd, r, scale=scale)
+    cap = min(n, 4096)
+    out, counts, idx, theta = sf.spark_attn_decode(to_dev(qb), to_dev(k1b), to_dev(k2b), to_dev(vb), ka, cap=cap)
+    torch.cuda.synchronize()
+    out, counts, idx, theta = (t.cpu().numpy() for t in (out, counts, idx, theta))
+    ref = oracle.spark_attn_decode(qb, k1b, k2b, vb, ka)
+    dense = n <= ka
+    for h in range(Hq):
+        s = ref["scores"][h]
+        if dense:
+            assert counts[h] == n and np.isnan(theta[h])
+            assert np.array_equal(idx[h, :min(n, cap)], np.arange(min(n, cap)))
+        else:
+            sd = s.std()
+            check_index_set(idx[h], counts[h], cap, s, ref["theta"][h], sd, f"head {h}")
+            assert abs(theta[h] - ref["theta"][h]) <= 1e-5 * (abs(ref["theta"][h]) + sd)
+        assert rel_err(out[h], ref["out"][h]) <= tol, (h, rel_err(out[h], ref["out"][h]))
+    return counts
+
+
+@pytest.mark.parametrize("n", [4096, 32768])
+def test_attn_config(n):
+    """BASELINE's attention workload: 8 query heads on 4 KV heads, hd 256,
+    r 128, k_attn 256, Q/K/V ~ N(0,1)/16 in bf16."""
+    counts = run_attn(8, 4, n, 256, 128, 256, 0)
+    assert np.all(np.abs(counts - 256) <= 256 * 0.5)
+
+
+@pytest.mark.parametrize("Hq,Hkv,n,hd,r,ka", [
+    (8, 4, 200, 256, 128, 256),     # dense: fewer tokens than k_attn
+    (8, 4, 256, 256, 128, 256),     # dense at the boundary
+    (8, 4, 257, 256, 128, 256),     # one past the boundary
+    (4, 4, 1000, 128, 64, 100),     # no grouping, ragged
+    (8, 2, 5000, 64, 32, 300),      # group of 4
+    (2, 1, 70000, 256, 128, 512),   # long context
+    (1, 1, 33, 16, 8, 8),           # tiny
+])
+def test_attn_shapes(Hq, Hkv, n, hd, r, ka):
+    run_attn(Hq, Hkv, n, hd, r, ka, n + hd, scale=0.5)
+
+
+def test_attn_deterministic():
+    qb, k1b, k2b, vb = synth.attn_inputs(4, 8, 4, 32768, 256, 128)
+    args = [to_dev(a) for a in (qb, k1b, k2b, vb)]
+    a = sf.spark_attn_decode(*args, 256)
+    b = sf.spark_attn_decode(*args, 256)
+    for u, w in zip(a, b):
+        assert torch.equal(u, w)

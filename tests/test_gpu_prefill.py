@@ -1,0 +1,75 @@
+"""Spark FFN prefill on the GPU against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import attention_spark_ffn_amd as sf
+import oracle
+import synth
+from parity import check_index_set, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def run_prefill(dm, dff, r, k, T, seed, sample=None, tol=2e-2):
+    layer = synth.ffn_layer(seed, 0, dm, dff, r, "bf16")
+    Q = synth.queries(seed, T, dm, "bf16")
+    Y, tr = sf.spark_ffn_prefill(to_dev(Q), tuple(to_dev(a) for a in layer), k, r, trace=True)
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy()
+    tr = {key: v.cpu().numpy() for key, v in tr.items()}
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    ref = oracle.spark_ffn(Q[rows], *layer, r, k)
+    flips = 0
+    for i, t in enumerate(rows):
+        flips += check_index_set(tr["idx"][t, 0], tr["counts"][t, 0], dff, ref["h"][i], ref["theta"][i],
+                                 ref["std"][i], f"token {t}")
+        assert abs(tr["theta"][t, 0] - ref["theta"][i]) <= 1e-5 * (abs(ref["theta"][i]) + ref["std"][i])
+        assert rel_err(Y[t], ref["y"][i]) <= tol, (t, rel_err(Y[t], ref["y"][i]))
+    return flips
+
+
+def test_prefill_config():
+    """BASELINE's prefill workload: 4096 tokens through one 2304 x 9216 layer
+    (r 1152, k 737), bf16; a sample of 96 tokens against the oracle, spread
+    over every 128-row tile of the predictor GEMM."""
+    T = 4096
+    sample = np.sort(np.random.default_rng(0).choice(T, 96, replace=False))
+    run_prefill(2304, 9216, 1152, 737, T, 0, sample)
+
+
+@pytest.mark.parametrize("dm,dff,r,k,T", [
+    (256, 1024, 128, 82, 300),      # ragged token count (not a multiple of 128)
+    (512, 512, 192, 40, 130),
+    (1024, 2048, 512, 160, 64),
+    (136, 256, 64, 20, 1),          # one token
+    (2304, 9216, 1152, 737, 257),
+])
+def test_prefill_shapes(dm, dff, r, k, T):
+    run_prefill(dm, dff, r, k, T, dm + T)
+
+
+def test_prefill_deterministic():
+    layer = [to_dev(a) for a in synth.ffn_layer(3, 0, 2304, 9216, 1152, "bf16")]
+    Q = to_dev(synth.queries(3, 512, 2304, "bf16"))
+    a = sf.spark_ffn_prefill(Q, layer, 737, 1152)
+    b = sf.spark_ffn_prefill(Q, layer, 737, 1152)
+    assert torch.equal(a, b)
+
+
+def test_prefill_matches_decode_per_token():
+    # the same layer through the prefill path and the decode path (bf16 q)
+    dm, dff, r, k = 512, 1024, 256, 80
+    layer_np = synth.ffn_layer(8, 0, dm, dff, r, "bf16")
+    Qb = synth.queries(8, 16, dm, "bf16")
+    layer = tuple(to_dev(a) for a in layer_np)
+    Y = sf.spark_ffn_prefill(to_dev(Qb), layer, k, r).cpu().numpy()
+    q32 = torch.from_numpy(synth.bf16_bits_to_f32(Qb)).to(DEV)
+    Yd = sf.spark_ffn_decode(q32, [layer], k, r).cpu().numpy()
+    for t in range(16):
+        assert rel_err(Y[t], Yd[t]) <= 1e-4
