@@ -6,7 +6,7 @@ N(0, 1), RMS normalisation between layers; batch 1.  One step = one token
 through the whole stack (one spark_ffn_decode call with T = 1), inputs
 resident in HBM before the timed region.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
 
 value = tokens/s.  roofline: the decode kernel's algorithmic HBM bytes per
 launch (K1 slab of every layer + the selected K2 and V rows, from the actual
@@ -81,13 +81,91 @@ def cpu_baseline(layers_np, budget_s: float = 15.0):
             "sample": f"{n} tokens through the same 26-layer stack (fp64 C oracle, OpenMP), {dt:.1f} s"}
 
 
+def _time_ms(torch, fn, reps=20, warm=3):
+    """Median time of fn() in ms, HIP events on the current stream."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def extra_workloads(torch, sf, synth, dev, seed):
+    """The other workloads of the hot path, each timed on its own."""
+    res = {}
+    # standalone statistical top-k: 65536 rows x 9216, k 737, Gaussian rows
+    # x = mu + s * e with mu ~ U(-1,1), s ~ U(0.5,2) (generated on the GPU)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    rows, d, k = 65536, 9216, 737
+    x = torch.randn((rows, d), generator=g, device=dev)
+    x.mul_(torch.rand((rows, 1), generator=g, device=dev) * 1.5 + 0.5)
+    x.add_(torch.rand((rows, 1), generator=g, device=dev) * 2 - 1)
+    cap = 2 * k
+    vals = torch.empty((rows, cap), device=dev)
+    idx = torch.empty((rows, cap), dtype=torch.int32, device=dev)
+    counts = torch.empty(rows, dtype=torch.int32, device=dev)
+    theta = torch.empty(rows, device=dev)
+    L = sf.lib()
+    st = lambda: L.stat_topk(sf._p(x), rows, d, d, k, sf._p(vals), sf._p(idx), cap, sf._p(counts), sf._p(theta),
+                             sf._stream(dev))
+    ms = _time_ms(torch, st)
+    nsel = float(counts.double().sum().item())
+    moved = rows * d * 4 + nsel * 8 + rows * 8
+    res["stat_topk"] = {"workload": "65536 x 9216 fp32 rows, k 737", "ms": ms, "GB_s": moved / ms / 1e6,
+                        "frac_of_8TBs": moved / ms / 1e6 / HBM_PEAK_GBS, "mean_count": nsel / rows}
+    del x, vals, idx
+    torch.cuda.empty_cache()
+    # prefill: 4096 tokens through one 2304 x 9216 layer, bf16
+    T = 4096
+    lw = synth.ffn_layer(seed, 0, D_MODEL, D_FF, R, "bf16")
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    layer = tuple(bf(a) for a in lw)
+    Q = bf(synth.queries(seed, T, D_MODEL, "bf16"))
+    ms = _time_ms(torch, lambda: sf.spark_ffn_prefill(Q, layer, K, R), reps=10)
+    flops = 2.0 * T * R * D_FF
+    Qr = Q[:, :R].contiguous()
+    K1 = layer[0].t().contiguous()  # [r][d_ff]
+    ref_ms = _time_ms(torch, lambda: torch.mm(Qr, K1), reps=10)
+    del Qr, K1
+    res["prefill"] = {"workload": "4096 tokens, one 2304 x 9216 layer (r 1152, k 737), bf16", "ms": ms,
+                      "us_per_token": ms * 1e3 / T, "predictor_gflop": flops / 1e9,
+                      "hipblaslt_predictor_gemm_ms": ref_ms,
+                      "hipblaslt_predictor_tflops": flops / ref_ms / 1e9}
+    del Q, layer
+    torch.cuda.empty_cache()
+    # attention decode: 8 query heads / 4 KV heads, hd 256, r 128, k_attn 256
+    att = {}
+    for n in (4096, 32768):
+        qb, k1b, k2b, vb = synth.attn_inputs(seed, 8, 4, n, 256, 128)
+        args = [bf(a) for a in (qb, k1b, k2b, vb)]
+        out, cnt, _, _ = sf.spark_attn_decode(*args, 256)
+        ms = _time_ms(torch, lambda: sf.spark_attn_decode(*args, 256), reps=50)
+        c = cnt.double().sum().item()
+        moved = 4 * n * 128 * 2 + c * (128 + 256) * 2 + 8 * 256 * 2
+        att[str(n)] = {"us": ms * 1e3, "GB_s": moved / ms / 1e6, "mean_attended": c / 8,
+                       "algorithmic_bytes": moved}
+    res["attention_decode"] = att
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads (stat top-k, prefill, attention)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the decode path is a single-GPU kernel); got --gpus {args.gpus}",
@@ -101,6 +179,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        a = torch.ones(1 << 28, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4, "launches": 5}))
+        return
     t0 = time.perf_counter()
     layers_np = synth.ffn_stack(args.seed, LAYERS, D_MODEL, D_FF, R, "bf16", workers=16)
 
@@ -167,6 +253,10 @@ def main():
         "cpu_baseline": None,
         "kernel_failed": bool(failed),
     }
+    if not args.no_extra:
+        del layers, qs
+        torch.cuda.empty_cache()
+        out["extra"] = extra_workloads(torch, sf, synth, dev, args.seed)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layers_np)
     print(json.dumps(out), flush=True)
