@@ -36,7 +36,7 @@ constexpr int kDecMaxC = 21;   // K1 chunks (16 B) held per streamer thread (a 3
 constexpr int kStreamers = 256;
 constexpr int kWorkers = 256;
 constexpr int kRep = 8;        // replicas of every broadcast record (one per XCD)
-constexpr int kCand = 16;      // owned neurons whose K2 dot is formed before theta is known
+constexpr int kCand = 12;      // owned neurons whose K2 dot is formed before theta is known
 constexpr int kRecWords = 16;  // selected-list record: 2 mask words + 14 entries
 constexpr int kRecEntries = kRecWords - 2;
 constexpr int kOvfWords = kDecodeMaxNeuronsPerWG - kRecEntries;
@@ -244,14 +244,19 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
         reduce_tile(g, S, tile, lane, wv);
         bar();
       }
-      // stream the next slab while the rest of this layer runs
-      const int nl = (l + 1 < g.L) ? l + 1 : ((t + 1 < g.T) ? 0 : -1);
-      if (nl >= 0) load_tile(nl, 0);
       bar();  // A
       if (S.fail) return;
       bar();  // S
       bar();  // M
       if (S.fail) return;
+      // Stream the next slab while the rest of this layer runs.  Issued here,
+      // once the two latency-critical exchanges of the layer are over, the
+      // 21 MB burst overlaps the LDS-only list placement instead of queueing in
+      // front of the exchanges' small loads.
+      {
+        const int nl = (l + 1 < g.L) ? l + 1 : ((t + 1 < g.T) ? 0 : -1);
+        if (nl >= 0) load_tile(nl, 0);
+      }
       bar();  // O
       bar();  // L
       if (S.fail) return;
@@ -293,39 +298,41 @@ __device__ __forceinline__ float k2_dot(const char* row, const float* qr, int K2
   return wave_sum_dpp(s);
 }
 
-// K2^T q[r:] for up to three owned neurons at once (j0, j1, j2; -1 = none), by one
-// wave: every K2 load of the three rows is issued before any is used.
-template <typename W>
-__device__ __forceinline__ void k2_dot3(const char* k2base, size_t k2row, int j0, int j1, int j2, const float* qr,
-                                        int K2C, int lane, float* out) {
+// K2^T q[r:] for up to NJ owned neurons (js[u] < 0: none), by one wave.  Each
+// lane takes chunks lane + 64 k (k < KS) of each step of 64 KS chunks; every
+// K2 load of the step for the NJ rows is issued before any is used.
+template <typename W, int NJ, int KS>
+__device__ __forceinline__ void k2_dots(const char* k2base, size_t k2row, const int* js, const float* qr, int K2C,
+                                        int lane, float* out) {
   constexpr int CN = Chunk<W>::N;
-  float s[3] = {0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < K2C; c0 += 192) {
-    u32x4 raw[3][3];
+  float s[NJ];
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int ju = u == 0 ? j0 : (u == 1 ? (j1 >= 0 ? j1 : j0) : (j2 >= 0 ? j2 : j0));
-      const char* row = k2base + (size_t)ju * k2row;
+  for (int u = 0; u < NJ; ++u) s[u] = 0.f;
+  for (int c0 = 0; c0 < K2C; c0 += 64 * KS) {
+    u32x4 raw[NJ][KS];
 #pragma unroll
-      for (int k = 0; k < 3; ++k) raw[u][k] = load16(row + (size_t)min(c0 + lane + 64 * k, K2C - 1) * 16);
+    for (int u = 0; u < NJ; ++u) {
+      const char* row = k2base + (size_t)(js[u] >= 0 ? js[u] : js[0]) * k2row;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) raw[u][k] = load16(row + (size_t)min(c0 + lane + 64 * k, K2C - 1) * 16);
     }
 #pragma unroll
-    for (int u = 0; u < 3; ++u)
+    for (int k = 0; k < KS; ++k) {
+      const int cc = c0 + lane + 64 * k;
+      float qv[CN];
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int cc = c0 + lane + 64 * k;
+      for (int e = 0; e < CN; ++e) qv[e] = cc < K2C ? qr[cc * CN + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < NJ; ++u) {
         float wf[CN];
         Chunk<W>::widen(raw[u][k], wf);
-        const float* qq = qr + (cc < K2C ? cc : 0) * CN;
-        float a = 0.f;
 #pragma unroll
-        for (int e = 0; e < CN; ++e) a += wf[e] * qq[e];
-        s[u] += cc < K2C ? a : 0.f;
-        __builtin_amdgcn_sched_barrier(0);  // one chunk's q reads at a time
+        for (int e = 0; e < CN; ++e) s[u] += wf[e] * qv[e];
       }
+    }
   }
 #pragma unroll
-  for (int u = 0; u < 3; ++u) out[u] = wave_sum_dpp(s[u]);
+  for (int u = 0; u < NJ; ++u) out[u] = wave_sum_dpp(s[u]);
 }
 
 // ---------------------------------------------------------------- worker role
@@ -426,34 +433,32 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           raise_failure(p.hdr);
         }
       } else {
-        // ---------------- waves 1..3, meanwhile: K2 dots of the top candidates
+        // ---------------- waves 1..3, meanwhile: K2 dots of the top candidates.
+        // Rank of each owned score among the workgroup's (ties by index), by
+        // broadcasting every lane's score across the wave (no LDS traffic).
         int rank = 0;
         for (int i = 0; i < g.nown; ++i) {
-          const float hi = S.h[i];
+          const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hj), i));
           rank += (hi > hj || (hi == hj && i < lane)) ? 1 : 0;
         }
-        const uint64_t cmask = __builtin_amdgcn_ballot_w64(own && rank < kCand);
-        if (wv == 1 && lane == 0) S.candmask = cmask;
-        // this wave's candidates: every third one (positions wv-1, wv+2, ...);
-        // their K2 rows are loaded three at a time, all loads issued first
         const bool isc = own && rank < kCand;
+        const uint64_t cmask = __builtin_amdgcn_ballot_w64(isc);
+        if (wv == 1 && lane == 0) S.candmask = cmask;
         const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cmask, 0));
-        int jsel[6];
+        // this wave's candidates: positions wv-1, wv+2, wv+5, wv+8
+        int jsel[kCand / 3];
 #pragma unroll
-        for (int u = 0; u < 6; ++u) {
+        for (int u = 0; u < kCand / 3; ++u) {
           const uint64_t bb = __builtin_amdgcn_ballot_w64(isc && pos == (wv - 1) + 3 * u);
           jsel[u] = bb ? __builtin_ctzll(bb) : -1;
         }
+        if (jsel[0] >= 0) {
+          float d[kCand / 3];
+          k2_dots<W, kCand / 3, (sizeof(W) == 2 ? 1 : 2)>(k2base, k2row, jsel, S.q + g.r, g.K2C, lane, d);
+          if (lane == 0) {
 #pragma unroll
-        for (int b0 = 0; b0 < 6; b0 += 3) {
-          if (jsel[b0] >= 0) {
-            float d3[3];
-            k2_dot3<W>(k2base, k2row, jsel[b0], jsel[b0 + 1], jsel[b0 + 2], S.q + g.r, g.K2C, lane, d3);
-            if (lane == 0) {
-#pragma unroll
-              for (int u = 0; u < 3; ++u)
-                if (jsel[b0 + u] >= 0) S.g[jsel[b0 + u]] = d3[u];
-            }
+            for (int u = 0; u < kCand / 3; ++u)
+              if (jsel[u] >= 0) S.g[jsel[u]] = d[u];
           }
         }
       }
