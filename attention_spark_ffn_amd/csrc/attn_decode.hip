@@ -30,18 +30,6 @@ namespace spark {
 constexpr int kScoreTokens = 256;  // tokens per score workgroup (16 passes of 16)
 constexpr int kMaxGroup = 8;       // query heads per KV head handled in registers
 
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the row sum.
-__device__ __forceinline__ float row16_sum(float v) {
-#define SPARK_DPP_ROW(v, ctrl) \
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xf, 0xf, true))
-  SPARK_DPP_ROW(v, 0xb1);   // quad_perm [1,0,3,2]
-  SPARK_DPP_ROW(v, 0x4e);   // quad_perm [2,3,0,1]
-  SPARK_DPP_ROW(v, 0x124);  // row_ror:4
-  SPARK_DPP_ROW(v, 0x128);  // row_ror:8
-#undef SPARK_DPP_ROW
-  return v;
-}
-
 __global__ __launch_bounds__(256) void attn_scores(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k1,
                                                    int Hq, int Hkv, int n_ctx, int hd, int r,
                                                    float* __restrict__ scores) {

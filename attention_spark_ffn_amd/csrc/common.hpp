@@ -67,6 +67,49 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 }
 #undef SPARK_DPP_ADD
 
+// Sum over each row of 16 lanes (DPP within rows); every lane of a row gets
+// its row's total.
+__device__ __forceinline__ float row16_sum(float v) {
+#define SPARK_DPP_ROW(v, ctrl) \
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xf, 0xf, true))
+  SPARK_DPP_ROW(v, 0xb1);   // quad_perm [1,0,3,2]
+  SPARK_DPP_ROW(v, 0x4e);   // quad_perm [2,3,0,1]
+  SPARK_DPP_ROW(v, 0x124);  // row_ror:4
+  SPARK_DPP_ROW(v, 0x128);  // row_ror:8
+#undef SPARK_DPP_ROW
+  return v;
+}
+
+// Column sums of NV per-lane values (NV a power of two, at most 64) over the
+// 64 lanes of a wave, all columns at once: at each step a lane hands half of
+// the values it still holds to its partner (lane xor m) and adds the other
+// half to what it receives, so after log2(NV) steps every lane holds a
+// partial of one column, col; the remaining steps add over the lanes that
+// share a column.  Every lane returns the full sum of its column col.
+template <int NV>
+__device__ __forceinline__ float wave_colsum(float (&v)[NV], int lane, int& col) {
+  constexpr int S = NV >= 64 ? 6 : NV >= 32 ? 5 : NV >= 16 ? 4 : NV >= 8 ? 3 : NV >= 4 ? 2 : NV >= 2 ? 1 : 0;
+  static_assert((1 << S) == NV, "NV must be a power of two");
+  col = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int m = 32 >> s, h = NV >> (s + 1);
+    const uint32_t upm = (lane & m) ? 0xffffffffu : 0u;  // bit mask select: no selects of array slots
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const uint32_t a = __float_as_uint(v[i]), b = __float_as_uint(v[i + h]);
+      const float give = __uint_as_float((a & upm) | (b & ~upm));
+      const float keep = __uint_as_float((b & upm) | (a & ~upm));
+      v[i] = keep + __shfl_xor(give, m, kWave);
+    }
+    col += (lane & m) ? h : 0;
+  }
+  float t = v[0];
+#pragma unroll
+  for (int m = 32 >> S; m >= 1; m >>= 1) t += __shfl_xor(t, m, kWave);
+  return t;
+}
+
 // Butterfly reductions: every lane ends with the same value, bit for bit
 // (each step adds a and b in either order, and fp add is commutative).
 __device__ __forceinline__ float wave_sum(float v) {

@@ -39,6 +39,10 @@ constexpr int kRep = 8;        // replicas of every broadcast record (one per XC
 constexpr int kCand = 12;      // owned neurons whose K2 dot is formed before theta is known
 constexpr int kRecWords = 16;  // selected-list record: 2 mask words + 14 entries
 constexpr int kRecEntries = kRecWords - 2;
+constexpr int kRecRow = 256;   // records are word-major: word k of workgroup w at k * kRecRow + w
+constexpr int kSpecE = 6;      // entries polled together with the mask words
+constexpr int kK2Step = 9;     // K2 chunks per lane in flight in a candidate dot
+constexpr int kQPer = 9;       // q chunks a streamer keeps in registers (period of its q offsets)
 constexpr int kOvfWords = kDecodeMaxNeuronsPerWG - kRecEntries;
 constexpr int kListMax = kDecodeMaxNeuronsPerWG * 256;
 
@@ -62,7 +66,7 @@ struct DecodeParams {
   uint64_t* rec;    // kRep x rec_stride: selected-list record per workgroup
   uint64_t* ovf;    // G x kOvfWords: list entries past the record
   uint64_t* ycol;   // kRep x ycol_stride: owned columns of y
-  int stats_stride, rec_stride, ycol_stride, ycol_done;
+  int stats_stride, rec_stride, ycol_stride;
   uint32_t spin_limit;
 };
 
@@ -97,6 +101,15 @@ __device__ __forceinline__ bool gather_tagged(const uint64_t* const (&ptrs)[K], 
     if ((spin & 1023) == 1023 && get_word(hdr + 1) != 0) return false;
     __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// A uniform pointer the compiler must treat as produced anew where this is
+// called: per-thread addresses derived from it are then formed inside the
+// layer loop instead of being hoisted out of it and held in registers.
+template <typename T>
+__device__ __forceinline__ T* fresh(T* ptr) {
+  asm volatile("" : "+s"(ptr));
+  return ptr;
 }
 
 __device__ __forceinline__ void raise_failure(uint64_t* hdr) {
@@ -143,7 +156,7 @@ __device__ __forceinline__ int own_first(int g, int d_ff, int G) { return (int)(
 // Both roles execute exactly the same sequence of workgroup barriers:
 //   per token:  1 (input loaded) [+2 when the input needs normalising]
 //   per layer:  2 per K1 tile, then A, S, M, O, L, V, and either Y (last
-//               layer) or C, R1, R2; the failure flag is read after A, M, L and C.
+//               layer) or C, R; the failure flag is read after A, M, L and C.
 __device__ __forceinline__ void bar() { __syncthreads(); }
 
 
@@ -167,12 +180,13 @@ __device__ __forceinline__ void reduce_tile(const DecGeo& g, DecShared& S, int t
         v[u][k] = ok ? v[u][k] : 0.f;
       }
     }
+    float t[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = wv + 8 * u;
-      const float s = wave_sum_dpp(v[u][0] + v[u][1] + v[u][2]);
-      if (lane == 0 && j < g.nown) S.h[j] = s;
-    }
+    for (int u = 0; u < 8; ++u) t[u] = (v[u][0] + v[u][1]) + v[u][2];
+    int u;
+    const float s = wave_colsum<8>(t, lane, u);
+    const int j = wv + 8 * u;
+    if ((lane & 7) == 0 && j < g.nown) S.h[j] = s;
     return;
   }
   for (int j = tb / g.CK + wv; j <= (te - 1) / g.CK; j += 8) {
@@ -191,24 +205,31 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
   const int sid = threadIdx.x - kWorkers, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int TILE = kStreamers * kDecMaxC;
   u32x4 pre[kDecMaxC];
-  // q offset of each register chunk of tile 0 (fixed for the whole kernel)
-  int qoff[kDecMaxC];
+  // q offsets of the first kQPer register chunks of tile 0
+  int qoff[kQPer];
 #pragma unroll
-  for (int m = 0; m < kDecMaxC; ++m) {
+  for (int m = 0; m < kQPer; ++m) {
     const int c = sid + kStreamers * m;
     qoff[m] = c < g.TC ? (c % g.CK) * CN : 0;
   }
   // Branch-free: chunks past the slab end re-read its last chunk (in bounds) and
   // their products go to a dummy slot; with no branches the loads issue back to
   // back and the LDS reads of consecutive chunks overlap.
+  // The chunk offsets are formed anew at every call (from an opaque copy of
+  // the thread index) rather than held in registers for the whole kernel.
   auto load_tile = [&](int layer, int tile) {
     const char* slab = (const char*)tab_k1[layer] + (size_t)g.n0 * g.r * sizeof(W);
+    int s0 = tile * TILE + sid;
+    asm volatile("" : "+v"(s0));
 #pragma unroll
     for (int m = 0; m < kDecMaxC; ++m) {
-      const int c = min(tile * TILE + sid + kStreamers * m, g.TC - 1);
-      pre[m] = load16_stream(slab + (size_t)c * 16);
+      const int c = min(s0 + kStreamers * m, g.TC - 1);
+      pre[m] = load16_stream(slab + (uint32_t)c * 16u);
     }
   };
+  // chunk c of the slab multiplies q[(c % CK) * CN ...]; with c = sid + 256 m
+  // that offset has period kQPer in m when 256 kQPer is a multiple of CK
+  const bool qreg = g.ntile == 1 && (kStreamers * kQPer) % g.CK == 0;
   load_tile(0, 0);
   for (int t = 0; t < g.T; ++t) {
     bar();
@@ -218,13 +239,44 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
     }
     for (int l = 0; l < g.L; ++l) {
       const bool last = l == g.L - 1;
-      for (int tile = 0; tile < g.ntile; ++tile) {
+      if (qreg) {
+        // one tile, and the q offsets of a thread's chunks repeat every kQPer
+        // chunks: the kQPer distinct q chunks are read from LDS once
+        float qv[kQPer][CN];
+#pragma unroll
+        for (int i = 0; i < kQPer; ++i) {
+          const f32x4* qq = reinterpret_cast<const f32x4*>(S.q + qoff[i]);
+#pragma unroll
+          for (int e4 = 0; e4 < CN / 4; ++e4) {
+            const f32x4 x = qq[e4];
+            qv[i][4 * e4] = x.x;
+            qv[i][4 * e4 + 1] = x.y;
+            qv[i][4 * e4 + 2] = x.z;
+            qv[i][4 * e4 + 3] = x.w;
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < kDecMaxC; ++m) {
+          const int c = sid + kStreamers * m;
+          float wf[CN];
+          Chunk<W>::widen(pre[m], wf);
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < CN; ++e) acc += wf[e] * qv[m % kQPer][e];
+          S.u.part[c < g.TC ? c : TILE] = acc;
+          if (m % 3 == 2) __builtin_amdgcn_sched_barrier(0);  // keep few chunks' conversions live
+        }
+        bar();
+        reduce_tile(g, S, 0, lane, wv);
+        bar();
+      }
+      for (int tile = 0; !qreg && tile < g.ntile; ++tile) {
         if (tile > 0) load_tile(l, tile);
 #pragma unroll
         for (int m = 0; m < kDecMaxC; ++m) {
           const int c = tile * TILE + sid + kStreamers * m;
           const bool ok = c < g.TC;
-          const int qo = tile == 0 ? qoff[m] : (ok ? (c % g.CK) * CN : 0);
+          const int qo = ok ? (c % g.CK) * CN : 0;
           float wf[CN];
           Chunk<W>::widen(pre[m], wf);
           const f32x4* qq = reinterpret_cast<const f32x4*>(S.q + qo);  // 16-byte aligned
@@ -265,11 +317,9 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
         bar();  // Y
         continue;
       }
-      bar();  // C0
       bar();  // C
       if (S.fail) return;
-      bar();  // R1
-      bar();  // R2
+      bar();  // R
     }
   }
 }
@@ -298,41 +348,34 @@ __device__ __forceinline__ float k2_dot(const char* row, const float* qr, int K2
   return wave_sum_dpp(s);
 }
 
-// K2^T q[r:] for up to NJ owned neurons (js[u] < 0: none), by one wave.  Each
-// lane takes chunks lane + 64 k (k < KS) of each step of 64 KS chunks; every
-// K2 load of the step for the NJ rows is issued before any is used.
-template <typename W, int NJ, int KS>
-__device__ __forceinline__ void k2_dots(const char* k2base, size_t k2row, const int* js, const float* qr, int K2C,
-                                        int lane, float* out) {
+// K2^T q[r:] for one owned neuron by a row of 16 lanes (the four rows of a
+// wave take four neurons).  Lane s of the row takes chunks s, s + 16, ...;
+// all kK2Step loads of a step are issued before any is used, so a row of up
+// to 16 kK2Step chunks costs one memory round trip.
+template <typename W>
+__device__ __forceinline__ float k2_dot_row16(const char* row, const float* qr, int K2C, int s) {
   constexpr int CN = Chunk<W>::N;
-  float s[NJ];
+  float acc = 0.f;
+  for (int c0 = 0; c0 < K2C; c0 += 16 * kK2Step) {
+    u32x4 raw[kK2Step];
 #pragma unroll
-  for (int u = 0; u < NJ; ++u) s[u] = 0.f;
-  for (int c0 = 0; c0 < K2C; c0 += 64 * KS) {
-    u32x4 raw[NJ][KS];
+    for (int i = 0; i < kK2Step; ++i) raw[i] = load16(row + (size_t)min(c0 + s + 16 * i, K2C - 1) * 16);
 #pragma unroll
-    for (int u = 0; u < NJ; ++u) {
-      const char* row = k2base + (size_t)(js[u] >= 0 ? js[u] : js[0]) * k2row;
+    for (int i = 0; i < kK2Step; ++i) {
+      const int cc = c0 + s + 16 * i;
+      float wf[CN];
+      Chunk<W>::widen(raw[i], wf);
+      const f32x4* qq = reinterpret_cast<const f32x4*>(qr + (cc < K2C ? cc : 0) * CN);  // 16-byte aligned
+      float a = 0.f;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) raw[u][k] = load16(row + (size_t)min(c0 + lane + 64 * k, K2C - 1) * 16);
-    }
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const int cc = c0 + lane + 64 * k;
-      float qv[CN];
-#pragma unroll
-      for (int e = 0; e < CN; ++e) qv[e] = cc < K2C ? qr[cc * CN + e] : 0.f;
-#pragma unroll
-      for (int u = 0; u < NJ; ++u) {
-        float wf[CN];
-        Chunk<W>::widen(raw[u][k], wf);
-#pragma unroll
-        for (int e = 0; e < CN; ++e) s[u] += wf[e] * qv[e];
+      for (int e4 = 0; e4 < CN / 4; ++e4) {
+        const f32x4 qv = qq[e4];
+        a += wf[4 * e4] * qv.x + wf[4 * e4 + 1] * qv.y + wf[4 * e4 + 2] * qv.z + wf[4 * e4 + 3] * qv.w;
       }
+      acc += cc < K2C ? a : 0.f;
     }
   }
-#pragma unroll
-  for (int u = 0; u < NJ; ++u) out[u] = wave_sum_dpp(s[u]);
+  return row16_sum(acc);
 }
 
 // ---------------------------------------------------------------- worker role
@@ -390,7 +433,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         }
         // poll the 4 mean words of this lane's records first (few words per
         // polling round), then read the M2 words, which are then normally there
-        const uint64_t* src = p.stats + (size_t)g.rep * p.stats_stride;
+        const uint64_t* src = fresh(p.stats + (size_t)g.rep * p.stats_stride);
         constexpr int KA = 8;  // 4 records (G <= 256) x 2 words per lane
         const uint64_t* pm[KA / 2];
         const uint64_t* pq[KA / 2];
@@ -445,21 +488,21 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         const uint64_t cmask = __builtin_amdgcn_ballot_w64(isc);
         if (wv == 1 && lane == 0) S.candmask = cmask;
         const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cmask, 0));
-        // this wave's candidates: positions wv-1, wv+2, wv+5, wv+8
-        int jsel[kCand / 3];
+        // this wave's candidates: positions wv-1, wv+2, wv+5, wv+8, one per
+        // row of 16 lanes
+        static_assert(kCand == 12, "three waves of four 16-lane rows");
+        int jsel[4];
 #pragma unroll
-        for (int u = 0; u < kCand / 3; ++u) {
+        for (int u = 0; u < 4; ++u) {
           const uint64_t bb = __builtin_amdgcn_ballot_w64(isc && pos == (wv - 1) + 3 * u);
           jsel[u] = bb ? __builtin_ctzll(bb) : -1;
         }
         if (jsel[0] >= 0) {
-          float d[kCand / 3];
-          k2_dots<W, kCand / 3, (sizeof(W) == 2 ? 1 : 2)>(k2base, k2row, jsel, S.q + g.r, g.K2C, lane, d);
-          if (lane == 0) {
-#pragma unroll
-            for (int u = 0; u < kCand / 3; ++u)
-              if (jsel[u] >= 0) S.g[jsel[u]] = d[u];
-          }
+          const int grp = lane >> 4;
+          const int jm = grp == 0 ? jsel[0] : grp == 1 ? jsel[1] : grp == 2 ? jsel[2] : jsel[3];
+          const float d = k2_dot_row16<W>(k2base + (size_t)(jm >= 0 ? jm : jsel[0]) * k2row, S.q + g.r, g.K2C,
+                                          lane & 15);
+          if ((lane & 15) == 0 && jm >= 0) S.g[jm] = d;
         }
       }
       bar();  // A
@@ -483,47 +526,78 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           if (e < kRecEntries) {
 #pragma unroll
             for (int rp = 0; rp < kRep; ++rp)
-              put_tagged(p.rec + (size_t)rp * p.rec_stride + (size_t)w * kRecWords + 2 + e, cval, tagB);
+              put_tagged(p.rec + (size_t)rp * p.rec_stride + (size_t)(2 + e) * kRecRow + w, cval, tagB);
           } else {
             put_tagged(p.ovf + (size_t)w * kOvfWords + (e - kRecEntries), cval, tagB);
           }
         }
         if (lane < 2 * kRep) {
           const int rp = lane >> 1;
-          put_tagged_u32(p.rec + (size_t)rp * p.rec_stride + (size_t)w * kRecWords + (lane & 1),
+          put_tagged_u32(p.rec + (size_t)rp * p.rec_stride + (size_t)(lane & 1) * kRecRow + w,
                          (lane & 1) ? (uint32_t)(M >> 32) : (uint32_t)M, tagB);
         }
       }
       bar();  // S
 
-      // ---------------- exchange B: every workgroup's record (one thread each)
+      // ---------------- exchange B: every workgroup's record (one thread each).
+      // Records are word-major, so one load instruction of a wave reads the
+      // same word of 64 records from a few cache lines.  One polling loop
+      // takes the two mask words and the first kSpecE entries; entries past
+      // those (a record with more selected neurons) are read afterwards.
       bool okB = true;
       uint64_t Mg = 0;
       {
-        // one thread per record: poll its first mask word alone, then read the
-        // second mask word and the entries it announces (re-polling stragglers)
         const int gg = tid;
-        const uint64_t* rp = p.rec + (size_t)g.rep * p.rec_stride + (size_t)(gg < G ? gg : 0) * kRecWords;
-        float m0[1];
-        const uint64_t* p0[1] = {gg < G ? rp : nullptr};
-        okB = gather_tagged<1>(p0, tagB, m0, p.hdr, p.spin_limit);
-        float m1[1];
-        const uint64_t* p1[1] = {gg < G ? rp + 1 : nullptr};
-        okB = okB && gather_tagged<1>(p1, tagB, m1, p.hdr, p.spin_limit);
-        if (gg < G && okB) Mg = ((uint64_t)__float_as_uint(m1[0]) << 32) | __float_as_uint(m0[0]);
-        const int n = __builtin_popcountll(Mg);
-#pragma unroll 1
-        for (int h0 = 0; h0 < kRecEntries; h0 += kRecEntries / 2) {
-          const uint64_t* pe[kRecEntries / 2];
+        const bool has = gg < G;
+        const uint64_t* rp = fresh(p.rec + (size_t)g.rep * p.rec_stride) + (has ? gg : 0);
+        constexpr int NW = 2 + kSpecE;
+        float val[NW];
+        bool got[NW];
 #pragma unroll
-          for (int k = 0; k < kRecEntries / 2; ++k) pe[k] = (gg < G && h0 + k < n) ? rp + 2 + h0 + k : nullptr;
-          float ev[kRecEntries / 2];
-          okB = okB && gather_tagged<kRecEntries / 2>(pe, tagB, ev, p.hdr, p.spin_limit);
-#pragma unroll
-          for (int k = 0; k < kRecEntries / 2; ++k)
-            if (gg < G && h0 + k < n) S.t.stage[gg][h0 + k] = ev[k];
+        for (int k = 0; k < NW; ++k) {
+          got[k] = !has;
+          val[k] = 0.f;
         }
-        if (gg < G) S.cnt[gg] = okB ? __builtin_popcountll(Mg) : 0;
+        int n = has ? -1 : 0;  // entries announced by the masks (-1: not seen yet)
+        for (uint32_t spin = 0;; ++spin) {
+          uint64_t raw[NW];
+#pragma unroll
+          for (int k = 0; k < NW; ++k) raw[k] = get_word(rp + (size_t)k * kRecRow);
+#pragma unroll
+          for (int k = 0; k < NW; ++k) {
+            if (!got[k] && (uint32_t)(raw[k] >> 32) == tagB) {
+              val[k] = __uint_as_float((uint32_t)raw[k]);
+              got[k] = true;
+            }
+          }
+          if (n < 0 && got[0] && got[1])
+            n = __builtin_popcountll(((uint64_t)__float_as_uint(val[1]) << 32) | __float_as_uint(val[0]));
+          bool all = got[0] && got[1];
+#pragma unroll
+          for (int k = 2; k < NW; ++k) all = all && (got[k] || (n >= 0 && k - 2 >= n));
+          if (all) break;
+          if (spin > p.spin_limit || ((spin & 1023) == 1023 && get_word(p.hdr + 1) != 0)) {
+            okB = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (has && okB) Mg = ((uint64_t)__float_as_uint(val[1]) << 32) | __float_as_uint(val[0]);
+#pragma unroll
+        for (int k = 0; k < kSpecE; ++k)
+          if (has && k < n) S.t.stage[gg][k] = val[2 + k];
+        if (okB && n > kSpecE) {
+          constexpr int NR = kRecEntries - kSpecE;
+          const uint64_t* pe[NR];
+#pragma unroll
+          for (int k = 0; k < NR; ++k) pe[k] = kSpecE + k < n ? rp + (size_t)(2 + kSpecE + k) * kRecRow : nullptr;
+          float ev[NR];
+          okB = gather_tagged<NR>(pe, tagB, ev, p.hdr, p.spin_limit);
+#pragma unroll
+          for (int k = 0; k < NR; ++k)
+            if (kSpecE + k < n) S.t.stage[gg][kSpecE + k] = ev[k];
+        }
+        if (has) S.cnt[gg] = okB ? __builtin_popcountll(Mg) : 0;
       }
       if (!okB) S.fail = 1;
       bar();  // M
@@ -622,13 +696,9 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
             }
           }
         }
-#pragma unroll
-        for (int i = 0; i < 2 * CN; ++i) {
-          if (i < g.ncol) {
-            const float sum = wave_sum_dpp(acc[i]);
-            if (lane == 0) S.colpart[wv][i] = sum;
-          }
-        }
+        int col;
+        const float sum = wave_colsum<2 * CN>(acc, lane, col);
+        if ((lane & (64 / (2 * CN) - 1)) == 0 && col < g.ncol) S.colpart[wv][col] = sum;
       }
       bar();  // V
       const float ymine =
@@ -639,27 +709,18 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         continue;
       }
 
-      // ---------------- exchange C: owned columns of y -> every workgroup
+      // ---------------- exchange C: owned columns of y -> every workgroup, with
+      // the sum of squares of the RMS normalisation taken on the way.  Thread
+      // t gathers (and later scales) columns t, t + 256, ..., the same in
+      // every workgroup, so every workgroup forms the same scale bit for bit.
       {
         if (tid < g.ncol)
 #pragma unroll
           for (int rp = 0; rp < kRep; ++rp) put_tagged(p.ycol + (size_t)rp * p.ycol_stride + g.c0 + tid, ymine, tagC);
-        // then this owner's "done" word (one per replica)
-        if (tid < kRep) put_tagged_u32(p.ycol + (size_t)tid * p.ycol_stride + p.ycol_done + w, 1u, tagC);
         bool okC = true;
-        const uint64_t* src = p.ycol + (size_t)g.rep * p.ycol_stride;
-        {
-          float dn[1];
-          const uint64_t* pd[1] = {tid < G ? src + p.ycol_done + tid : nullptr};
-          okC = gather_tagged<1>(pd, tagC, dn, p.hdr, p.spin_limit);
-        }
-        if (!okC) S.fail = 1;
-      }
-      bar();  // C0
-      {
-        bool okC = S.fail == 0;
-        const uint64_t* src = p.ycol + (size_t)g.rep * p.ycol_stride;
-        constexpr int KC = 5;
+        float ss = 0.f;
+        const uint64_t* src = fresh(p.ycol + (size_t)g.rep * p.ycol_stride);
+        constexpr int KC = 9;
         for (int c00 = 0; okC && c00 < d_model; c00 += kWorkers * KC) {
           const uint64_t* ptrs[KC];
 #pragma unroll
@@ -668,13 +729,18 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
             ptrs[k] = c < d_model ? src + c : nullptr;
           }
           float vals[KC];
-          okC &= gather_tagged<KC>(ptrs, tagC, vals, p.hdr, p.spin_limit);
+          okC = gather_tagged<KC>(ptrs, tagC, vals, p.hdr, p.spin_limit);
 #pragma unroll
           for (int k = 0; k < KC; ++k) {
             const int c = c00 + tid + kWorkers * k;
-            if (c < d_model) S.q[c] = vals[k];
+            if (c < d_model) {
+              S.q[c] = vals[k];
+              ss += vals[k] * vals[k];
+            }
           }
         }
+        ss = wave_sum_dpp(ss);
+        if (lane == 0) S.wred[wv] = ss;
         if (!okC) S.fail = 1;
       }
       bar();  // C
@@ -682,21 +748,11 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         if (tid == 0) raise_failure(p.hdr);
         return;
       }
-      // RMS normalisation (identical order in every workgroup)
-      {
-        float ss = 0.f;
-#pragma unroll 4
-        for (int c = tid; c < d_model; c += kWorkers) ss += S.q[c] * S.q[c];
-        ss = wave_sum_dpp(ss);
-        if (lane == 0) S.wred[wv] = ss;
-      }
-      bar();  // R1
       {
         const float inv = 1.f / sqrtf((S.wred[0] + S.wred[1] + S.wred[2] + S.wred[3]) / (float)d_model + p.eps);
-#pragma unroll 4
-        for (int c = tid; c < d_model; c += kWorkers) S.q[c] *= inv;
+        for (int c = tid; c < d_model; c += kWorkers) S.q[c] *= inv;  // this thread's own columns
       }
-      bar();  // R2
+      bar();  // R
     }
   }
   if (w == 0 && tid == 0) __hip_atomic_store(p.hdr, (uint64_t)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -748,15 +804,14 @@ static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct DecodeLayout {
   size_t hdr, stats, rec, ovf, ycol, qbuf, total;
-  int stats_stride, rec_stride, ycol_stride, ycol_done;
+  int stats_stride, rec_stride, ycol_stride;
 };
 
 static DecodeLayout decode_layout(int64_t d_model, int64_t T, int grid, int n_layers) {
   DecodeLayout L;
   L.stats_stride = (int)round_up((size_t)2 * grid + 64, 512);  // words; replicas 4 KB+ apart
-  L.rec_stride = (int)round_up((size_t)kRecWords * grid + 64, 512);
-  L.ycol_done = (int)round_up((size_t)d_model, 64);  // words: owners' "done" flags follow the columns
-  L.ycol_stride = (int)round_up((size_t)L.ycol_done + grid + 64, 512);
+  L.rec_stride = (int)round_up((size_t)kRecWords * kRecRow + 64, 512);
+  L.ycol_stride = (int)round_up((size_t)d_model + 64, 512);
   size_t off = 0;
   L.hdr = off;
   off += 256;
@@ -831,7 +886,6 @@ static hipError_t launch_decode_t(const spark_ffn_shape& s, const spark_ffn_weig
     p.stats_stride = Lo.stats_stride;
     p.rec_stride = Lo.rec_stride;
     p.ycol_stride = Lo.ycol_stride;
-    p.ycol_done = Lo.ycol_done;
     p.spin_limit = 1u << 22;
     void* args[] = {&p};
     e = hipLaunchCooperativeKernel((const void*)decode_kernel<W>, dim3(grid), dim3(kDecodeThreads), args, 0, st);
