@@ -62,7 +62,7 @@ struct DecodeParams {
   float* tr_q;
   int64_t tr_cap;
   uint64_t* hdr;    // [0]: last tag used, [1]: failure flag
-  uint64_t* stats;  // kRep x stats_stride: (mean, M2) per workgroup
+  uint64_t* stats;  // kRep x stats_stride: means of all workgroups, then their M2 (kRecRow apart)
   uint64_t* rec;    // kRep x rec_stride: selected-list record per workgroup
   uint64_t* ovf;    // G x kOvfWords: list entries past the record
   uint64_t* ycol;   // kRep x ycol_stride: owned columns of y
@@ -151,7 +151,10 @@ struct DecGeo {
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
 
-__device__ __forceinline__ int own_first(int g, int d_ff, int G) { return (int)((int64_t)g * d_ff / G); }
+// First neuron of workgroup g (g * d_ff < 2^32 under the decode limits).
+__device__ __forceinline__ int own_first(int g, int d_ff, int G) {
+  return (int)((uint32_t)g * (uint32_t)d_ff / (uint32_t)G);
+}
 
 // Both roles execute exactly the same sequence of workgroup barriers:
 //   per token:  1 (input loaded) [+2 when the input needs normalising]
@@ -217,15 +220,27 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
   // back and the LDS reads of consecutive chunks overlap.
   // The chunk offsets are formed anew at every call (from an opaque copy of
   // the thread index) rather than held in registers for the whole kernel.
-  auto load_tile = [&](int layer, int tile) {
+  // Register chunks [m0, m1) of a tile.
+  auto load_part = [&](int layer, int tile, int m0, int m1) {
     const char* slab = (const char*)tab_k1[layer] + (size_t)g.n0 * g.r * sizeof(W);
     int s0 = tile * TILE + sid;
     asm volatile("" : "+v"(s0));
 #pragma unroll
     for (int m = 0; m < kDecMaxC; ++m) {
+      if (m < m0 || m >= m1) continue;
       const int c = min(s0 + kStreamers * m, g.TC - 1);
       pre[m] = load16_stream(slab + (uint32_t)c * 16u);
     }
+  };
+  auto load_tile = [&](int layer, int tile) { load_part(layer, tile, 0, kDecMaxC); };
+  // The next slab is streamed in three parts, issued after exchange B, after
+  // the list placement and after the V product: a part's loads are issued
+  // by the streamers before the next barrier, so one 21 MB burst would hold
+  // that barrier for its whole transfer, and its loads would queue in front
+  // of the next exchange's small loads.
+  auto prefetch_part = [&](int t, int l, int m0, int m1) {
+    const int nl = (l + 1 < g.L) ? l + 1 : ((t + 1 < g.T) ? 0 : -1);
+    if (nl >= 0) load_part(nl, 0, m0, m1);
   };
   // chunk c of the slab multiplies q[(c % CK) * CN ...]; with c = sid + 256 m
   // that offset has period kQPer in m when 256 kQPer is a multiple of CK
@@ -301,18 +316,13 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
       bar();  // S
       bar();  // M
       if (S.fail) return;
-      // Stream the next slab while the rest of this layer runs.  Issued here,
-      // once the two latency-critical exchanges of the layer are over, the
-      // 21 MB burst overlaps the LDS-only list placement instead of queueing in
-      // front of the exchanges' small loads.
-      {
-        const int nl = (l + 1 < g.L) ? l + 1 : ((t + 1 < g.T) ? 0 : -1);
-        if (nl >= 0) load_tile(nl, 0);
-      }
+      prefetch_part(t, l, 0, 7);
       bar();  // O
       bar();  // L
       if (S.fail) return;
+      prefetch_part(t, l, 7, 14);
       bar();  // V
+      prefetch_part(t, l, 14, kDecMaxC);
       if (last) {
         bar();  // Y
         continue;
@@ -389,6 +399,15 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
   const size_t k2row = (size_t)(d_model - g.r) * sizeof(W);
   const size_t vrow = (size_t)d_model * sizeof(W);
   uint32_t tag = S.tag0;
+  // neurons owned by the workgroups whose statistics this lane combines, and
+  // the first neuron of the workgroup whose record this thread places
+  float ngk[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int gg = lane + 64 * k;
+    ngk[k] = gg < G ? (float)(own_first(gg + 1, g.d_ff, G) - own_first(gg, g.d_ff, G)) : 0.f;
+  }
+  const int nb_rec = own_first(tid < G ? tid : 0, g.d_ff, G);
 
   for (int t = 0; t < g.T; ++t) {
     for (int c = tid; c < d_model; c += kWorkers) S.q[c] = p.q_in[(size_t)t * d_model + c];
@@ -427,47 +446,34 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         const float dv = own ? hj - mean_w : 0.f;
         const float m2_w = wave_sum_dpp(dv * dv);
         if (lane < kRep) {
-          uint64_t* dst = p.stats + (size_t)lane * p.stats_stride + 2 * w;
+          uint64_t* dst = p.stats + (size_t)lane * p.stats_stride + w;
           put_tagged(dst, mean_w, tagA);
-          put_tagged(dst + 1, m2_w, tagA);
+          put_tagged(dst + kRecRow, m2_w, tagA);
         }
-        // poll the 4 mean words of this lane's records first (few words per
-        // polling round), then read the M2 words, which are then normally there
+        // every record's two words in one polling loop: the means of all
+        // workgroups are contiguous, then their M2 values
         const uint64_t* src = fresh(p.stats + (size_t)g.rep * p.stats_stride);
         constexpr int KA = 8;  // 4 records (G <= 256) x 2 words per lane
-        const uint64_t* pm[KA / 2];
-        const uint64_t* pq[KA / 2];
+        const uint64_t* pa[KA];
 #pragma unroll
         for (int k = 0; k < KA / 2; ++k) {
           const int gg = lane + 64 * k;
-          pm[k] = gg < G ? src + 2 * gg : nullptr;
-          pq[k] = gg < G ? src + 2 * gg + 1 : nullptr;
+          pa[2 * k] = gg < G ? src + gg : nullptr;
+          pa[2 * k + 1] = gg < G ? src + kRecRow + gg : nullptr;
         }
-        float vm[KA / 2], vq[KA / 2], vals[KA];
-        bool ok = gather_tagged<KA / 2>(pm, tagA, vm, p.hdr, p.spin_limit);
-        ok = ok && gather_tagged<KA / 2>(pq, tagA, vq, p.hdr, p.spin_limit);
-#pragma unroll
-        for (int k = 0; k < KA / 2; ++k) {
-          vals[2 * k] = vm[k];
-          vals[2 * k + 1] = vq[k];
-        }
+        float vals[KA];
+        const bool ok = gather_tagged<KA>(pa, tagA, vals, p.hdr, p.spin_limit);
         // two passes over the records: the mean, then the squared deviations
         // about it (Chan et al.'s combination, written as two plain sums)
         float s1 = 0.f;
 #pragma unroll
-        for (int k = 0; k < KA / 2; ++k) {
-          const int gg = lane + 64 * k;
-          const float ng = (float)(own_first(gg + 1, g.d_ff, G) - own_first(gg, g.d_ff, G));
-          s1 += gg < G ? ng * vals[2 * k] : 0.f;
-        }
+        for (int k = 0; k < KA / 2; ++k) s1 += ngk[k] > 0.f ? ngk[k] * vals[2 * k] : 0.f;  // no record: no term
         const float mu = wave_sum_dpp(s1) / (float)g.d_ff;
         float s2 = 0.f;
 #pragma unroll
         for (int k = 0; k < KA / 2; ++k) {
-          const int gg = lane + 64 * k;
-          const float ng = (float)(own_first(gg + 1, g.d_ff, G) - own_first(gg, g.d_ff, G));
           const float d = vals[2 * k] - mu;
-          s2 += gg < G ? vals[2 * k + 1] + ng * d * d : 0.f;
+          s2 += ngk[k] > 0.f ? vals[2 * k + 1] + ngk[k] * d * d : 0.f;
         }
         const float m2 = wave_sum_dpp(s2);
         if (lane == 0) S.theta = mu + sqrtf(m2 / (float)g.d_ff) * p.z;
@@ -546,6 +552,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       // those (a record with more selected neurons) are read afterwards.
       bool okB = true;
       uint64_t Mg = 0;
+      float cspec[kSpecE];  // this thread's record: its first kSpecE gated values
       {
         const int gg = tid;
         const bool has = gg < G;
@@ -584,8 +591,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         }
         if (has && okB) Mg = ((uint64_t)__float_as_uint(val[1]) << 32) | __float_as_uint(val[0]);
 #pragma unroll
-        for (int k = 0; k < kSpecE; ++k)
-          if (has && k < n) S.t.stage[gg][k] = val[2 + k];
+        for (int k = 0; k < kSpecE; ++k) cspec[k] = val[2 + k];
         if (okB && n > kSpecE) {
           constexpr int NR = kRecEntries - kSpecE;
           const uint64_t* pe[NR];
@@ -627,9 +633,19 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       {
         const int gg = tid;
         if (gg < G) {
-          const int n = __builtin_popcountll(Mg), o = S.off[gg], nb = own_first(gg, g.d_ff, G);
+          const int n = __builtin_popcountll(Mg), o = S.off[gg], nb = nb_rec;
           uint64_t mm = Mg;
-          for (int e = 0; e < n; ++e) {
+          // the first kSpecE entries come from registers, without a loop
+#pragma unroll
+          for (int e = 0; e < kSpecE; ++e) {
+            const int j = mm ? __builtin_ctzll(mm) : 0;
+            mm &= mm - 1;
+            if (e < n && o + e < kListMax) {
+              S.u.list.c[o + e] = cspec[e];
+              S.u.list.idx[o + e] = (uint16_t)(nb + j);
+            }
+          }
+          for (int e = kSpecE; e < n; ++e) {
             const int j = __builtin_ctzll(mm);
             mm &= mm - 1;
             float cv;
@@ -697,8 +713,16 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           }
         }
         int col;
-        const float sum = wave_colsum<2 * CN>(acc, lane, col);
-        if ((lane & (64 / (2 * CN) - 1)) == 0 && col < g.ncol) S.colpart[wv][col] = sum;
+        if (g.nch > 1) {
+          const float sum = wave_colsum<2 * CN>(acc, lane, col);
+          if ((lane & (64 / (2 * CN) - 1)) == 0 && col < g.ncol) S.colpart[wv][col] = sum;
+        } else {  // one owned chunk: only the first CN sums are needed
+          float a1[CN];
+#pragma unroll
+          for (int i = 0; i < CN; ++i) a1[i] = acc[i];
+          const float sum = wave_colsum<CN>(a1, lane, col);
+          if ((lane & (64 / CN - 1)) == 0 && col < g.ncol) S.colpart[wv][col] = sum;
+        }
       }
       bar();  // V
       const float ymine =
@@ -809,7 +833,7 @@ struct DecodeLayout {
 
 static DecodeLayout decode_layout(int64_t d_model, int64_t T, int grid, int n_layers) {
   DecodeLayout L;
-  L.stats_stride = (int)round_up((size_t)2 * grid + 64, 512);  // words; replicas 4 KB+ apart
+  L.stats_stride = (int)round_up((size_t)2 * kRecRow + 64, 512);  // words; replicas 4 KB+ apart
   L.rec_stride = (int)round_up((size_t)kRecWords * kRecRow + 64, 512);
   L.ycol_stride = (int)round_up((size_t)d_model + 64, 512);
   size_t off = 0;
