@@ -103,6 +103,49 @@ __device__ __forceinline__ bool gather_tagged(const uint64_t* const (&ptrs)[K], 
   }
 }
 
+// As gather_tagged, with two polling rounds in flight: the loads of the next
+// round are issued before the words of the previous one are checked, so a
+// word that appears just after a round was issued is seen about half a round
+// trip later instead of a whole one.
+template <int K>
+__device__ __forceinline__ bool gather_tagged2(const uint64_t* const (&ptrs)[K], uint32_t tag, float (&out)[K],
+                                               const uint64_t* hdr, uint32_t spin_limit) {
+  bool got[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) got[k] = ptrs[k] == nullptr;
+  uint64_t a[K], b[K];
+  auto issue = [&](uint64_t (&r)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (!got[k]) r[k] = get_word(ptrs[k]);
+  };
+  auto check = [&](const uint64_t (&r)[K]) {
+    bool all = true;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (!got[k]) {
+        if ((uint32_t)(r[k] >> 32) == tag) {
+          out[k] = __uint_as_float((uint32_t)r[k]);
+          got[k] = true;
+        } else {
+          all = false;
+        }
+      }
+    }
+    return all;
+  };
+  issue(a);
+  for (uint32_t spin = 0;; spin += 2) {
+    issue(b);
+    if (check(a)) return true;
+    issue(a);
+    if (check(b)) return true;
+    if (spin > spin_limit) return false;
+    if ((spin & 1022) == 1022 && get_word(hdr + 1) != 0) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // A uniform pointer the compiler must treat as produced anew where this is
 // called: per-thread addresses derived from it are then formed inside the
 // layer loop instead of being hoisted out of it and held in registers.
@@ -462,7 +505,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           pa[2 * k + 1] = gg < G ? src + kRecRow + gg : nullptr;
         }
         float vals[KA];
-        const bool ok = gather_tagged<KA>(pa, tagA, vals, p.hdr, p.spin_limit);
+        const bool ok = gather_tagged2<KA>(pa, tagA, vals, p.hdr, p.spin_limit);
         // two passes over the records: the mean, then the squared deviations
         // about it (Chan et al.'s combination, written as two plain sums)
         float s1 = 0.f;
@@ -566,14 +609,17 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           val[k] = 0.f;
         }
         int n = has ? -1 : 0;  // entries announced by the masks (-1: not seen yet)
-        for (uint32_t spin = 0;; ++spin) {
-          uint64_t raw[NW];
+        // two polling rounds in flight (see gather_tagged2)
+        uint64_t ra[NW], rb[NW];
+        auto issue = [&](uint64_t (&r)[NW]) {
 #pragma unroll
-          for (int k = 0; k < NW; ++k) raw[k] = get_word(rp + (size_t)k * kRecRow);
+          for (int k = 0; k < NW; ++k) r[k] = get_word(rp + (size_t)k * kRecRow);
+        };
+        auto check = [&](const uint64_t (&r)[NW]) {
 #pragma unroll
           for (int k = 0; k < NW; ++k) {
-            if (!got[k] && (uint32_t)(raw[k] >> 32) == tagB) {
-              val[k] = __uint_as_float((uint32_t)raw[k]);
+            if (!got[k] && (uint32_t)(r[k] >> 32) == tagB) {
+              val[k] = __uint_as_float((uint32_t)r[k]);
               got[k] = true;
             }
           }
@@ -582,8 +628,15 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           bool all = got[0] && got[1];
 #pragma unroll
           for (int k = 2; k < NW; ++k) all = all && (got[k] || (n >= 0 && k - 2 >= n));
-          if (all) break;
-          if (spin > p.spin_limit || ((spin & 1023) == 1023 && get_word(p.hdr + 1) != 0)) {
+          return all;
+        };
+        issue(ra);
+        for (uint32_t spin = 0;; spin += 2) {
+          issue(rb);
+          if (check(ra)) break;
+          issue(ra);
+          if (check(rb)) break;
+          if (spin > p.spin_limit || ((spin & 1022) == 1022 && get_word(p.hdr + 1) != 0)) {
             okB = false;
             break;
           }
@@ -753,7 +806,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
             ptrs[k] = c < d_model ? src + c : nullptr;
           }
           float vals[KC];
-          okC = gather_tagged<KC>(ptrs, tagC, vals, p.hdr, p.spin_limit);
+          okC = gather_tagged2<KC>(ptrs, tagC, vals, p.hdr, p.spin_limit);
 #pragma unroll
           for (int k = 0; k < KC; ++k) {
             const int c = c00 + tid + kWorkers * k;
