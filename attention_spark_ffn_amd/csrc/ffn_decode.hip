@@ -40,7 +40,7 @@ constexpr int kCand = 12;      // owned neurons whose K2 dot is formed before th
 constexpr int kRecWords = 16;  // selected-list record: 2 mask words + 14 entries
 constexpr int kRecEntries = kRecWords - 2;
 constexpr int kRecRow = 256;   // records are word-major: word k of workgroup w at k * kRecRow + w
-constexpr int kSpecE = 6;      // entries polled together with the mask words
+constexpr int kSpecE = 10;     // entries polled together with the mask words
 constexpr int kK2Step = 9;     // K2 chunks per lane in flight in a candidate dot
 constexpr int kQPer = 9;       // q chunks a streamer keeps in registers (period of its q offsets)
 constexpr int kOvfWords = kDecodeMaxNeuronsPerWG - kRecEntries;
@@ -277,10 +277,10 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
   };
   auto load_tile = [&](int layer, int tile) { load_part(layer, tile, 0, kDecMaxC); };
   // The next slab is streamed in three parts, issued after exchange B, after
-  // the list placement and after the V product: a part's loads are issued
-  // by the streamers before the next barrier, so one 21 MB burst would hold
-  // that barrier for its whole transfer, and its loads would queue in front
-  // of the next exchange's small loads.
+  // the prefix of the counts and after the list placement: a part's loads are
+  // issued by the streamers before the next barrier, so one 21 MB burst would
+  // hold that barrier for its whole transfer, and its loads would queue in
+  // front of the next exchange's small loads.
   auto prefetch_part = [&](int t, int l, int m0, int m1) {
     const int nl = (l + 1 < g.L) ? l + 1 : ((t + 1 < g.T) ? 0 : -1);
     if (nl >= 0) load_part(nl, 0, m0, m1);
@@ -361,11 +361,11 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
       if (S.fail) return;
       prefetch_part(t, l, 0, 7);
       bar();  // O
+      prefetch_part(t, l, 7, 14);
       bar();  // L
       if (S.fail) return;
-      prefetch_part(t, l, 7, 14);
-      bar();  // V
       prefetch_part(t, l, 14, kDecMaxC);
+      bar();  // V
       if (last) {
         bar();  // Y
         continue;
