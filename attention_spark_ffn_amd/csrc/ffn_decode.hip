@@ -44,7 +44,6 @@ constexpr int kSpecE = 10;     // entries polled together with the mask words
 constexpr int kK2Step = 9;     // K2 chunks per lane in flight in a candidate dot
 constexpr int kQPer = 9;       // q chunks a streamer keeps in registers (period of its q offsets)
 constexpr int kOvfWords = kDecodeMaxNeuronsPerWG - kRecEntries;
-constexpr int kListMax = kDecodeMaxNeuronsPerWG * 256;
 
 struct DecodeParams {
   const void* k1t[kDecodeMaxLayersPerLaunch];
@@ -164,10 +163,6 @@ struct DecShared {
   alignas(16) float q[kDecodeMaxDModel];  // current layer input
   union {
     float part[kStreamers * kDecMaxC + 64];  // per-chunk partial dot products (+ a dummy slot)
-    struct {
-      float c[kListMax];          // gated values of every selected neuron, ascending neuron order
-      uint16_t idx[kListMax];     // their neuron indices
-    } list;
   } u;
   float h[kDecodeMaxNeuronsPerWG];   // predictor scores of the owned neurons
   float g[kDecodeMaxNeuronsPerWG];   // K2^T q[r:] of the owned neurons (candidates, then misses)
@@ -201,8 +196,9 @@ __device__ __forceinline__ int own_first(int g, int d_ff, int G) {
 
 // Both roles execute exactly the same sequence of workgroup barriers:
 //   per token:  1 (input loaded) [+2 when the input needs normalising]
-//   per layer:  2 per K1 tile, then A, S, M, O, L, V, and either Y (last
-//               layer) or C, R; the failure flag is read after A, M, L and C.
+//   per layer:  2 per K1 tile, then A, S, [T1, T2: workgroup 0, when a
+//               trace is asked for], V, and either Y (last layer) or C, R;
+//               the failure flag is read after A, V and C.
 __device__ __forceinline__ void bar() { __syncthreads(); }
 
 
@@ -276,11 +272,11 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
     }
   };
   auto load_tile = [&](int layer, int tile) { load_part(layer, tile, 0, kDecMaxC); };
-  // The next slab is streamed in three parts, issued after exchange B, after
-  // the prefix of the counts and after the list placement: a part's loads are
-  // issued by the streamers before the next barrier, so one 21 MB burst would
-  // hold that barrier for its whole transfer, and its loads would queue in
-  // front of the next exchange's small loads.
+  // The next slab is streamed from the moment theta is known: its loads then
+  // overlap the list exchange and the V product.  (Issued earlier they would
+  // queue in front of the statistics exchange and the candidate K2 loads;
+  // issued later, in front of the exchange of the layer output, or too late
+  // to land before the next predictor product.)
   auto prefetch_part = [&](int t, int l, int m0, int m1) {
     const int nl = (l + 1 < g.L) ? l + 1 : ((t + 1 < g.T) ? 0 : -1);
     if (nl >= 0) load_part(nl, 0, m0, m1);
@@ -288,6 +284,7 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
   // chunk c of the slab multiplies q[(c % CK) * CN ...]; with c = sid + 256 m
   // that offset has period kQPer in m when 256 kQPer is a multiple of CK
   const bool qreg = g.ntile == 1 && (kStreamers * kQPer) % g.CK == 0;
+  const bool trace_here = g.w == 0 && (p.tr_idx || p.tr_counts || p.tr_theta);
   load_tile(0, 0);
   for (int t = 0; t < g.T; ++t) {
     bar();
@@ -356,16 +353,14 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
       }
       bar();  // A
       if (S.fail) return;
+      prefetch_part(t, l, 0, kDecMaxC);
       bar();  // S
-      bar();  // M
-      if (S.fail) return;
-      prefetch_part(t, l, 0, 7);
-      bar();  // O
-      prefetch_part(t, l, 7, 14);
-      bar();  // L
-      if (S.fail) return;
-      prefetch_part(t, l, 14, kDecMaxC);
+      if (trace_here) {
+        bar();  // T1
+        bar();  // T2
+      }
       bar();  // V
+      if (S.fail) return;
       if (last) {
         bar();  // Y
         continue;
@@ -431,6 +426,65 @@ __device__ __forceinline__ float k2_dot_row16(const char* row, const float* qr, 
   return row16_sum(acc);
 }
 
+// This thread's share of the V product: the selected neurons of one record
+// (workgroup gg's), NCH owned 16-byte chunks of each V row.  The first kSpecE
+// entries take their gated values from registers and all their loads are
+// issued before any is used; later entries (a record with more selected
+// neurons) are read one at a time.  Returns false if an overflow entry never
+// appeared.
+template <typename W, int NCH>
+__device__ __forceinline__ bool v_record(const DecodeParams& p, const DecShared& S, const char* vbase, size_t vrow,
+                                         uint64_t Mg, int nb, const float (&cspec)[kSpecE], int gg, uint32_t tagB,
+                                         float (&acc)[2 * Chunk<W>::N]) {
+  constexpr int CN = Chunk<W>::N;
+  const int n = __builtin_popcountll(Mg);
+  uint64_t mm = Mg;
+  int jv[kSpecE];
+#pragma unroll
+  for (int e = 0; e < kSpecE; ++e) {
+    jv[e] = mm ? __builtin_ctzll(mm) : 0;
+    mm &= mm - 1;
+  }
+  u32x4 raw[kSpecE][NCH];
+#pragma unroll
+  for (int e = 0; e < kSpecE; ++e)
+    if (e < n)
+#pragma unroll
+      for (int hh = 0; hh < NCH; ++hh) raw[e][hh] = load16(vbase + (size_t)(nb + jv[e]) * vrow + hh * 16);
+#pragma unroll
+  for (int e = 0; e < kSpecE; ++e)
+    if (e < n)
+#pragma unroll
+      for (int hh = 0; hh < NCH; ++hh) {
+        float wf[CN];
+        Chunk<W>::widen(raw[e][hh], wf);
+#pragma unroll
+        for (int i = 0; i < CN; ++i) acc[hh * CN + i] += cspec[e] * wf[i];
+      }
+  bool ok = true;
+  for (int e = kSpecE; e < n; ++e) {
+    const int j = __builtin_ctzll(mm);
+    mm &= mm - 1;
+    float cv;
+    if (e < kRecEntries) {
+      cv = S.t.stage[gg][e];
+    } else {
+      const uint64_t* op[1] = {p.ovf + (size_t)gg * kOvfWords + (e - kRecEntries)};
+      float ov[1];
+      ok = ok && gather_tagged<1>(op, tagB, ov, p.hdr, p.spin_limit);
+      cv = ok ? ov[0] : 0.f;
+    }
+#pragma unroll
+    for (int hh = 0; hh < NCH; ++hh) {
+      float wf[CN];
+      Chunk<W>::widen(load16(vbase + (size_t)(nb + j) * vrow + hh * 16), wf);
+#pragma unroll
+      for (int i = 0; i < CN; ++i) acc[hh * CN + i] += cv * wf[i];
+    }
+  }
+  return ok;
+}
+
 // ---------------------------------------------------------------- worker role
 template <typename W>
 __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, const void* const* tab_v,
@@ -451,6 +505,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
     ngk[k] = gg < G ? (float)(own_first(gg + 1, g.d_ff, G) - own_first(gg, g.d_ff, G)) : 0.f;
   }
   const int nb_rec = own_first(tid < G ? tid : 0, g.d_ff, G);
+  const bool trace_here = w == 0 && (p.tr_idx || p.tr_counts || p.tr_theta);
 
   for (int t = 0; t < g.T; ++t) {
     for (int c = tid; c < d_model; c += kWorkers) S.q[c] = p.q_in[(size_t)t * d_model + c];
@@ -659,112 +714,23 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         if (has) S.cnt[gg] = okB ? __builtin_popcountll(Mg) : 0;
       }
       if (!okB) S.fail = 1;
-      bar();  // M
-      if (S.fail) {
-        if (tid == 0) raise_failure(p.hdr);
-        return;
-      }
-      if (wv == 0) {  // exclusive prefix of the counts, workgroup order
-        int c4[4], s4 = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int gg = 4 * lane + k;
-          c4[k] = gg < G ? S.cnt[gg] : 0;
-          s4 += c4[k];
-        }
-        int run = wave_excl_scan(s4, lane);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int gg = 4 * lane + k;
-          if (gg < G) S.off[gg] = run;
-          run += c4[k];
-        }
-        if (lane == 63) S.ntot = run;
-      }
-      bar();  // O
-      // place this record's entries into the list (ascending neuron order)
-      {
-        const int gg = tid;
-        if (gg < G) {
-          const int n = __builtin_popcountll(Mg), o = S.off[gg], nb = nb_rec;
-          uint64_t mm = Mg;
-          // the first kSpecE entries come from registers, without a loop
-#pragma unroll
-          for (int e = 0; e < kSpecE; ++e) {
-            const int j = mm ? __builtin_ctzll(mm) : 0;
-            mm &= mm - 1;
-            if (e < n && o + e < kListMax) {
-              S.u.list.c[o + e] = cspec[e];
-              S.u.list.idx[o + e] = (uint16_t)(nb + j);
-            }
-          }
-          for (int e = kSpecE; e < n; ++e) {
-            const int j = __builtin_ctzll(mm);
-            mm &= mm - 1;
-            float cv;
-            if (e < kRecEntries) {
-              cv = S.t.stage[gg][e];
-            } else {
-              const uint64_t* op[1] = {p.ovf + (size_t)gg * kOvfWords + (e - kRecEntries)};
-              float ov[1];
-              okB &= gather_tagged<1>(op, tagB, ov, p.hdr, p.spin_limit);
-              cv = ov[0];
-            }
-            if (o + e < kListMax) {
-              S.u.list.c[o + e] = cv;
-              S.u.list.idx[o + e] = (uint16_t)(nb + j);
-            }
-          }
-        }
-        if (!okB) S.fail = 1;
-      }
-      bar();  // L
-      if (S.fail) {
-        if (tid == 0) raise_failure(p.hdr);
-        return;
-      }
-      const int ntot = S.ntot;
-      if (w == 0 && tid == 0) {
-        if (p.tr_counts) p.tr_counts[trow] = ntot;
-        if (p.tr_theta) p.tr_theta[trow] = theta;
-      }
-      if (w == 0 && p.tr_idx)
-        for (int e = tid; e < ntot && e < p.tr_cap; e += kWorkers) p.tr_idx[trow * p.tr_cap + e] = S.u.list.idx[e];
 
-      // ---------------- V: the owned columns of y over every selected neuron.
-      // Ownership is by 16-byte chunks of a V row (at most 2 per workgroup per
-      // pass); thread t takes entries t, t + 256, ... and loads each entry's
-      // owned chunks with 16-byte loads, three entries at a time.  Column sums
-      // then run over lanes (DPP) and waves in a fixed order.
+      // ---------------- V: the owned columns of y.  Thread gg takes the
+      // selected neurons of record gg; column sums then run over lanes and
+      // waves in a fixed order.
       {
-        const int n = min(ntot, kListMax);
         const char* vbase = (const char*)tab_v[l] + (size_t)g.ch0 * 16;
         float acc[2 * CN];
 #pragma unroll
         for (int i = 0; i < 2 * CN; ++i) acc[i] = 0.f;
-        for (int e0 = tid; e0 < n; e0 += 3 * kWorkers) {
-          u32x4 raw[3][2];
-          float cv[3];
-#pragma unroll
-          for (int u = 0; u < 3; ++u) {
-            const int e = e0 + u * kWorkers;
-            const bool ok = e < n;
-            const char* row = vbase + (size_t)(ok ? S.u.list.idx[e] : 0) * vrow;
-            cv[u] = ok ? S.u.list.c[e] : 0.f;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) raw[u][hh] = load16(row + (size_t)(hh < g.nch ? hh : 0) * 16);
-          }
-#pragma unroll
-          for (int u = 0; u < 3; ++u) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              float wf[CN];
-              Chunk<W>::widen(raw[u][hh], wf);
-#pragma unroll
-              for (int i = 0; i < CN; ++i) acc[hh * CN + i] += cv[u] * wf[i];
-            }
-          }
+        bool okV = true;
+        if (tid < G && okB) {
+          if (g.nch > 1)
+            okV = v_record<W, 2>(p, S, vbase, vrow, Mg, nb_rec, cspec, tid, tagB, acc);
+          else
+            okV = v_record<W, 1>(p, S, vbase, vrow, Mg, nb_rec, cspec, tid, tagB, acc);
         }
+        if (!okV) S.fail = 1;
         int col;
         if (g.nch > 1) {
           const float sum = wave_colsum<2 * CN>(acc, lane, col);
@@ -777,7 +743,48 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           if ((lane & (64 / CN - 1)) == 0 && col < g.ncol) S.colpart[wv][col] = sum;
         }
       }
+
+      // ---------------- trace (workgroup 0 only): the selected list in
+      // ascending neuron order, its length and theta
+      if (trace_here) {
+        bar();  // T1
+        if (wv == 0) {  // exclusive prefix of the counts, workgroup order
+          int c4[4], s4 = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int gg = 4 * lane + k;
+            c4[k] = gg < G ? S.cnt[gg] : 0;
+            s4 += c4[k];
+          }
+          int run = wave_excl_scan(s4, lane);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int gg = 4 * lane + k;
+            if (gg < G) S.off[gg] = run;
+            run += c4[k];
+          }
+          if (lane == 63) S.ntot = run;
+        }
+        bar();  // T2
+        if (tid < G && p.tr_idx) {
+          const int n = __builtin_popcountll(Mg), o = S.off[tid];
+          uint64_t mm = Mg;
+          for (int e = 0; e < n; ++e) {
+            const int j = __builtin_ctzll(mm);
+            mm &= mm - 1;
+            if (o + e < p.tr_cap) p.tr_idx[trow * p.tr_cap + o + e] = nb_rec + j;
+          }
+        }
+        if (tid == 0) {
+          if (p.tr_counts) p.tr_counts[trow] = S.ntot;
+          if (p.tr_theta) p.tr_theta[trow] = theta;
+        }
+      }
       bar();  // V
+      if (S.fail) {
+        if (tid == 0) raise_failure(p.hdr);
+        return;
+      }
       const float ymine =
           tid < g.ncol ? ((S.colpart[0][tid] + S.colpart[1][tid]) + S.colpart[2][tid]) + S.colpart[3][tid] : 0.f;
       if (last) {
