@@ -834,7 +834,20 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       }
       {
         const float inv = 1.f / sqrtf((S.wred[0] + S.wred[1] + S.wred[2] + S.wred[3]) / (float)d_model + p.eps);
-        for (int c = tid; c < d_model; c += kWorkers) S.q[c] *= inv;  // this thread's own columns
+        // this thread's own columns: all reads issued before any write
+        for (int c0 = tid; c0 < d_model; c0 += kWorkers * 9) {
+          float v[9];
+#pragma unroll
+          for (int k = 0; k < 9; ++k) {
+            const int c = c0 + kWorkers * k;
+            v[k] = c < d_model ? S.q[c] : 0.f;
+          }
+#pragma unroll
+          for (int k = 0; k < 9; ++k) {
+            const int c = c0 + kWorkers * k;
+            if (c < d_model) S.q[c] = v[k] * inv;
+          }
+        }
       }
       bar();  // R
     }
