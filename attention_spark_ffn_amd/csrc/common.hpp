@@ -67,6 +67,20 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 }
 #undef SPARK_DPP_ADD
 
+// Inclusive prefix sum over the 64 lanes with DPP row shifts and row
+// broadcasts (VALU only).
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+#define SPARK_DPP_SCAN(v, ctrl, rmask) v += __builtin_amdgcn_update_dpp(0, v, ctrl, rmask, 0xf, true)
+  SPARK_DPP_SCAN(v, 0x111, 0xf);  // row_shr:1
+  SPARK_DPP_SCAN(v, 0x112, 0xf);  // row_shr:2
+  SPARK_DPP_SCAN(v, 0x114, 0xf);  // row_shr:4
+  SPARK_DPP_SCAN(v, 0x118, 0xf);  // row_shr:8  -> prefix within each row of 16
+  SPARK_DPP_SCAN(v, 0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+  SPARK_DPP_SCAN(v, 0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+#undef SPARK_DPP_SCAN
+  return v;
+}
+
 // Sum over each row of 16 lanes (DPP within rows); every lane of a row gets
 // its row's total.
 __device__ __forceinline__ float row16_sum(float v) {

@@ -7,129 +7,174 @@
 //
 // gfx950 mapping: the row is held in registers (lane t owns the 4 consecutive
 // elements 4t + 4*NT*e, e < E, read with 16-byte loads, so each load
-// instruction of the workgroup covers 4*NT contiguous floats).  Mean and
-// sum of squared deviations are two exact passes over the registers, reduced
-// with wave butterflies and a fixed-order sum across waves.  Compaction: per
-// chunk e each lane counts its survivors (0..4), a wave prefix scan plus the
-// per-wave totals in LDS give every survivor its ascending output slot.
-// One HBM read of the row, writes only the survivors.
+// instruction of the workgroup covers 4*NT contiguous floats).  Mean and sum
+// of squared deviations are two exact passes over the registers, reduced with
+// DPP wave sums and a fixed-order sum across waves.  Compaction: each lane
+// keeps a 4-bit survivor mask per chunk; a DPP prefix scan of the mask counts
+// plus the per-wave totals give every survivor its ascending slot without a
+// serial walk; the list is staged in LDS and written out with contiguous
+// stores.  One HBM read of the row, writes only the survivors.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace spark {
 
-template <int NT, int E, bool VEC>
-__global__ __launch_bounds__(NT) void stat_topk_kernel(const float* __restrict__ x, int64_t rows, int d, int64_t ldx,
-                                                       float z, float* __restrict__ vals, int32_t* __restrict__ idx,
-                                                       int64_t cap, int32_t* __restrict__ counts,
-                                                       float* __restrict__ theta_out) {
+constexpr int kStage = 2048;  // list entries of a row staged in LDS before the contiguous write-out
+
+// Shared memory of one workgroup: per-wave partial sums (mean, then M2),
+// per-(wave, chunk) survivor counts, and the staged list.  Each array is
+// written once per row between two barriers, so a row needs no trailing
+// barrier before the next one starts.
+template <int NW, int E>
+struct StatShared {
+  float red[2][NW];
+  int wtot[NW][E];
+  int s_idx[kStage];
+  float s_val[kStage];
+};
+
+// Lane t's elements 4t + 4*NT*e + j (e < E, j < 4) of one row.  Entries past
+// the row end are 0.  EXACT: d == 4*NT*E, no bounds tests.
+template <int NT, int E, bool VEC, bool EXACT>
+__device__ __forceinline__ void load_row(const float* xr, int d, int tid, float (&v)[E][4]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i0 = 4 * tid + 4 * NT * e;
+    if (EXACT || (VEC && i0 + 3 < d)) {
+      const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xr + i0));
+      v[e][0] = t.x;
+      v[e][1] = t.y;
+      v[e][2] = t.z;
+      v[e][3] = t.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[e][j] = i0 + j < d ? xr[i0 + j] : 0.f;
+    }
+  }
+}
+
+// Statistics, threshold and list of one row held in registers.
+template <int NT, int E, bool EXACT>
+__device__ __forceinline__ void process_row(const float (&v)[E][4], int64_t row, int d, int tid, float z,
+                                            float* __restrict__ vals, int32_t* __restrict__ idx, int64_t cap,
+                                            int32_t* __restrict__ counts, float* __restrict__ theta_out,
+                                            StatShared<NT / kWave, E>& S) {
   constexpr int NW = NT / kWave;
-  __shared__ float red[NW];
-  __shared__ int wtot[NW][E];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int lane = tid & (kWave - 1), wv = tid / kWave;
+  // pass 1: mean (entries past the row end are 0)
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) s += (v[e][0] + v[e][1]) + (v[e][2] + v[e][3]);
+  s = wave_sum_dpp(s);
+  if (lane == 0) S.red[0][wv] = s;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot += S.red[0][w];
+  const float mean = tot / (float)d;
+  // pass 2: sum of squared deviations about the mean
+  float q = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float dv = v[e][j] - mean;
+      q += (EXACT || 4 * tid + 4 * NT * e + j < d) ? dv * dv : 0.f;
+    }
+  q = wave_sum_dpp(q);
+  if (lane == 0) S.red[1][wv] = q;
+  __syncthreads();
+  float m2 = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) m2 += S.red[1][w];
+  const float theta = mean + sqrtf(m2 / (float)d) * z;
 
-  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-    const float* xr = x + row * ldx;
-    float v[E][4];
-    bool ok[E][4];
+  // survivors of chunk e as a 4-bit mask per lane, their prefix within the
+  // wave, and the per-wave totals
+  int pre[E], msk[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    int m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m |= ((EXACT || 4 * tid + 4 * NT * e + j < d) && v[e][j] > theta) ? (1 << j) : 0;
+    // opaque: later tests read the bits rather than keeping the compares
+    asm volatile("" : "+v"(m));
+    const int c = __builtin_popcount(m);
+    const int incl = wave_incl_scan_dpp(c);
+    msk[e] = m;
+    pre[e] = incl - c;
+    if (lane == kWave - 1) S.wtot[wv][e] = incl;
+  }
+  __syncthreads();
+  // totals of every chunk and of the waves before this one, one wave of the
+  // table at a time (a fully unrolled walk would hold NW x E values)
+  int before[E], all[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) before[e] = all[e] = 0;
+#pragma unroll(NW <= 4 ? NW : 1)
+  for (int w = 0; w < NW; ++w) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int i0 = 4 * tid + 4 * NT * e;
-      if (VEC && i0 + 3 < d) {
-        const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xr + i0));
-        v[e][0] = t.x; v[e][1] = t.y; v[e][2] = t.z; v[e][3] = t.w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ok[e][j] = true;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          ok[e][j] = i0 + j < d;
-          v[e][j] = ok[e][j] ? xr[i0 + j] : 0.f;
-        }
-      }
+      const int t = S.wtot[w][e];
+      before[e] += (w < wv) ? t : 0;
+      all[e] += t;
     }
-    // pass 1: mean
-    float s = 0.f;
+  }
+  int base = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    pre[e] += base + before[e];
+    base += all[e];
+  }
+  if (idx != nullptr || vals != nullptr) {
+    // slot of survivor (e, j) of this lane: the chunk's prefix plus this
+    // lane's survivors before it in the chunk (no serial dependence)
 #pragma unroll
     for (int e = 0; e < E; ++e)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s += v[e][j];  // masked entries are 0
-    s = wave_sum(s);
-    __syncthreads();
-    if (lane == 0) red[wv] = s;
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) tot += red[w];
-    const float mean = tot / (float)d;
-    // pass 2: sum of squared deviations
-    float q = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float dv = v[e][j] - mean;
-        q += ok[e][j] ? dv * dv : 0.f;
-      }
-    q = wave_sum(q);
-    __syncthreads();
-    if (lane == 0) red[wv] = q;
-    __syncthreads();
-    float m2 = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) m2 += red[w];
-    const float theta = mean + sqrtf(m2 / (float)d) * z;
-
-    // survivors per (lane, chunk) and per-wave prefix
-    int cnt[E], pre[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      int c = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) c += (ok[e][j] && v[e][j] > theta) ? 1 : 0;
-      cnt[e] = c;
-      pre[e] = wave_excl_scan(c, lane);
-      const int wt = __shfl(pre[e] + c, kWave - 1, kWave);
-      if (lane == 0) wtot[wv][e] = wt;
-    }
-    __syncthreads();
-    int base = 0, total = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      int before = 0, all = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const int t = wtot[w][e];
-        before += (w < wv) ? t : 0;
-        all += t;
-      }
-      pre[e] += base + before;
-      base += all;
-    }
-    total = base;
-    if (idx != nullptr || vals != nullptr) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (cnt[e] == 0) continue;
-        int pos = pre[e];
-        const int i0 = 4 * tid + 4 * NT * e;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (ok[e][j] && v[e][j] > theta) {
-            if (pos < cap) {
-              if (idx) idx[row * cap + pos] = i0 + j;
-              if (vals) vals[row * cap + pos] = v[e][j] - theta;
-            }
-            ++pos;
+      for (int j = 0; j < 4; ++j)
+        if (msk[e] & (1 << j)) {
+          const int pos = pre[e] + __builtin_popcount(msk[e] & ((1 << j) - 1));
+          const int i = 4 * tid + 4 * NT * e + j;
+          if (pos < kStage) {
+            S.s_idx[pos] = i;
+            S.s_val[pos] = v[e][j] - theta;
+          } else if (pos < cap) {
+            if (idx) idx[row * cap + pos] = i;
+            if (vals) vals[row * cap + pos] = v[e][j] - theta;
           }
         }
-      }
-    }
-    if (tid == 0) {
-      counts[row] = total;
-      if (theta_out) theta_out[row] = theta;
-    }
+  }
+  if (tid == 0) {
+    counts[row] = base;
+    if (theta_out) theta_out[row] = theta;
+  }
+  if (idx != nullptr || vals != nullptr) {
     __syncthreads();
+    const int nst = (int)min((int64_t)min(base, kStage), cap);
+    for (int i = tid; i < nst; i += NT) {
+      if (idx) idx[row * cap + i] = S.s_idx[i];
+      if (vals) vals[row * cap + i] = S.s_val[i];
+    }
+  }
+}
+
+// One workgroup per row (rows strided by the grid).
+template <int NT, int E, bool VEC, bool EXACT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 && E <= 9 ? 4 : 1)))
+void stat_topk_kernel(const float* __restrict__ x, int64_t rows, int d_arg, int64_t ldx, float z,
+                      float* __restrict__ vals, int32_t* __restrict__ idx, int64_t cap, int32_t* __restrict__ counts,
+                      float* __restrict__ theta_out) {
+  __shared__ StatShared<NT / kWave, E> S;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    // Opaque copies of the thread index and the row length: the element
+    // indices and bounds tests derived from them are formed anew for every
+    // row instead of being hoisted out of the loop and held in registers.
+    int tid = threadIdx.x, d = d_arg;
+    asm volatile("" : "+v"(tid), "+s"(d));
+    float v[E][4];
+    load_row<NT, E, VEC, EXACT>(x + row * ldx, d, tid, v);
+    process_row<NT, E, EXACT>(v, row, d, tid, z, vals, idx, cap, counts, theta_out, S);
   }
 }
 
@@ -137,12 +182,16 @@ template <int NT, int E>
 static hipError_t launch_e(bool vec, const float* x, int64_t rows, int d, int64_t ldx, float z, float* vals,
                            int32_t* idx, int64_t cap, int32_t* counts, float* theta, hipStream_t st) {
   const int64_t grid = rows < (1 << 30) ? rows : (1 << 30);
-  if (vec)
-    hipLaunchKernelGGL((stat_topk_kernel<NT, E, true>), dim3((unsigned)grid), dim3(NT), 0, st, x, rows, d, ldx, z,
-                       vals, idx, cap, counts, theta);
+  const dim3 g((unsigned)grid), b(NT);
+  if (vec && d == 4 * NT * E)
+    hipLaunchKernelGGL((stat_topk_kernel<NT, E, true, true>), g, b, 0, st, x, rows, d, ldx, z, vals, idx, cap, counts,
+                       theta);
+  else if (vec)
+    hipLaunchKernelGGL((stat_topk_kernel<NT, E, true, false>), g, b, 0, st, x, rows, d, ldx, z, vals, idx, cap,
+                       counts, theta);
   else
-    hipLaunchKernelGGL((stat_topk_kernel<NT, E, false>), dim3((unsigned)grid), dim3(NT), 0, st, x, rows, d, ldx, z,
-                       vals, idx, cap, counts, theta);
+    hipLaunchKernelGGL((stat_topk_kernel<NT, E, false, false>), g, b, 0, st, x, rows, d, ldx, z, vals, idx, cap,
+                       counts, theta);
   return hipGetLastError();
 }
 
