@@ -125,7 +125,8 @@ int spark_ffn_prefill_workspace_size(const spark_ffn_shape* s, int64_t T, size_t
   int st = check_ffn_shape(s);
   if (st != SPARK_OK) return st;
   if (T < 0) return SPARK_EINVAL;
-  if (s->wdtype != SPARK_BF16 || s->d_ff % 256 != 0 || s->r % 64 != 0 || s->d_model > 8192 || s->d_ff > 65536)
+  if (s->wdtype != SPARK_BF16 || s->d_ff % 256 != 0 || s->r % 64 != 0 || s->d_model % 8 != 0 ||
+      s->d_model > 8192 || s->d_ff > 65536)
     return SPARK_EUNSUPPORTED;
   *bytes = spark::prefill_workspace_bytes(s->d_model, s->d_ff, T);
   return SPARK_OK;

@@ -2,20 +2,24 @@
 //
 // Method (Spark Transformer reading notes, section "方法详解 / 关键设计", items
 // "Spark FFN" and "Statistical Top-k"): per token, predictor scores
-// h = K1^T q[:r], statistical top-k of h, then only the selected neurons' K2
-// columns and V rows: y = sum_i GELU(h_i - theta) (K2[:, i] . q[r:]) V[i, :].
+// h = K1^T q[:r], statistical top-k of h, then
+// y = sum over the selected i of GELU(h_i - theta) (K2[:, i] . q[r:]) V[i, :].
 //
-// gfx950 mapping:
-//   1. predictor_gemm: H = Q[:, :r] K1 for all tokens as a dense bf16 GEMM on
-//      the matrix cores (v_mfma_f32_32x32x16_bf16), fp32 accumulation and fp32
-//      scores (rounding the scores to bf16 would move them by far more than the
-//      tie band of the threshold).  128x128 output tile per workgroup, K in
-//      steps of 64 through double-buffered LDS.
-//   2. the statistical top-k kernel over the rows of H (one workgroup per
-//      token), giving each token's ascending neuron list and x - theta values;
-//   3. prefill_gather: one workgroup per token forms the gated values
-//      c_i = GELU(m_i) (K2^T q[r:])_i of its selected neurons, then y from
-//      their V rows (fixed summation order).
+// gfx950 mapping (every product on the matrix cores, v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation):
+//   1. H = Q[:, :r] K1 (fp32 scores: rounding them to bf16 would move them by
+//      far more than the tie band of the threshold);
+//   2. the statistical top-k kernel over the rows of H gives every token's
+//      theta (and, when a trace is asked for, its list);
+//   3. G = Q[:, r:] K2 with the gate in the epilogue: the tile writes
+//      C = GELU(H - theta) * G where H > theta and exact zeros elsewhere, as
+//      bf16;
+//   4. Y = C V over all neurons.  A neuron that is not selected contributes
+//      an exact zero, so this is the same sum as over the selected list; at a
+//      selection rate near 8% the dense products on the matrix cores take a
+//      fraction of the time of gathering ~737 K2 and V rows per token.  V is
+//      first transposed into the workspace so that both operands of every
+//      product are read along K.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -27,13 +31,21 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int GBM = 128, GBN = 128, GBK = 64;
 constexpr int GLD = GBK + 8;  // LDS row length in bf16 (16-byte pad against bank conflicts)
 
-// C[M][N] (fp32, row stride ldc) = A[M][K] (bf16, row stride lda) * B^T where
-// B is stored [N][K] (bf16, row stride ldb).  Requires N % 128 == 0,
-// K % 64 == 0, 16-byte aligned rows; rows of A past M are clamped on load and
-// not stored.
-__global__ __launch_bounds__(256) void predictor_gemm(const bf16_t* __restrict__ A, int lda,
-                                                      const bf16_t* __restrict__ B, int ldb, float* __restrict__ C,
-                                                      int ldc, int M, int N, int K) {
+enum { kEpiStore = 0, kEpiGate = 1 };
+
+// D = A[M][K] (bf16, row stride lda) * B^T where B is stored [N][K] (bf16,
+// row stride ldb), with K a multiple of 8 and 16-byte aligned rows.  Rows of
+// A and B past M and N are clamped on load and not stored; K past the end
+// reads as zeros.  128x128 output tile per workgroup (4 waves, 64x64 each),
+// K in steps of 64 through double-buffered LDS.
+//   kEpiStore: C[m][n] (fp32, row stride ldc) = D.
+//   kEpiGate:  Cg[m][n] (bf16, row stride ldc) = GELU(H - theta[m]) * D where
+//              H = H[m][n] (fp32, row stride ldh) > theta[m], else 0.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda,
+                                                    const bf16_t* __restrict__ B, int ldb, void* __restrict__ Cv,
+                                                    int ldc, int M, int N, int K, const float* __restrict__ H,
+                                                    int ldh, const float* __restrict__ theta) {
   __shared__ alignas(16) bf16_t As[2][GBM * GLD];
   __shared__ alignas(16) bf16_t Bs[2][GBN * GLD];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -48,9 +60,14 @@ __global__ __launch_bounds__(256) void predictor_gemm(const bf16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      const int am = min(m0 + row, M - 1);
-      ra[i] = load16(A + (size_t)am * lda + k0 + kc * 8);
-      rb[i] = load16(B + (size_t)(n0 + row) * ldb + k0 + kc * 8);
+      const int am = min(m0 + row, M - 1), bn = min(n0 + row, N - 1);
+      const int k = k0 + kc * 8;
+      const bool kin = k < K;
+      const int kk = kin ? k : 0;
+      const u32x4 va = load16(A + (size_t)am * lda + kk), vb = load16(B + (size_t)bn * ldb + kk);
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      ra[i] = kin ? va : zero;
+      rb[i] = kin ? vb : zero;
     }
   };
   auto sstore = [&](int buf) {
@@ -70,7 +87,7 @@ __global__ __launch_bounds__(256) void predictor_gemm(const bf16_t* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = K / GBK;
+  const int KT = (K + GBK - 1) / GBK;
   gload(0);
   sstore(0);
   __syncthreads();
@@ -104,120 +121,62 @@ __global__ __launch_bounds__(256) void predictor_gemm(const bf16_t* __restrict__
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (m < M) C[(size_t)m * ldc + n] = acc[i][j][r];
+        if (m < M && n < N) {
+          if (EPI == kEpiStore) {
+            reinterpret_cast<float*>(Cv)[(size_t)m * ldc + n] = acc[i][j][r];
+          } else {
+            const float h = H[(size_t)m * ldh + n], th = theta[m];
+            const float c = h > th ? gelu_tanh(h - th) * acc[i][j][r] : 0.f;
+            reinterpret_cast<bf16_t*>(Cv)[(size_t)m * ldc + n] = f32_to_bf16(c);
+          }
+        }
       }
 }
 
-constexpr int kGatherSeg = 4096;  // selected entries per LDS segment
-
-// One workgroup per token: gated values of the selected neurons, then y.
-__global__ __launch_bounds__(256) void prefill_gather(const bf16_t* __restrict__ Q, int d_model, int r,
-                                                      const bf16_t* __restrict__ k2t, const bf16_t* __restrict__ v,
-                                                      const int32_t* __restrict__ idx, const float* __restrict__ vals,
-                                                      const int32_t* __restrict__ counts, int cap,
-                                                      float* __restrict__ Y) {
-  __shared__ alignas(16) float qr[kDecodeMaxDModel];
-  __shared__ float cs[kGatherSeg];
-  __shared__ int is[kGatherSeg];
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int rc = d_model - r, K2C = rc / 8, VC = d_model / 8;
-  const int n = min(counts[t], cap);
-  for (int j = tid; j < rc; j += 256) qr[j] = bf16_to_f32(Q[(size_t)t * d_model + r + j]);
+// Vt[n][k] = V[k][n] for a bf16 [K][N] matrix, 64x64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_bf16(const bf16_t* __restrict__ V, int K, int N,
+                                                      bf16_t* __restrict__ Vt) {
+  __shared__ bf16_t tile[64][66];
+  const int tiles_n = (N + 63) / 64;
+  const int tk = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int k0 = tk * 64, n0 = tn * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = tid + 256 * i, r = e >> 6, c = e & 63;
+    if (k0 + r < K && n0 + c < N) tile[r][c] = V[(size_t)(k0 + r) * N + n0 + c];
+  }
   __syncthreads();
-  for (int s0 = 0; s0 < n || s0 == 0; s0 += kGatherSeg) {
-    const int ns = min(kGatherSeg, n - s0);
-    for (int e = tid; e < ns; e += 256) is[e] = idx[(size_t)t * cap + s0 + e];
-    __syncthreads();
-    // K2 gather-dot: wave wv takes entries wv, wv + 4, ...; three rows per pass
-    for (int e0 = wv; e0 < ns; e0 += 12) {
-      float sacc[3] = {0.f, 0.f, 0.f};
-      for (int c0 = 0; c0 < K2C; c0 += 64) {
-        u32x4 raw[3];
-        const int cc = min(c0 + lane, K2C - 1);
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
-          const int e = min(e0 + 4 * u, ns - 1);
-          raw[u] = load16(k2t + (size_t)is[e] * rc + (size_t)cc * 8);
-        }
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-          float wf[8];
-          Chunk<bf16_t>::widen(raw[u], wf);
-          const f32x4* qq = reinterpret_cast<const f32x4*>(qr + cc * 8);
-          const f32x4 q0 = qq[0], q1 = qq[1];
-          const float a = wf[0] * q0.x + wf[1] * q0.y + wf[2] * q0.z + wf[3] * q0.w + wf[4] * q1.x + wf[5] * q1.y +
-                          wf[6] * q1.z + wf[7] * q1.w;
-          sacc[u] += (c0 + lane < K2C) ? a : 0.f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        const float g = wave_sum_dpp(sacc[u]);
-        const int e = e0 + 4 * u;
-        if (lane == 0 && e < ns) cs[e] = gelu_tanh(vals[(size_t)t * cap + s0 + e]) * g;
-      }
-    }
-    __syncthreads();
-    // V rows: thread owns 8 consecutive output columns, entries in ascending order
-    for (int vc = tid; vc < VC; vc += 256) {
-      float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = s0 == 0 ? 0.f : Y[(size_t)t * d_model + vc * 8 + i];
-      int e = 0;
-      for (; e + 8 <= ns; e += 8) {
-        u32x4 raw[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) raw[u] = load16(v + (size_t)is[e + u] * d_model + (size_t)vc * 8);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          float wf[8];
-          Chunk<bf16_t>::widen(raw[u], wf);
-          const float c = cs[e + u];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] += c * wf[i];
-        }
-      }
-      for (; e < ns; ++e) {
-        float wf[8];
-        Chunk<bf16_t>::widen(load16(v + (size_t)is[e] * d_model + (size_t)vc * 8), wf);
-        const float c = cs[e];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += c * wf[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Y[(size_t)t * d_model + vc * 8 + i] = acc[i];
-    }
-    __syncthreads();
-    if (n == 0) break;
+  for (int i = 0; i < 16; ++i) {
+    const int e = tid + 256 * i, r = e >> 6, c = e & 63;  // r: n within tile, c: k within tile
+    if (n0 + r < N && k0 + c < K) Vt[(size_t)(n0 + r) * K + k0 + c] = tile[c][r];
   }
 }
 
-// Copy the first `cap` list entries of every token into the caller's trace
-// (-1 past the token's count).
-__global__ void copy_lists(const int32_t* __restrict__ src, int src_cap, const int32_t* __restrict__ counts,
-                           int32_t* __restrict__ dst, int64_t dst_cap, int64_t T) {
+// Positions of the caller's list trace past a token's count read -1.
+__global__ void pad_lists(const int32_t* __restrict__ counts, int32_t* __restrict__ dst, int64_t cap, int64_t T) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T * dst_cap) return;
-  const int64_t t = i / dst_cap, e = i - t * dst_cap;
-  dst[i] = (e < src_cap && e < counts[t]) ? src[t * src_cap + e] : -1;
+  if (i >= T * cap) return;
+  const int64_t t = i / cap, e = i - t * cap;
+  if (e >= counts[t]) dst[i] = -1;
 }
 
 // ---------------------------------------------------------------- host side
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct PrefillLayout {
-  size_t H, vals, idx, counts, theta, total;
+  size_t H, C, Vt, counts, theta, total;
 };
 
-static PrefillLayout prefill_layout(int64_t d_ff, int64_t T) {
+static PrefillLayout prefill_layout(int64_t d_model, int64_t d_ff, int64_t T) {
   PrefillLayout L;
   size_t off = 0;
-  L.H = off;
+  L.H = off;  // fp32 predictor scores [T][d_ff]
   off += round_up((size_t)T * d_ff * 4, 256);
-  L.vals = off;
-  off += round_up((size_t)T * d_ff * 4, 256);
-  L.idx = off;
-  off += round_up((size_t)T * d_ff * 4, 256);
+  L.C = off;  // bf16 gated values [T][d_ff] (zero where not selected)
+  off += round_up((size_t)T * d_ff * 2, 256);
+  L.Vt = off;  // bf16 V^T [d_model][d_ff]
+  off += round_up((size_t)d_model * d_ff * 2, 256);
   L.counts = off;
   off += round_up((size_t)T * 4, 256);
   L.theta = off;
@@ -227,39 +186,55 @@ static PrefillLayout prefill_layout(int64_t d_ff, int64_t T) {
 }
 
 size_t prefill_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t T) {
-  (void)d_model;
-  return prefill_layout(d_ff, T).total;
+  return prefill_layout(d_model, d_ff, T).total;
+}
+
+template <int EPI>
+static hipError_t launch_gemm(const bf16_t* A, int lda, const bf16_t* B, int ldb, void* C, int ldc, int M, int N,
+                              int K, const float* H, int ldh, const float* theta, hipStream_t st) {
+  const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+  hipLaunchKernelGGL(gemm_bf16_nt<EPI>, dim3(tiles), dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K, H, ldh,
+                     theta);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(const spark_ffn_shape& s, const spark_ffn_weights& w, const void* Q, int64_t T, float* Y,
                           double z, const spark_ffn_trace* trace, void* ws, hipStream_t st) {
-  const PrefillLayout L = prefill_layout(s.d_ff, T);
+  const PrefillLayout L = prefill_layout(s.d_model, s.d_ff, T);
   char* base = (char*)ws;
   float* H = (float*)(base + L.H);
-  float* vals = (float*)(base + L.vals);
-  int32_t* idx = (int32_t*)(base + L.idx);
+  bf16_t* C = (bf16_t*)(base + L.C);
+  bf16_t* Vt = (bf16_t*)(base + L.Vt);
   int32_t* counts = (int32_t*)(base + L.counts);
   float* theta = (float*)(base + L.theta);
-  const int M = (int)T, N = (int)s.d_ff, K = (int)s.r, dm = (int)s.d_model;
-  const int tiles = ((M + GBM - 1) / GBM) * (N / GBN);
-  hipLaunchKernelGGL(predictor_gemm, dim3(tiles), dim3(256), 0, st, (const bf16_t*)Q, dm, (const bf16_t*)w.k1t, K, H,
-                     N, M, N, K);
-  hipError_t e = hipGetLastError();
+  const int M = (int)T, F = (int)s.d_ff, r = (int)s.r, dm = (int)s.d_model;
+  const bf16_t* Qb = (const bf16_t*)Q;
+  // 1. predictor scores
+  hipError_t e = launch_gemm<kEpiStore>(Qb, dm, (const bf16_t*)w.k1t, r, H, F, M, F, r, nullptr, 0, nullptr, st);
   if (e != hipSuccess) return e;
-  e = launch_stat_topk(H, T, s.d_ff, s.d_ff, z, vals, idx, s.d_ff, counts, theta, st);
+  // 2. theta per token (and the lists, straight into the trace when asked for)
+  const bool want_idx = trace && trace->idx && trace->cap > 0;
+  e = launch_stat_topk(H, T, s.d_ff, s.d_ff, z, nullptr, want_idx ? trace->idx : nullptr, want_idx ? trace->cap : 0,
+                       counts, theta, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_gather, dim3((unsigned)T), dim3(256), 0, st, (const bf16_t*)Q, dm, K,
-                     (const bf16_t*)w.k2t, (const bf16_t*)w.v, idx, vals, counts, N, Y);
+  // 3. gated values C = GELU(H - theta) * (Q[:, r:] K2) on the selected entries
+  e = launch_gemm<kEpiGate>(Qb + r, dm, (const bf16_t*)w.k2t, dm - r, C, F, M, F, dm - r, H, F, theta, st);
+  if (e != hipSuccess) return e;
+  // 4. Y = C V
+  hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)(((F + 63) / 64) * ((dm + 63) / 64))), dim3(256), 0, st,
+                     (const bf16_t*)w.v, F, dm, Vt);
   e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_gemm<kEpiStore>(C, F, Vt, F, Y, dm, M, dm, F, nullptr, 0, nullptr, st);
   if (e != hipSuccess) return e;
   if (trace) {
     if (trace->counts) e = hipMemcpyAsync(trace->counts, counts, (size_t)T * 4, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess && trace->theta)
       e = hipMemcpyAsync(trace->theta, theta, (size_t)T * 4, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess && trace->idx && trace->cap > 0) {
+    if (e == hipSuccess && want_idx) {
       const int64_t n = T * trace->cap;
-      hipLaunchKernelGGL(copy_lists, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx, N, counts,
-                         trace->idx, trace->cap, T);
+      hipLaunchKernelGGL(pad_lists, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, counts, trace->idx,
+                         trace->cap, T);
       e = hipGetLastError();
     }
   }

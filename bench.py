@@ -135,8 +135,12 @@ def extra_workloads(torch, sf, synth, dev, seed):
     K1 = layer[0].t().contiguous()  # [r][d_ff]
     ref_ms = _time_ms(torch, lambda: torch.mm(Qr, K1), reps=10)
     del Qr, K1
+    # the three products run dense on the matrix cores (unselected neurons
+    # contribute exact zeros): scores, gated K2 values, and C V
+    dense = 2.0 * T * D_FF * (R + (D_MODEL - R) + D_MODEL)
     res["prefill"] = {"workload": "4096 tokens, one 2304 x 9216 layer (r 1152, k 737), bf16", "ms": ms,
                       "us_per_token": ms * 1e3 / T, "predictor_gflop": flops / 1e9,
+                      "dense_products_gflop": dense / 1e9, "dense_products_tflops": dense / ms / 1e9,
                       "hipblaslt_predictor_gemm_ms": ref_ms,
                       "hipblaslt_predictor_tflops": flops / ref_ms / 1e9}
     del Q, layer

@@ -117,14 +117,17 @@ int spark_ffn_decode(const spark_ffn_shape *s, const spark_ffn_weights *layers, 
                      hipStream_t stream);
 
 /*
- * Spark FFN prefill: the same layer (one layer) applied to T tokens at once.
- * The predictor K1^T Q[:, :r] runs as a dense GEMM on the matrix cores, the
- * statistical top-k per token over its fp32 scores, then each token's
- * selected K2 columns and V rows.
+ * Spark FFN prefill: the same layer (one layer) applied to T tokens at once
+ * (same result as spark_ffn_decode of one layer per token, without the
+ * normalisation).  The predictor scores K1^T Q[:, :r] are a dense GEMM on the
+ * matrix cores (fp32 scores), the statistical top-k runs per token over them,
+ * and the gated K2 and V products run dense on the matrix cores with the
+ * unselected neurons' gated values set to exact zeros.
  *   Q [T][d_model] of dtype s->wdtype; Y [T][d_model] fp32; trace may be NULL
  *   (its q_in is ignored).
  * Requires bf16 weights and Q, d_ff a multiple of 256, r a multiple of 64,
- * d_model <= 8192, d_ff <= 65536.
+ * d_model a multiple of 8, d_model <= 8192, d_ff <= 65536.  The workspace
+ * holds the scores, the gated values and a transposed copy of V.
  */
 int spark_ffn_prefill(const spark_ffn_shape *s, const spark_ffn_weights *w, const void *Q, int64_t T, float *Y,
                       const spark_ffn_trace *trace, void *ws, size_t ws_bytes, hipStream_t stream);

@@ -71,5 +71,8 @@ def test_prefill_matches_decode_per_token():
     Y = sf.spark_ffn_prefill(to_dev(Qb), layer, k, r).cpu().numpy()
     q32 = torch.from_numpy(synth.bf16_bits_to_f32(Qb)).to(DEV)
     Yd = sf.spark_ffn_decode(q32, [layer], k, r).cpu().numpy()
+    # prefill feeds the gated values to the V product on the matrix cores as
+    # bf16 (relative rounding 2^-9 each); decode keeps them fp32.  The rounding
+    # errors of the ~80 terms add at random, far inside 2^-8 of the norm.
     for t in range(16):
-        assert rel_err(Y[t], Yd[t]) <= 1e-4
+        assert rel_err(Y[t], Yd[t]) <= 2.0 ** -8
