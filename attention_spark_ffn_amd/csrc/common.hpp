@@ -198,9 +198,12 @@ __device__ __forceinline__ Moments wave_merge(Moments m) {
 
 // ---------------------------------------------------------------- activations
 // GELU, tanh form: 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
+// GELU, tanh form: 0.5 v (1 + tanh(u)), u = sqrt(2/pi) (v + 0.044715 v^3),
+// evaluated through the identity 0.5 (1 + tanh(u)) = 1 / (1 + e^(-2u)): one
+// exponential and one division, and no cancellation for either sign of v.
 __device__ __forceinline__ float gelu_tanh(float v) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * v * (1.f + tanhf(c * (v + 0.044715f * v * v * v)));
+  const float c2 = 1.5957691216057308f;  // 2 sqrt(2/pi)
+  return v / (1.f + __expf(-c2 * (v + 0.044715f * v * v * v)));
 }
 // softplus log(1 + e^v) in the overflow-free form max(v,0) + log1p(e^-|v|).
 __device__ __forceinline__ float softplus(float v) { return fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v))); }

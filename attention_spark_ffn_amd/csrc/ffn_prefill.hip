@@ -54,28 +54,32 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt(const bf16_t* __restrict__ A
   const int m0 = tm * GBM, n0 = tn * GBN;
   const int wm = wv >> 1, wn = wv & 1;  // 2 x 2 waves, 64 x 64 outputs each
 
-  // global -> register staging: 4 chunks of 16 bytes of A and of B per thread
+  // global -> register staging: 4 chunks of 16 bytes of A and of B per
+  // thread.  Chunks past K are loaded from column 0 and replaced by zeros only
+  // when stored to LDS, after the MFMAs of the current step, so the loads stay
+  // in flight across those MFMAs.
   u32x4 ra[4], rb[4];
+  int kload = 0;
   auto gload = [&](int k0) {
+    kload = k0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
       const int am = min(m0 + row, M - 1), bn = min(n0 + row, N - 1);
       const int k = k0 + kc * 8;
-      const bool kin = k < K;
-      const int kk = kin ? k : 0;
-      const u32x4 va = load16(A + (size_t)am * lda + kk), vb = load16(B + (size_t)bn * ldb + kk);
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      ra[i] = kin ? va : zero;
-      rb[i] = kin ? vb : zero;
+      const int kk = k < K ? k : 0;
+      ra[i] = load16(A + (size_t)am * lda + kk);
+      rb[i] = load16(B + (size_t)bn * ldb + kk);
     }
   };
   auto sstore = [&](int buf) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      *reinterpret_cast<u32x4*>(&As[buf][row * GLD + kc * 8]) = ra[i];
-      *reinterpret_cast<u32x4*>(&Bs[buf][row * GLD + kc * 8]) = rb[i];
+      const bool kin = kload + kc * 8 < K;
+      *reinterpret_cast<u32x4*>(&As[buf][row * GLD + kc * 8]) = kin ? ra[i] : zero;
+      *reinterpret_cast<u32x4*>(&Bs[buf][row * GLD + kc * 8]) = kin ? rb[i] : zero;
     }
   };
 
@@ -114,23 +118,38 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt(const bf16_t* __restrict__ A
   }
   // D layout of the 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
+    float th[16];
+    if (EPI == kEpiGate) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int r = 0; r < 16; ++r)
+        th[r] = theta[min(m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), M - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+      float hv[16];
+      if (EPI == kEpiGate) {  // all 16 score loads of the block before any use
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          hv[r] = H[(size_t)min(m, M - 1) * ldh + min(n, N - 1)];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
         if (m < M && n < N) {
           if (EPI == kEpiStore) {
             reinterpret_cast<float*>(Cv)[(size_t)m * ldc + n] = acc[i][j][r];
           } else {
-            const float h = H[(size_t)m * ldh + n], th = theta[m];
-            const float c = h > th ? gelu_tanh(h - th) * acc[i][j][r] : 0.f;
+            const float c = hv[r] > th[r] ? gelu_tanh(hv[r] - th[r]) * acc[i][j][r] : 0.f;
             reinterpret_cast<bf16_t*>(Cv)[(size_t)m * ldc + n] = f32_to_bf16(c);
           }
         }
       }
+    }
+  }
 }
 
 // Vt[n][k] = V[k][n] for a bf16 [K][N] matrix, 64x64 tiles through LDS.
