@@ -221,9 +221,13 @@ def main():
     per_launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
     failed = sf.decode_workspace_failed(device=dev)
 
-    # actual per-layer selected counts of the timed tokens (same inputs, deterministic)
-    _, tr = sf.spark_ffn_decode(qs[args.warmup:], layers, K, R, trace=True, cap=1)
-    counts = tr["counts"].cpu().numpy()
+    # actual per-layer selected counts of the timed tokens (same inputs,
+    # deterministic), one launch per token like the timed launches
+    counts = []
+    for i in range(args.steps):
+        _, tr = sf.spark_ffn_decode(qs[args.warmup + i:args.warmup + i + 1], layers, K, R, trace=True, cap=1)
+        counts.append(tr["counts"])
+    counts = torch.cat(counts).cpu().numpy()
     bytes_per_token = np.array([algorithmic_bytes(c) for c in counts])
     avg_launch_s = per_launch_ms.mean() / 1e3
     achieved_gbs = bytes_per_token.mean() / avg_launch_s / 1e9
