@@ -9,17 +9,23 @@
 //   s_j = q_h[:r] . k1[g][j];  S = stat top-k of s (all j when n_ctx <= k_attn)
 //   out_h = sum_{j in S} softmax_S(s)_j * softplus(q_h[r:] . k2[g][j]) * v[g][j]
 //
-// gfx950 mapping:
-//   attn_scores: the predictor scan, the only pass over all n_ctx tokens.  A
-//     workgroup takes 256 tokens of one KV head; 16 lanes read one 16-byte
-//     chunk each of a token's k1 row (r = 128 bf16 is exactly one 256-byte
-//     row per 16 lanes), multiply by both (all) query heads of the group held
-//     in registers, and reduce within the 16-lane DPP row.
-//   attn_select_gather: one 1024-thread workgroup per query head: mean and
-//     squared deviations of the scores (two exact passes), theta, ascending
-//     compaction of the selected tokens (one block scan over per-thread
-//     contiguous segments), softmax over S, softplus gates from the k2 rows,
-//     and the weighted sum of the v rows, every reduction in a fixed order.
+// gfx950 mapping: the context is cut into chunks of 256 tokens, and every
+// step runs over (head, chunk) pairs so that the whole chip works on one
+// decode step:
+//   attn_scores (KV head, chunk): the predictor scan, the only pass over all
+//     n_ctx tokens.  16 lanes read one 16-byte chunk each of a token's k1 row
+//     (r = 128 bf16 is one 256-byte row per 16 lanes), all 16 tokens of a
+//     lane group's rows are loaded before any is used, and every query head of
+//     the group is applied from registers (DPP row sums).  The workgroup also
+//     writes each head's (mean, M2) over the chunk.
+//   attn_chunk (query head, chunk): theta from the chunk statistics (the same
+//     fixed-order combination in every workgroup of the head), the chunk's
+//     selected tokens in ascending order, their softplus gates from the k2
+//     rows, and the chunk's part of the softmax-weighted sum of v rows relative
+//     to the chunk's own maximum score (m_c, l_c = sum of e^(s - m_c), o_c).
+//   attn_merge (query head): out = sum_c e^(m_c - m) o_c / sum_c e^(m_c - m) l_c
+//     with m the largest m_c, the count, theta and (when asked for) the
+//     ascending list.  Every sum runs in a fixed order.
 #include <cmath>
 
 #include "common.hpp"
@@ -27,22 +33,30 @@
 
 namespace spark {
 
-constexpr int kScoreTokens = 256;  // tokens per score workgroup (16 passes of 16)
-constexpr int kMaxGroup = 8;       // query heads per KV head handled in registers
+constexpr int kChunk = 256;   // tokens per chunk (one workgroup of the scan and of the selection)
+constexpr int kMaxGroup = 8;  // query heads per KV head handled in registers
 
 __global__ __launch_bounds__(256) void attn_scores(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k1,
                                                    int Hq, int Hkv, int n_ctx, int hd, int r,
-                                                   float* __restrict__ scores) {
-  const int tid = threadIdx.x, l16 = tid & 15, tok = tid >> 4;  // 16 tokens per pass
+                                                   float* __restrict__ scores, float2* __restrict__ cstat) {
+  __shared__ float sc[kMaxGroup][kChunk];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = tid & 15, tok = tid >> 4;  // 16 tokens/pass
   const int group = Hq / Hkv;
-  const int nsplit = (n_ctx + kScoreTokens - 1) / kScoreTokens;
-  const int g = blockIdx.x / nsplit, j0 = (blockIdx.x % nsplit) * kScoreTokens;
+  const int nch = (n_ctx + kChunk - 1) / kChunk;
+  const int g = blockIdx.x / nch, c0 = blockIdx.x % nch, j0 = c0 * kChunk;
+  const int nc = min(kChunk, n_ctx - j0);
   const int CT = r / 8;  // 16-byte chunks per k1 row
   for (int h0 = 0; h0 < group; h0 += kMaxGroup) {
     const int nh = min(kMaxGroup, group - h0);
     for (int cb = 0; cb < CT; cb += 16) {
       const int c = cb + l16;
-      // this lane's q chunk for each head of the group
+      // every k1 load of the lane first (16 tokens), then the q chunks
+      u32x4 raw[kChunk / 16];
+#pragma unroll
+      for (int p = 0; p < kChunk / 16; ++p) {
+        const int j = min(j0 + p * 16 + tok, n_ctx - 1);
+        raw[p] = load16(k1 + ((size_t)g * n_ctx + j) * r + (size_t)min(c, CT - 1) * 8);
+      }
       float qv[kMaxGroup][8];
 #pragma unroll
       for (int u = 0; u < kMaxGroup; ++u) {
@@ -52,134 +66,130 @@ __global__ __launch_bounds__(256) void attn_scores(const bf16_t* __restrict__ q,
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[u][e] = (c < CT && u < nh) ? wf[e] : 0.f;
       }
-      for (int p = 0; p < kScoreTokens / 16; p += 4) {
-        u32x4 raw[4];
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const int j = min(j0 + (p + pp) * 16 + tok, n_ctx - 1);
-          raw[pp] = load16(k1 + ((size_t)g * n_ctx + j) * r + (size_t)min(c, CT - 1) * 8);
-        }
+      for (int p = 0; p < kChunk / 16; ++p) {
+        const int t = p * 16 + tok;
+        float wf[8];
+        Chunk<bf16_t>::widen(raw[p], wf);
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const int j = j0 + (p + pp) * 16 + tok;
-          float wf[8];
-          Chunk<bf16_t>::widen(raw[pp], wf);
+        for (int u = 0; u < kMaxGroup; ++u) {
+          if (u < nh) {
+            float a = 0.f;
 #pragma unroll
-          for (int u = 0; u < kMaxGroup; ++u) {
-            if (u < nh) {
-              float a = 0.f;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) a += wf[e] * qv[u][e];
-              a = row16_sum(a);
-              if (l16 == 0 && j < n_ctx) {
-                float* dst = scores + (size_t)(g * group + h0 + u) * n_ctx + j;
-                *dst = cb == 0 ? a : *dst + a;
-              }
-            }
+            for (int e = 0; e < 8; ++e) a += wf[e] * qv[u][e];
+            a = row16_sum(a);
+            if (l16 == 0) sc[u][t] = cb == 0 ? a : sc[u][t] + a;
           }
         }
       }
     }
+    __syncthreads();
+    // scores out, and each head's (mean, M2) over the chunk: wave w takes heads
+    // w, w + 4, each lane four tokens
+    for (int e = tid; e < nh * kChunk; e += 256) {
+      const int u = e / kChunk, t = e % kChunk;
+      if (t < nc) scores[(size_t)(g * group + h0 + u) * n_ctx + j0 + t] = sc[u][t];
+    }
+    for (int u = wv; u < nh; u += 4) {
+      float x[kChunk / 64], s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < kChunk / 64; ++i) {
+        const int t = lane + 64 * i;
+        x[i] = t < nc ? sc[u][t] : 0.f;
+        s1 += x[i];
+      }
+      const float mean = wave_sum_dpp(s1) / (float)nc;
+      float s2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < kChunk / 64; ++i) {
+        const float d = x[i] - mean;
+        s2 += lane + 64 * i < nc ? d * d : 0.f;
+      }
+      const float m2 = wave_sum_dpp(s2);
+      if (lane == 0) cstat[(size_t)(g * group + h0 + u) * nch + c0] = make_float2(mean, m2);
+    }
+    __syncthreads();
   }
 }
 
-// Fixed-order reductions over the 1024 threads of the selection kernel.
-struct SelShared {
-  float red[16];
-  int ired[16];
-  int wpre[16];
-};
-__device__ __forceinline__ float block_sum(float v, SelShared& S) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  v = wave_sum_dpp(v);
-  __syncthreads();
-  if (lane == 0) S.red[wv] = v;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) t += S.red[w];
-  return t;
-}
-__device__ __forceinline__ float block_max(float v, SelShared& S) {
+// Fixed-order reductions over the 256 threads of a chunk workgroup.
+__device__ __forceinline__ float block_max256(float v, float* red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   v = wave_max(v);
+  if (lane == 0) red[wv] = v;
   __syncthreads();
-  if (lane == 0) S.red[wv] = v;
+  const float t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
-  float t = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) t = fmaxf(t, S.red[w]);
   return t;
 }
 
-__global__ __launch_bounds__(1024) void attn_select_gather(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k2, const bf16_t* __restrict__ v, int Hq, int Hkv,
-    int n_ctx, int hd, int r, int dense, float z, const float* __restrict__ scores, int32_t* __restrict__ lidx,
-    float* __restrict__ lval, float* __restrict__ out, int32_t* __restrict__ counts, int32_t* __restrict__ idx_out,
-    int64_t cap, float* __restrict__ theta_out) {
-  __shared__ SelShared S;
-  __shared__ alignas(16) float qc[512];    // q_h[r:]
-  __shared__ float opart[4][512];          // per-quarter sums of the output
-  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// theta of head h from its chunk statistics: mean = sum n_c mean_c / n, then
+// M2 = sum (M2_c + n_c (mean_c - mean)^2) (two plain sums in a fixed order,
+// Chan et al.'s combination).  Called by one wave; every lane gets the result.
+__device__ __forceinline__ float head_theta(const float2* __restrict__ cst, int nch, int n_ctx, float z, int lane) {
+  float s1 = 0.f;
+  for (int c = lane; c < nch; c += 64) s1 += (float)min(kChunk, n_ctx - c * kChunk) * cst[c].x;
+  const float mean = wave_sum_dpp(s1) / (float)n_ctx;
+  float s2 = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    const float2 st = cst[c];
+    const float d = st.x - mean;
+    s2 += st.y + (float)min(kChunk, n_ctx - c * kChunk) * d * d;
+  }
+  const float m2 = wave_sum_dpp(s2);
+  return mean + sqrtf(m2 / (float)n_ctx) * z;
+}
+
+// Partial of one (query head, chunk): m_c, l_c, count, then o_c[hd].
+constexpr int kPartHead = 4;
+
+__global__ __launch_bounds__(256) void attn_chunk(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k2,
+                                                  const bf16_t* __restrict__ v, int Hq, int Hkv, int n_ctx, int hd,
+                                                  int r, int dense, float z, const float* __restrict__ scores,
+                                                  const float2* __restrict__ cstat, float* __restrict__ part,
+                                                  int32_t* __restrict__ lidx) {
+  __shared__ alignas(16) float qc[512];  // q_h[r:]
+  __shared__ int loc[kChunk];            // selected tokens of the chunk (offsets), ascending
+  __shared__ float sv[kChunk];           // their scores, then e^(s - m_c)
+  __shared__ float wu[kChunk];           // e^(s - m_c) * softplus gate
+  __shared__ float red[4];
+  __shared__ int wcnt[4];
+  __shared__ float th_s;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nch = (n_ctx + kChunk - 1) / kChunk;
+  const int h = blockIdx.x / nch, c0 = blockIdx.x % nch, j0 = c0 * kChunk;
+  const int nc = min(kChunk, n_ctx - j0);
   const int g = h / (Hq / Hkv), rc = hd - r;
-  const float* s = scores + (size_t)h * n_ctx;
-  int32_t* li = lidx + (size_t)h * n_ctx;
-  float* lv = lval + (size_t)h * n_ctx;
-  for (int c = tid; c < rc; c += 1024) qc[c] = bf16_to_f32(q[(size_t)h * hd + r + c]);
-  // thread-contiguous segment of the scores
-  const int seg = (n_ctx + 1023) / 1024, a0 = min(tid * seg, n_ctx), a1 = min(a0 + seg, n_ctx);
-  float theta = NAN;
-  if (!dense) {
-    float t1 = 0.f;
-    for (int j = a0; j < a1; ++j) t1 += s[j];
-    const float mean = block_sum(t1, S) / (float)n_ctx;
-    float t2 = 0.f;
-    for (int j = a0; j < a1; ++j) {
-      const float d = s[j] - mean;
-      t2 += d * d;
-    }
-    const float m2 = block_sum(t2, S);
-    theta = mean + sqrtf(m2 / (float)n_ctx) * z;
+  for (int c = tid; c < rc; c += 256) qc[c] = bf16_to_f32(q[(size_t)h * hd + r + c]);
+  if (wv == 0) {
+    const float th = dense ? -INFINITY : head_theta(cstat + (size_t)h * nch, nch, n_ctx, z, lane);
+    if (lane == 0) th_s = th;
   }
-  // ascending compaction of the selected tokens
-  int cnt = 0;
-  float smax = -INFINITY;
-  for (int j = a0; j < a1; ++j) {
-    const bool on = dense || s[j] > theta;
-    cnt += on ? 1 : 0;
-    smax = on ? fmaxf(smax, s[j]) : smax;
-  }
-  const int pre_w = wave_excl_scan(cnt, lane);
-  const int wtot = __shfl(pre_w + cnt, 63, 64);
+  const float s = tid < nc ? scores[(size_t)h * n_ctx + j0 + tid] : -INFINITY;
   __syncthreads();
-  if (lane == 0) S.ired[wv] = wtot;
+  const float theta = th_s;
+  const bool on = tid < nc && (dense || s > theta);
+  // ascending compaction within the chunk
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+  const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+  if (lane == 0) wcnt[wv] = __builtin_popcountll(bal);
   __syncthreads();
-  int base = 0, total = 0;
+  int base = 0, cnt = 0;
 #pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    base += w < wv ? S.ired[w] : 0;
-    total += S.ired[w];
+  for (int w = 0; w < 4; ++w) {
+    base += w < wv ? wcnt[w] : 0;
+    cnt += wcnt[w];
   }
-  int pos = base + pre_w;
-  for (int j = a0; j < a1; ++j) {
-    if (dense || s[j] > theta) {
-      li[pos] = j;
-      lv[pos] = s[j];
-      ++pos;
-    }
+  if (on) {
+    loc[base + pre] = tid;
+    sv[base + pre] = s;
   }
-  const float mx = block_max(smax, S);
-  __syncthreads();  // list entries written by other threads
-  // softmax denominator over S (ascending order within each thread's slice)
-  const int per = (total + 1023) / 1024, b0 = min(tid * per, total), b1 = min(b0 + per, total);
-  float den = 0.f;
-  for (int e = b0; e < b1; ++e) den += __expf(lv[e] - mx);
-  den = block_sum(den, S);
-  // gates: softplus(q[r:] . k2[g][j]) for every selected token; 16 lanes per token
-  const int CT2 = rc / 8, l16 = lane & 15, sub = tid >> 4;  // 64 tokens per pass
-  for (int e0 = 0; e0 < total; e0 += 64) {
+  const float mc = block_max256(on ? s : -INFINITY, red);  // also orders the list writes
+  // gates: softplus(q[r:] . k2[g][j]), 16 lanes per token, 16 tokens per pass
+  const int CT2 = rc / 8, l16 = tid & 15, sub = tid >> 4;
+  for (int e0 = 0; e0 < cnt; e0 += 16) {
     const int e = e0 + sub;
-    const int j = li[min(e, total - 1)];
+    const int j = j0 + loc[min(e, cnt - 1)];
     float acc = 0.f;
     for (int cb = 0; cb < CT2; cb += 16) {
       const int c = cb + l16;
@@ -192,60 +202,209 @@ __global__ __launch_bounds__(1024) void attn_select_gather(
       acc += c < CT2 ? a : 0.f;
     }
     acc = row16_sum(acc);
-    __syncthreads();  // every lane has read lv[e] before it is overwritten below
-    if (l16 == 0 && e < total) lv[e] = (__expf(lv[e] - mx) / den) * softplus(acc);
+    if (l16 == 0 && e < cnt) {
+      const float p = __expf(sv[e] - mc);
+      wu[e] = p * softplus(acc);
+      sv[e] = p;
+    }
   }
   __syncthreads();
-  // out[c] = sum over S (ascending, in four interleaved quarters) of w u v[c]
-  const int c = tid & 255, quarter = tid >> 8;
-  float o = 0.f;
-  if (c < hd)
-    for (int e = quarter; e < total; e += 4) {
-      const int j = li[e];
-      o += lv[e] * bf16_to_f32(v[((size_t)g * n_ctx + j) * hd + c]);
-    }
-  if (c < hd) opart[quarter][c] = o;
-  __syncthreads();
-  if (tid < hd) out[(size_t)h * hd + tid] = ((opart[0][tid] + opart[1][tid]) + opart[2][tid]) + opart[3][tid];
-  if (hd > 256)  // wider heads: the remaining columns, same order
-    for (int cc = 256 + tid; cc < hd; cc += 1024) {
-      float oo = 0.f;
-      for (int e = 0; e < total; ++e) oo += lv[e] * bf16_to_f32(v[((size_t)g * n_ctx + li[e]) * hd + cc]);
-      out[(size_t)h * hd + cc] = oo;
-    }
+  float* pt = part + (size_t)blockIdx.x * (kPartHead + hd);
   if (tid == 0) {
-    if (counts) counts[h] = total;
-    if (theta_out) theta_out[h] = theta;
+    float l = 0.f;
+    for (int e = 0; e < cnt; ++e) l += sv[e];  // ascending
+    pt[0] = mc;
+    pt[1] = l;
+    pt[2] = __int_as_float(cnt);
+    pt[3] = dense ? NAN : theta;  // every token attended: no threshold
   }
-  if (idx_out)
-    for (int e = tid; e < cap; e += 1024) idx_out[(size_t)h * cap + e] = e < total ? li[e] : -1;
+  // o_c[col]: sum over the chunk's selected tokens, ascending; four loads in flight
+  for (int col = tid; col < hd; col += 256) {
+    float o = 0.f;
+    int e = 0;
+    for (; e + 4 <= cnt; e += 4) {
+      float x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = bf16_to_f32(v[((size_t)g * n_ctx + j0 + loc[e + u]) * hd + col]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o += wu[e + u] * x[u];
+    }
+    for (; e < cnt; ++e) o += wu[e] * bf16_to_f32(v[((size_t)g * n_ctx + j0 + loc[e]) * hd + col]);
+    pt[kPartHead + col] = o;
+  }
+  if (lidx)
+    for (int e = tid; e < cnt; e += 256) lidx[(size_t)h * n_ctx + j0 + e] = j0 + loc[e];
+}
+
+constexpr int kMaxChunks = 4096;  // n_ctx <= 2^20
+
+// One 1024-thread workgroup per query head.  The chunk statistics are read in
+// parallel; the weighted column sums run in four quarters of the chunks (chunk
+// c in quarter c % 4, eight loads in flight per thread) combined in a fixed
+// order.
+__global__ __launch_bounds__(1024) void attn_merge(int n_ctx, int hd, const float* __restrict__ part,
+                                                   const int32_t* __restrict__ lidx, float* __restrict__ out,
+                                                   int32_t* __restrict__ counts, int32_t* __restrict__ idx_out,
+                                                   int64_t cap, float* __restrict__ theta_out) {
+  __shared__ float wexp[kMaxChunks];  // m_c, then e^(m_c - m)
+  __shared__ int ccnt[kMaxChunks];
+  __shared__ float red[16];
+  __shared__ int ired[16];
+  __shared__ float opart[4][256];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nch = (n_ctx + kChunk - 1) / kChunk;
+  const int stride = kPartHead + hd;
+  const float* ph = part + (size_t)h * nch * stride;
+  // chunk maxima and counts
+  float mx = -INFINITY;
+  int cn = 0;
+  for (int c = tid; c < nch; c += 1024) {
+    const float mc = ph[(size_t)c * stride];
+    const int k = __float_as_int(ph[(size_t)c * stride + 2]);
+    wexp[c] = mc;
+    ccnt[c] = k;
+    mx = fmaxf(mx, mc);
+    cn += k;
+  }
+  mx = wave_max(mx);
+  cn = wave_sum_int(cn);
+  if (lane == 0) {
+    red[wv] = mx;
+    ired[wv] = cn;
+  }
+  __syncthreads();
+  float m = -INFINITY;
+  int tot = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    m = fmaxf(m, red[w]);
+    tot += ired[w];
+  }
+  __syncthreads();
+  // weights and the softmax denominator (fixed order: per thread, then lanes, then waves)
+  float dsum = 0.f;
+  for (int c = tid; c < nch; c += 1024) {
+    const float mc = wexp[c];
+    const float w = mc == -INFINITY ? 0.f : __expf(mc - m);
+    wexp[c] = w;
+    dsum += w * ph[(size_t)c * stride + 1];
+  }
+  dsum = wave_sum_dpp(dsum);
+  if (lane == 0) red[wv] = dsum;
+  __syncthreads();
+  float den = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) den += red[w];
+  // columns
+  const int quarter = tid >> 8;
+  for (int col0 = 0; col0 < hd; col0 += 256) {
+    const int col = col0 + (tid & 255);
+    float o = 0.f;
+    if (col < hd) {
+      int c = quarter;
+      for (; c + 28 < nch; c += 32) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = ph[(size_t)(c + 4 * u) * stride + kPartHead + col];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o += wexp[c + 4 * u] * x[u];
+      }
+      for (; c < nch; c += 4) o += wexp[c] * ph[(size_t)c * stride + kPartHead + col];
+    }
+    opart[quarter][tid & 255] = o;
+    __syncthreads();
+    if (tid < 256 && col < hd) {
+      const float oo = ((opart[0][tid] + opart[1][tid]) + opart[2][tid]) + opart[3][tid];
+      out[(size_t)h * hd + col] = den > 0.f ? oo / den : 0.f;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (counts) counts[h] = tot;
+    if (theta_out) theta_out[h] = ph[3];
+  }
+  if (idx_out) {  // the ascending list
+    // chunk offsets: exclusive prefix of the counts over contiguous segments
+    // of chunks (thread-serial), then over threads (block scan)
+    const int seg = (nch + 1023) / 1024, a0 = min(tid * seg, nch), a1 = min(a0 + seg, nch);
+    int mine = 0;
+    for (int c = a0; c < a1; ++c) mine += ccnt[c];
+    const int incl = wave_incl_scan_dpp(mine);
+    if (lane == 63) ired[wv] = incl;
+    __syncthreads();
+    int run = incl - mine;
+    for (int w = 0; w < wv; ++w) run += ired[w];
+    for (int c = a0; c < a1; ++c) {
+      const int k = ccnt[c];
+      ccnt[c] = run;
+      run += k;
+    }
+    __syncthreads();
+    // position p comes from the last chunk whose offset is <= p (binary search)
+    const int np = (int)min((int64_t)tot, cap);
+    for (int p = tid; p < np; p += 1024) {
+      int lo = 0, hi = nch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ccnt[mid] <= p) lo = mid; else hi = mid - 1;
+      }
+      idx_out[(size_t)h * cap + p] = lidx[(size_t)h * n_ctx + lo * kChunk + (p - ccnt[lo])];
+    }
+    for (int64_t e = tot + tid; e < cap; e += 1024) idx_out[(size_t)h * cap + e] = -1;
+  }
 }
 
 // ---------------------------------------------------------------- host side
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workspace: scores [Hq][n_ctx], chunk statistics [Hq][nch] (mean, M2), chunk
+// partials [Hq][nch][4 + hd], chunk-local lists [Hq][n_ctx].
+struct AttnLayout {
+  size_t scores, cstat, part, lidx, total;
+};
+static AttnLayout attn_layout(int64_t Hq, int64_t n_ctx, int64_t hd) {
+  const int64_t nch = (n_ctx + kChunk - 1) / kChunk;
+  AttnLayout L;
+  size_t off = 0;
+  L.scores = off;
+  off += round_up((size_t)Hq * n_ctx * 4, 256);
+  L.cstat = off;
+  off += round_up((size_t)Hq * nch * 8, 256);
+  L.part = off;
+  off += round_up((size_t)Hq * nch * (kPartHead + hd) * 4, 256);
+  L.lidx = off;
+  off += round_up((size_t)Hq * n_ctx * 4, 256);
+  L.total = off;
+  return L;
+}
+
 size_t attn_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn) {
-  (void)Hkv, (void)hd, (void)r, (void)k_attn;
-  return 3 * round_up((size_t)Hq * n_ctx * 4, 256);
+  (void)Hkv, (void)r, (void)k_attn;
+  return attn_layout(Hq, n_ctx, hd).total;
 }
 
 hipError_t launch_attn_decode(const void* q, const void* k1, const void* k2, const void* v, int64_t Hq, int64_t Hkv,
                               int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn, double z, float* out,
                               int32_t* counts, int32_t* idx, int64_t cap, float* theta, void* ws, hipStream_t st) {
+  const AttnLayout L = attn_layout(Hq, n_ctx, hd);
   char* base = (char*)ws;
-  const size_t plane = round_up((size_t)Hq * n_ctx * 4, 256);
-  float* scores = (float*)base;
-  int32_t* lidx = (int32_t*)(base + plane);
-  float* lval = (float*)(base + 2 * plane);
-  const int nsplit = (int)((n_ctx + kScoreTokens - 1) / kScoreTokens);
-  hipLaunchKernelGGL(attn_scores, dim3((unsigned)(Hkv * nsplit)), dim3(256), 0, st, (const bf16_t*)q,
-                     (const bf16_t*)k1, (int)Hq, (int)Hkv, (int)n_ctx, (int)hd, (int)r, scores);
+  float* scores = (float*)(base + L.scores);
+  float2* cstat = (float2*)(base + L.cstat);
+  float* part = (float*)(base + L.part);
+  int32_t* lidx = idx ? (int32_t*)(base + L.lidx) : nullptr;
+  const int nch = (int)((n_ctx + kChunk - 1) / kChunk);
+  hipLaunchKernelGGL(attn_scores, dim3((unsigned)(Hkv * nch)), dim3(256), 0, st, (const bf16_t*)q,
+                     (const bf16_t*)k1, (int)Hq, (int)Hkv, (int)n_ctx, (int)hd, (int)r, scores, cstat);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int dense = n_ctx <= k_attn ? 1 : 0;
-  hipLaunchKernelGGL(attn_select_gather, dim3((unsigned)Hq), dim3(1024), 0, st, (const bf16_t*)q, (const bf16_t*)k2,
-                     (const bf16_t*)v, (int)Hq, (int)Hkv, (int)n_ctx, (int)hd, (int)r, dense, (float)z, scores, lidx,
-                     lval, out, counts, idx, cap, theta);
+  hipLaunchKernelGGL(attn_chunk, dim3((unsigned)(Hq * nch)), dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)k2,
+                     (const bf16_t*)v, (int)Hq, (int)Hkv, (int)n_ctx, (int)hd, (int)r, dense, (float)z, scores,
+                     cstat, part, lidx);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_merge, dim3((unsigned)Hq), dim3(1024), 0, st, (int)n_ctx, (int)hd, part, lidx, out, counts,
+                     idx, cap, theta);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ sample of tokens on the host's cores.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -151,7 +152,15 @@ def extra_workloads(torch, sf, synth, dev, seed):
         qb, k1b, k2b, vb = synth.attn_inputs(seed, 8, 4, n, 256, 128)
         args = [bf(a) for a in (qb, k1b, k2b, vb)]
         out, cnt, _, _ = sf.spark_attn_decode(*args, 256)
-        ms = _time_ms(torch, lambda: sf.spark_attn_decode(*args, 256), reps=50)
+        # the operator alone through the C ABI: outputs preallocated, no list
+        need = ctypes.c_size_t(0)
+        L.spark_attn_workspace_size(8, 4, n, 256, 128, 256, ctypes.byref(need))
+        ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+        o2 = torch.empty((8, 256), device=dev)
+        c2 = torch.empty(8, dtype=torch.int32, device=dev)
+        call = lambda: L.spark_attn_decode(*[sf._p(a) for a in args], 8, 4, n, 256, 128, 256, sf._p(o2), sf._p(c2),
+                                           None, 0, None, sf._p(ws), need.value, sf._stream(dev))
+        ms = _time_ms(torch, call, reps=50)
         c = cnt.double().sum().item()
         moved = 4 * n * 128 * 2 + c * (128 + 256) * 2 + 8 * 256 * 2
         att[str(n)] = {"us": ms * 1e3, "GB_s": moved / ms / 1e6, "mean_attended": c / 8,
