@@ -99,9 +99,28 @@ def _time_ms(torch, fn, reps=20, warm=3):
     return float(np.median(ts))
 
 
-def extra_workloads(torch, sf, synth, dev, seed):
-    """The other workloads of the hot path, each timed on its own."""
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def _oracle_rate(fn, n_units: int, unit: str, sample: str) -> dict:
+    """Time fn() (one call of the fp64 oracle over a bounded sample of n_units)."""
+    import oracle
+
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    return {"value": n_units / dt, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{sample}, {dt:.1f} s"}
+
+
+def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
+    """The other workloads of the hot path, each timed on its own, with its
+    roofline and (with_cpu) the oracle timed on a bounded sample."""
     res = {}
+    if with_cpu:
+        import oracle
+
+        oracle.build()
     # standalone statistical top-k: 65536 rows x 9216, k 737, Gaussian rows
     # x = mu + s * e with mu ~ U(-1,1), s ~ U(0.5,2) (generated on the GPU)
     g = torch.Generator(device=dev).manual_seed(seed)
@@ -120,8 +139,14 @@ def extra_workloads(torch, sf, synth, dev, seed):
     ms = _time_ms(torch, st)
     nsel = float(counts.double().sum().item())
     moved = rows * d * 4 + nsel * 8 + rows * 8
-    res["stat_topk"] = {"workload": "65536 x 9216 fp32 rows, k 737", "ms": ms, "GB_s": moved / ms / 1e6,
-                        "frac_of_8TBs": moved / ms / 1e6 / HBM_PEAK_GBS, "mean_count": nsel / rows}
+    res["stat_topk"] = {"workload": "65536 x 9216 fp32 rows, k 737", "ms": ms, "rows_per_s": rows / ms * 1e3,
+                        "mean_count": nsel / rows,
+                        "roofline": {"bound": "hbm", "achieved": moved / ms / 1e6, "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": moved / ms / 1e6 / HBM_PEAK_GBS}}
+    if with_cpu:
+        xs = synth.stat_rows(seed, 2000, d)
+        res["stat_topk"]["cpu_baseline"] = _oracle_rate(lambda: oracle.stat_topk(xs, k, cap), 2000, "rows/s",
+                                                        "2000 rows of 9216 (same recipe, host-generated)")
     del x, vals, idx
     torch.cuda.empty_cache()
     # prefill: 4096 tokens through one 2304 x 9216 layer, bf16
@@ -140,10 +165,17 @@ def extra_workloads(torch, sf, synth, dev, seed):
     # contribute exact zeros): scores, gated K2 values, and C V
     dense = 2.0 * T * D_FF * (R + (D_MODEL - R) + D_MODEL)
     res["prefill"] = {"workload": "4096 tokens, one 2304 x 9216 layer (r 1152, k 737), bf16", "ms": ms,
-                      "us_per_token": ms * 1e3 / T, "predictor_gflop": flops / 1e9,
-                      "dense_products_gflop": dense / 1e9, "dense_products_tflops": dense / ms / 1e9,
+                      "tokens_per_s": T / ms * 1e3, "us_per_token": ms * 1e3 / T, "predictor_gflop": flops / 1e9,
+                      "dense_products_gflop": dense / 1e9,
+                      "roofline": {"bound": "mfma", "achieved": dense / ms / 1e9, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": dense / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+                                   "note": "all three products (scores, gated K2, C V) over the whole call"},
                       "hipblaslt_predictor_gemm_ms": ref_ms,
                       "hipblaslt_predictor_tflops": flops / ref_ms / 1e9}
+    if with_cpu:
+        Qs = synth.queries(seed, 64, D_MODEL, "bf16")
+        res["prefill"]["cpu_baseline"] = _oracle_rate(lambda: oracle.spark_ffn(Qs, *lw, R, K), 64, "tokens/s",
+                                                      "64 tokens of the same layer")
     del Q, layer
     torch.cuda.empty_cache()
     # attention decode: 8 query heads / 4 KV heads, hd 256, r 128, k_attn 256
@@ -163,8 +195,12 @@ def extra_workloads(torch, sf, synth, dev, seed):
         ms = _time_ms(torch, call, reps=50)
         c = cnt.double().sum().item()
         moved = 4 * n * 128 * 2 + c * (128 + 256) * 2 + 8 * 256 * 2
-        att[str(n)] = {"us": ms * 1e3, "GB_s": moved / ms / 1e6, "mean_attended": c / 8,
-                       "algorithmic_bytes": moved}
+        att[str(n)] = {"us": ms * 1e3, "mean_attended": c / 8, "algorithmic_bytes": moved,
+                       "roofline": {"bound": "hbm", "achieved": moved / ms / 1e6, "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": moved / ms / 1e6 / HBM_PEAK_GBS}}
+        if with_cpu:
+            att[str(n)]["cpu_baseline"] = _oracle_rate(lambda: oracle.spark_attn_decode(qb, k1b, k2b, vb, 256), 1,
+                                                       "steps/s", f"one decode step at n_ctx {n}")
     res["attention_decode"] = att
     return res
 
@@ -273,7 +309,7 @@ def main():
     if not args.no_extra:
         del layers, qs
         torch.cuda.empty_cache()
-        out["extra"] = extra_workloads(torch, sf, synth, dev, args.seed)
+        out["extra"] = extra_workloads(torch, sf, synth, dev, args.seed, not args.no_cpu)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layers_np)
     print(json.dumps(out), flush=True)
