@@ -65,6 +65,8 @@ class _Lib:
         lib.oracle_spark_attn_decode.restype = ci
         lib.oracle_spark_attn_decode.argtypes = [ci, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, vp,
                                                  vp]
+        lib.oracle_spark_attn_prefill.restype = ci
+        lib.oracle_spark_attn_prefill.argtypes = [ci, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, vp]
         self.c = lib
 
 
@@ -249,3 +251,25 @@ def spark_attn_decode(q: np.ndarray, k1: np.ndarray, k2: np.ndarray, v: np.ndarr
     if rc != 0:
         raise ValueError("oracle_spark_attn_decode: bad arguments")
     return dict(out=out, counts=counts, theta=theta, scores=scores)
+
+
+def spark_attn_prefill(q: np.ndarray, k1: np.ndarray, k2: np.ndarray, v: np.ndarray, k_attn: int) -> dict:
+    """Spark attention over a whole prompt, causal: the query of position t
+    attends over positions 0..t with its own statistical top-k.  q [T][Hq][hd];
+    k1 [Hkv][T][r]; k2 [Hkv][T][hd-r]; v [Hkv][T][hd]; one dtype for all.
+    Returns out [T][Hq][hd] fp64, counts [T][Hq], theta [T][Hq] (NaN where
+    t + 1 <= k_attn)."""
+    q, k1, k2, v = _c(q), _c(k1), _c(k2), _c(v)
+    dt = _dtype_code(q)
+    assert all(_dtype_code(a) == dt for a in (k1, k2, v))
+    T, Hq, hd = q.shape
+    Hkv, n, r = k1.shape
+    assert n == T and k2.shape == (Hkv, T, hd - r) and v.shape == (Hkv, T, hd)
+    out = np.zeros((T, Hq, hd), np.float64)
+    counts = np.zeros((T, Hq), np.int32)
+    theta = np.zeros((T, Hq), np.float64)
+    rc = _load().oracle_spark_attn_prefill(dt, _ptr(q), _ptr(k1), _ptr(k2), _ptr(v), T, Hq, Hkv, hd, r,
+                                           int(k_attn), _ptr(out), _ptr(counts), _ptr(theta))
+    if rc != 0:
+        raise ValueError("oracle_spark_attn_prefill: bad arguments")
+    return dict(out=out, counts=counts, theta=theta)

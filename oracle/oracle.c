@@ -1,6 +1,6 @@
 /*
  * oracle.c -- plain, slow, fp64 CPU oracle for the Spark FFN layer, the
- * statistical top-k operator and Spark attention decode.
+ * statistical top-k operator and Spark attention (decode and causal prefill).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file: only the tests, the smoke check and the bench's CPU
@@ -30,7 +30,8 @@
  *   GELU; V is stored [d_ff][d_model] and its rows are neurons; attention
  *   uses no 1/sqrt(hd) factor, softmax runs over the selected set only,
  *   query head h reads KV head h / (Hq/Hkv), and when n_ctx <= k_attn all
- *   tokens are attended.  An empty selected set gives a zero output.
+ *   tokens are attended; in a causal prefill the query of position t
+ *   attends over positions 0..t with its own threshold.  An empty selected set gives a zero output.
  *
  * Arithmetic: every stored input (fp32, or bf16 widened exactly) is read as
  * is and all arithmetic is IEEE fp64 in plain loops, summing in ascending
@@ -341,6 +342,65 @@ int oracle_decode_stack(int64_t d_model, int64_t d_ff, int64_t r, int64_t k, int
 }
 
 /*
+ * Spark attention for one query over the first n tokens of one KV head's
+ * cache (rows j < n of a cache with N rows per head), the "Spark Attention"
+ * item of the notes' key-design section: predictor scores s_j = q[:r].k1_j,
+ * statistical top-k of s with k_attn (every token when n <= k_attn), softmax
+ * of s over the selected set, softplus of q[r:].k2_j, and the weighted sum of
+ * the v rows.  qi is the index of the query's first element in q.
+ */
+static void attn_query(int dtype, const void *q, int64_t qi, const void *k1, const void *k2, const void *v,
+                       int64_t g, int64_t N, int64_t n, int64_t hd, int64_t r, int64_t k_attn, double *o,
+                       int32_t *count, double *theta, double *scores)
+{
+    const int64_t rc = hd - r;
+    const int dense = n <= k_attn;
+    const double z = dense ? 0.0 : oracle_threshold_z(k_attn, n);
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+    for (int64_t j = 0; j < n; ++j) {
+        double a = 0.0;
+        for (int64_t c = 0; c < r; ++c)
+            a += ld(q, dtype, qi + c) * ld(k1, dtype, (g * N + j) * r + c);
+        s[j] = a;
+    }
+    if (scores) memcpy(scores, s, sizeof(double) * (size_t)n);
+    int64_t m;
+    double th = NAN;
+    if (dense) {
+        for (int64_t j = 0; j < n; ++j)
+            S[j] = (int32_t)j;
+        m = n;
+    } else {
+        m = stat_topk_row(s, n, z, NULL, NULL, &th, S, NULL, n);
+    }
+    for (int64_t c = 0; c < hd; ++c)
+        o[c] = 0.0;
+    if (m > 0) {
+        double smax = -INFINITY;
+        for (int64_t t = 0; t < m; ++t)
+            if (s[S[t]] > smax) smax = s[S[t]];
+        double den = 0.0;
+        for (int64_t t = 0; t < m; ++t)
+            den += exp(s[S[t]] - smax);
+        for (int64_t t = 0; t < m; ++t) {
+            const int64_t j = S[t];
+            double w = exp(s[j] - smax) / den;
+            double a = 0.0;
+            for (int64_t c = 0; c < rc; ++c)
+                a += ld(q, dtype, qi + r + c) * ld(k2, dtype, (g * N + j) * rc + c);
+            double wu = w * oracle_softplus(a);
+            for (int64_t c = 0; c < hd; ++c)
+                o[c] += wu * ld(v, dtype, (g * N + j) * hd + c);
+        }
+    }
+    if (count) *count = (int32_t)m;
+    if (theta) *theta = th;
+    free(s);
+    free(S);
+}
+
+/*
  * Spark attention, one decode step (notes, "Spark Attention" item).
  * q [Hq][hd]; k1 [Hkv][n_ctx][r] (predictor key dims); k2 [Hkv][n_ctx][hd-r]
  * (compute key dims); v [Hkv][n_ctx][hd]; all of dtype `dtype`.  Query head h
@@ -358,55 +418,35 @@ int oracle_spark_attn_decode(int dtype, const void *q, const void *k1, const voi
     if (!q || !k1 || !k2 || !v || !out || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || n_ctx <= 0 || hd <= 0 ||
         r <= 0 || r >= hd || k_attn <= 0)
         return -1;
-    const int64_t group = Hq / Hkv, rc = hd - r;
-    const int dense = n_ctx <= k_attn;
-    const double z = dense ? 0.0 : oracle_threshold_z(k_attn, n_ctx);
+    const int64_t group = Hq / Hkv;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t h = 0; h < Hq; ++h) {
-        const int64_t g = h / group;
-        double *s = (double *)malloc(sizeof(double) * (size_t)n_ctx);
-        int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)n_ctx);
-        for (int64_t j = 0; j < n_ctx; ++j) {
-            double a = 0.0;
-            for (int64_t c = 0; c < r; ++c)
-                a += ld(q, dtype, h * hd + c) * ld(k1, dtype, (g * n_ctx + j) * r + c);
-            s[j] = a;
-        }
-        if (scores) memcpy(scores + h * n_ctx, s, sizeof(double) * (size_t)n_ctx);
-        int64_t n;
-        double th = NAN;
-        if (dense) {
-            for (int64_t j = 0; j < n_ctx; ++j)
-                S[j] = (int32_t)j;
-            n = n_ctx;
-        } else {
-            n = stat_topk_row(s, n_ctx, z, NULL, NULL, &th, S, NULL, n_ctx);
-        }
-        double *o = out + h * hd;
-        for (int64_t c = 0; c < hd; ++c)
-            o[c] = 0.0;
-        if (n > 0) {
-            double smax = -INFINITY;
-            for (int64_t t = 0; t < n; ++t)
-                if (s[S[t]] > smax) smax = s[S[t]];
-            double den = 0.0;
-            for (int64_t t = 0; t < n; ++t)
-                den += exp(s[S[t]] - smax);
-            for (int64_t t = 0; t < n; ++t) {
-                const int64_t j = S[t];
-                double w = exp(s[j] - smax) / den;
-                double a = 0.0;
-                for (int64_t c = 0; c < rc; ++c)
-                    a += ld(q, dtype, h * hd + r + c) * ld(k2, dtype, (g * n_ctx + j) * rc + c);
-                double wu = w * oracle_softplus(a);
-                for (int64_t c = 0; c < hd; ++c)
-                    o[c] += wu * ld(v, dtype, (g * n_ctx + j) * hd + c);
-            }
-        }
-        if (counts) counts[h] = (int32_t)n;
-        if (theta) theta[h] = th;
-        free(s);
-        free(S);
+    for (int64_t h = 0; h < Hq; ++h)
+        attn_query(dtype, q, h * hd, k1, k2, v, h / group, n_ctx, n_ctx, hd, r, k_attn, out + h * hd,
+                   counts ? counts + h : NULL, theta ? theta + h : NULL, scores ? scores + h * n_ctx : NULL);
+    return 0;
+}
+
+/*
+ * Spark attention over a whole prompt (causal prefill): the query of
+ * position t attends over positions 0..t of the same cache, each query with
+ * its own statistical top-k over its t + 1 scores ("Spark Attention" item;
+ * the prefix reading is the causal form of the same operator).
+ *   q [T][Hq][hd]; k1 [Hkv][T][r]; k2 [Hkv][T][hd-r]; v [Hkv][T][hd];
+ *   out [T][Hq][hd]; counts, theta [T][Hq] (theta NaN when t + 1 <= k_attn).
+ */
+int oracle_spark_attn_prefill(int dtype, const void *q, const void *k1, const void *k2, const void *v, int64_t T,
+                              int64_t Hq, int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, double *out,
+                              int32_t *counts, double *theta)
+{
+    if (!q || !k1 || !k2 || !v || !out || T <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || hd <= 0 || r <= 0 ||
+        r >= hd || k_attn <= 0)
+        return -1;
+    const int64_t group = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t th = 0; th < T * Hq; ++th) {
+        const int64_t t = th / Hq, h = th % Hq;
+        attn_query(dtype, q, th * hd, k1, k2, v, h / group, T, t + 1, hd, r, k_attn, out + th * hd,
+                   counts ? counts + th : NULL, theta ? theta + th : NULL, NULL);
     }
     return 0;
 }

@@ -98,3 +98,15 @@ def attn_inputs(seed: int, Hq: int, Hkv: int, n_ctx: int, hd: int, r: int, scale
     v = _normal(rng(seed, 2, ATTN_ID), (Hkv, n_ctx, hd), sc)
     b = f32_to_bf16_bits
     return b(q), b(np.ascontiguousarray(k[:, :, :r])), b(np.ascontiguousarray(k[:, :, r:])), b(v)
+
+
+def attn_prefill_inputs(seed: int, T: int, Hq: int, Hkv: int, hd: int, r: int, scale: float | None = None):
+    """Spark attention prefill inputs, bf16 bits: queries q [T][Hq][hd] and the
+    split cache of the same T positions k1 [Hkv][T][r], k2 [Hkv][T][hd-r],
+    v [Hkv][T][hd], all ~ N(0,1)*scale with scale = 1/sqrt(hd) by default."""
+    sc = (1.0 / np.sqrt(hd)) if scale is None else scale
+    q = _normal(rng(seed, 3, ATTN_ID), (T, Hq, hd), sc)
+    k = _normal(rng(seed, 4, ATTN_ID), (Hkv, T, hd), sc)
+    v = _normal(rng(seed, 5, ATTN_ID), (Hkv, T, hd), sc)
+    b = f32_to_bf16_bits
+    return b(q), b(np.ascontiguousarray(k[:, :, :r])), b(np.ascontiguousarray(k[:, :, r:])), b(v)

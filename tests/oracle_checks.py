@@ -284,6 +284,30 @@ def check_attention():
     assert np.all(z["counts"] == 0) and np.all(z["out"] == 0)
 
 
+# ---------------------------------------------------------------- P15 causal attention prefill
+def check_attention_prefill():
+    """Each position against the masked-softmax reference on its own prefix
+    (dense rows while t + 1 <= k_attn, statistical top-k after), and causality:
+    keys and values after position t never change its output."""
+    w = synth.bf16_bits_to_f32
+    for (T, Hq, Hkv, hd, r, ka) in [(40, 4, 2, 32, 16, 8), (24, 2, 1, 16, 8, 64)]:
+        qb, k1b, k2b, vb = synth.attn_prefill_inputs(41, T, Hq, Hkv, hd, r, scale=0.5)
+        res = oracle.spark_attn_prefill(qb, k1b, k2b, vb, ka)
+        q64, k164, k264, v64 = (w(a).astype(np.float64) for a in (qb, k1b, k2b, vb))
+        for t in range(T):
+            ref, cnt = _attn_ref(q64[t], k164[:, :t + 1], k264[:, :t + 1], v64[:, :t + 1], ka)
+            assert np.array_equal(res["counts"][t], cnt), (t, res["counts"][t], cnt)
+            assert rel(res["out"][t], ref) < 1e-12, (t, rel(res["out"][t], ref))
+            assert np.all(np.isnan(res["theta"][t])) == (t + 1 <= ka)
+        t0 = T // 2
+        k1c, k2c, vc = k1b.copy(), k2b.copy(), vb.copy()
+        k1c[:, t0:] = k1c[:, t0:][:, ::-1]
+        k2c[:, t0:] = 0
+        vc[:, t0:] = vc[:, t0:][:, ::-1]
+        b = oracle.spark_attn_prefill(qb, k1c, k2c, vc, ka)
+        assert np.array_equal(res["out"][:t0], b["out"][:t0]) and not np.allclose(res["out"][t0:], b["out"][t0:])
+
+
 # ---------------------------------------------------------------- P13 continuity at theta
 def check_continuity():
     dm, dff, r, k = 16, 64, 8, 6
@@ -322,5 +346,5 @@ def check_decode_chain():
 
 ALL_CHECKS = [check_quantile, check_threshold_closed_form, check_special_rows, check_quantile_grid,
               check_invariants, check_scale_invariance, check_theorem31, check_student_t, check_ffn_dense_masked,
-              check_ffn_bf16_widening, check_topk_is_largest, check_activations, check_attention, check_continuity,
-              check_decode_chain]
+              check_ffn_bf16_widening, check_topk_is_largest, check_activations, check_attention,
+              check_attention_prefill, check_continuity, check_decode_chain]

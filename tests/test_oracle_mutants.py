@@ -24,11 +24,13 @@ MUTANTS = [
     ("quantile_coef", "4.5921953931549871457e4", "4.5921953931549871457e3"),
     ("quantile_tail_coef", "7.74545014278341407640e-4", "7.74545014278341407640e-3"),
     ("rms_sum_not_mean", "double inv = 1.0 / sqrt(ss / (double)d_model + eps);", "double inv = 1.0 / sqrt(ss + eps);"),
-    ("gqa_modulo", "const int64_t g = h / group;", "const int64_t g = h % Hkv;"),
+    ("gqa_modulo", "attn_query(dtype, q, h * hd, k1, k2, v, h / group,", "attn_query(dtype, q, h * hd, k1, k2, v, h % Hkv,"),
     ("softmax_unnormalised", "double w = exp(s[j] - smax) / den;", "double w = exp(s[j] - smax);"),
     ("softplus_as_relu", "return (v > 0.0 ? v : 0.0) + log1p(exp(-fabs(v)));", "return (v > 0.0 ? v : 0.0);"),
-    ("attn_compute_half_offset", "a += ld(q, dtype, h * hd + r + c) * ld(k2, dtype, (g * n_ctx + j) * rc + c);",
-     "a += ld(q, dtype, h * hd + c) * ld(k2, dtype, (g * n_ctx + j) * rc + c);"),
+    ("attn_compute_half_offset", "a += ld(q, dtype, qi + r + c) * ld(k2, dtype, (g * N + j) * rc + c);",
+     "a += ld(q, dtype, qi + c) * ld(k2, dtype, (g * N + j) * rc + c);"),
+    ("attn_prefix_short", "h / group, T, t + 1, hd, r, k_attn,", "h / group, T, t, hd, r, k_attn,"),
+    ("attn_prefix_stride", "h / group, T, t + 1, hd, r, k_attn,", "h / group, t + 1, t + 1, hd, r, k_attn,"),
     ("bf16_widen_shift", "uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16;",
      "uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 15;"),
     ("mean_off_by_one", "double mean = s / (double)d;", "double mean = s / (double)(d + 1);"),
@@ -37,7 +39,7 @@ MUTANTS = [
 # faster, smaller versions of the slow checks are enough to catch the mutants
 FAST = [oc.check_quantile, oc.check_threshold_closed_form, oc.check_special_rows, oc.check_quantile_grid,
         oc.check_invariants, oc.check_ffn_dense_masked, oc.check_ffn_bf16_widening, oc.check_activations,
-        oc.check_attention, oc.check_continuity, oc.check_decode_chain]
+        oc.check_attention, oc.check_attention_prefill, oc.check_continuity, oc.check_decode_chain]
 
 
 def _caught(path):
