@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   spark_ffn_decode(q, layers, k, r, eps, ...)       -> y  (and a trace dict)
   spark_ffn_prefill(Q, layer, k, r, ...)            -> Y  (and a trace dict)
   spark_attn_decode(q, k1, k2, v, k_attn, cap=None) -> (out, counts, idx, theta)
+  spark_attn_prefill(q, k1, k2, v, k_attn)          -> (out, counts, theta)
 """
 from __future__ import annotations
 
@@ -77,6 +78,12 @@ def lib() -> ctypes.CDLL:
                 L.spark_ffn_prefill_workspace_size.argtypes = [ctypes.POINTER(ShapeC), _i64, ctypes.POINTER(_sz)]
                 L.spark_attn_workspace_size.restype = _ci
                 L.spark_attn_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_sz)]
+                L.spark_attn_prefill.restype = _ci
+                L.spark_attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
+                                                 _vp, _vp, _sz, _vp]
+                L.spark_attn_prefill_workspace_size.restype = _ci
+                L.spark_attn_prefill_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64,
+                                                                ctypes.POINTER(_sz)]
                 _lib = L
     return _lib
 
@@ -276,3 +283,29 @@ def spark_attn_decode(q: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor, v: to
                                  _p(idx), cap, _p(theta), _p(ws), ws.numel(), _stream(dev))
     _check(st, "spark_attn_decode")
     return out, counts, idx, theta
+
+
+def spark_attn_prefill(q: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor, v: torch.Tensor, k_attn: int):
+    """Causal Spark attention over a prompt.  q [T][Hq][hd] bf16; k1 [Hkv][T][r],
+    k2 [Hkv][T][hd-r], v [Hkv][T][hd] bf16.  Returns out [T][Hq][hd] fp32,
+    counts [T][Hq] and theta [T][Hq] (NaN where t + 1 <= k_attn)."""
+    _need_cuda(q, k1, k2, v)
+    for t in (q, k1, k2, v):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("attention inputs must be bf16")
+    T, Hq, hd = q.shape
+    Hkv, n, r = k1.shape
+    if n != T:
+        raise ValueError("the cache must hold the T prompt positions")
+    need = ctypes.c_size_t(0)
+    _check(lib().spark_attn_prefill_workspace_size(T, Hq, Hkv, hd, r, int(k_attn), ctypes.byref(need)),
+           "spark_attn_prefill_workspace_size")
+    dev = q.device
+    ws = _cached_workspace("attn_prefill", dev, need.value)
+    out = torch.empty((T, Hq, hd), dtype=torch.float32, device=dev)
+    counts = torch.empty((T, Hq), dtype=torch.int32, device=dev)
+    theta = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    st = lib().spark_attn_prefill(_p(q), _p(k1), _p(k2), _p(v), T, Hq, Hkv, hd, r, int(k_attn), _p(out), _p(counts),
+                                  _p(theta), _p(ws), ws.numel(), _stream(dev))
+    _check(st, "spark_attn_prefill")
+    return out, counts, theta

@@ -174,4 +174,28 @@ int spark_attn_decode(const void* q, const void* k1, const void* k2, const void*
                                               idx ? cap : 0, theta, ws, stream));
 }
 
+int spark_attn_prefill_workspace_size(int64_t T, int64_t Hq, int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn,
+                                      size_t* bytes) {
+  if (!bytes) return SPARK_EINVAL;
+  if (T <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || hd <= 0 || r <= 0 || r >= hd || k_attn <= 0)
+    return SPARK_EINVAL;
+  if (r % 8 != 0 || (hd - r) % 8 != 0) return SPARK_EINVAL;
+  if (hd > 512 || T > 16384 || Hq > 1024) return SPARK_EUNSUPPORTED;
+  *bytes = spark::attn_prefill_workspace_bytes(T, Hq, Hkv, hd);
+  return SPARK_OK;
+}
+
+int spark_attn_prefill(const void* q, const void* k1, const void* k2, const void* v, int64_t T, int64_t Hq,
+                       int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float* out, int32_t* counts, float* theta,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  size_t need = 0;
+  int st = spark_attn_prefill_workspace_size(T, Hq, Hkv, hd, r, k_attn, &need);
+  if (st != SPARK_OK) return st;
+  if (!q || !k1 || !k2 || !v || !out) return SPARK_EINVAL;
+  if (!aligned(q, 16) || !aligned(k1, 16) || !aligned(k2, 16) || !aligned(v, 16)) return SPARK_EINVAL;
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return SPARK_EWORKSPACE;
+  return hip_status(spark::launch_attn_prefill(q, k1, k2, v, T, Hq, Hkv, hd, r, k_attn, out, counts, theta, ws,
+                                               stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,273 @@
+// Dense bf16 GEMM on the matrix cores for the prefill paths, with the
+// epilogues that apply the Spark gates.  Included by ffn_prefill.hip and
+// attn_prefill.hip.
+#pragma once
+#include "common.hpp"
+
+namespace spark {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int GBK = 64;       // K per LDS stage
+constexpr int GLD = GBK + 8;  // LDS row length in bf16 (16-byte pad against bank conflicts)
+
+enum { kEpiStore = 0, kEpiGate = 1, kEpiAttn = 2 };
+enum { kCausalNone = 0, kCausalTiles = 1, kCausalK = 2 };
+
+// Arguments of one (batched) product D = A * B^T.  Batch z = blockIdx.z uses
+// A + z*sA, B + (z / bgroup)*sB, C + z*sC, H + z*sH and the row arrays + z*sR.
+struct GemmArgs {
+  const bf16_t* A;
+  const bf16_t* B;
+  void* C;
+  int lda, ldb, ldc, M, N, K, ksplit, bgroup;
+  int64_t sA, sB, sC;
+  const float* H;  // fp32 scores read by the gate epilogues (row stride ldh)
+  int ldh;
+  int64_t sH;
+  const float* r0;  // per-row arrays of the epilogues (see gemm_bf16_nt)
+  const float* r1;
+  const float* r2;
+  int64_t sR;
+  int causal;
+};
+
+// D = A[M][K] (bf16, row stride lda) * B^T where B is stored [N][K] (bf16,
+// row stride ldb), with K a multiple of 8 and 16-byte aligned rows, over the
+// K range of split blockIdx.y (ksplit columns each, a multiple of 64).  Rows of
+// A and B past M and N are clamped on load and not stored; K past the end
+// reads as zeros.
+//
+// Workgroup tile (WM*MI*32) x (WN*NI*32): WM x WN waves, each holding MI x NI
+// accumulators of v_mfma_f32_32x32x16_bf16 (a 32*MI x 32*NI block).  A wave
+// reads MI + NI fragments from LDS per 16 of K for MI*NI MFMAs.  K in steps
+// of 64 through double-buffered LDS, staged through registers.
+//   kEpiStore: C[m][n] (fp32, row stride ldc) = D; with a K split, split s
+//              writes its partial to C + s * M * ldc.
+//   kEpiGate:  C[m][n] (bf16) = GELU(H - r0[m]) * D where H = H[m][n] > r0[m]
+//              (theta), else 0.
+//   kEpiAttn:  C[m][n] (bf16) = e^(H - r1[m]) / r2[m] * softplus(D) where
+//              n <= m and H > r0[m] (theta, -inf when every token is
+//              attended; r1 the largest selected score, r2 the sum of
+//              e^(s - r1) over the selected), else 0.
+// causal: kCausalTiles skips tiles wholly above the diagonal (n0 > m0 + BM - 1);
+// kCausalK stops K at the end of the tile's rows (A's columns past the
+// diagonal tile are never read).
+template <int EPI, int WM, int WN, int MI, int NI>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BM = WM * MI * 32, BN = WN * NI * 32;
+  constexpr int CA = BM * GBK / 8 / NT, CB = BN * GBK / 8 / NT;  // 16-byte chunks per thread per stage
+  static_assert(CA * NT * 8 == BM * GBK && CB * NT * 8 == BN * GBK, "tile must split evenly over threads");
+  __shared__ alignas(16) bf16_t As[2][BM * GLD];
+  __shared__ alignas(16) bf16_t Bs[2][BN * GLD];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int M = g.M, N = g.N;
+  const int MT = (M + BM - 1) / BM;
+  const int tm = blockIdx.x % MT, tn = blockIdx.x / MT;
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (g.causal == kCausalTiles && n0 > m0 + BM - 1) return;
+  const int wm = wv / WN, wn = wv % WN;
+  const int z = blockIdx.z;
+  const bf16_t* A = g.A + (size_t)z * g.sA;
+  const bf16_t* B = g.B + (size_t)(z / g.bgroup) * g.sB;
+  const int lda = g.lda, ldb = g.ldb;
+  const int kbeg = blockIdx.y * g.ksplit;
+  int kend = min(g.K, kbeg + g.ksplit);
+  if (g.causal == kCausalK) kend = min(kend, m0 + BM);
+
+  // Chunks past K are loaded from column 0 and replaced by zeros only when
+  // stored to LDS, after the MFMAs of the current stage, so the loads stay in
+  // flight across those MFMAs.
+  u32x4 ra[CA], rb[CB];
+  int kload = 0;
+  auto gload = [&](int k0) {
+    kload = k0;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + NT * i, row = c >> 3, kc = c & 7;
+      const int k = k0 + kc * 8;
+      ra[i] = load16(A + (size_t)min(m0 + row, M - 1) * lda + (k < kend ? k : 0));
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + NT * i, row = c >> 3, kc = c & 7;
+      const int k = k0 + kc * 8;
+      rb[i] = load16(B + (size_t)min(n0 + row, N - 1) * ldb + (k < kend ? k : 0));
+    }
+  };
+  auto sstore = [&](int buf) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + NT * i, row = c >> 3, kc = c & 7;
+      *reinterpret_cast<u32x4*>(&As[buf][row * GLD + kc * 8]) = kload + kc * 8 < kend ? ra[i] : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + NT * i, row = c >> 3, kc = c & 7;
+      *reinterpret_cast<u32x4*>(&Bs[buf][row * GLD + kc * 8]) = kload + kc * 8 < kend ? rb[i] : zero;
+    }
+  };
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int KT = kend > kbeg ? (kend - kbeg + GBK - 1) / GBK : 0;
+  if (KT > 0) {
+    gload(kbeg);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kbeg + (kt + 1) * GBK);
+#pragma unroll
+    for (int kk = 0; kk < GBK; kk += 16) {
+      const int ko = kk + (lane >> 5) * 8;  // lanes 0-31: k 0..7, lanes 32-63: k 8..15
+      bf16x8 a[MI], b[NI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * MI * 32 + i * 32 + (lane & 31)) * GLD + ko]);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn * NI * 32 + j * 32 + (lane & 31)) * GLD + ko]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  // D layout of the 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
+  const int ldc = g.ldc;
+  float* Cf = reinterpret_cast<float*>(g.C) + (size_t)z * g.sC + (size_t)blockIdx.y * M * ldc;
+  bf16_t* Cb = reinterpret_cast<bf16_t*>(g.C) + (size_t)z * g.sC;
+  const float* H = g.H + (size_t)z * g.sH;
+  const float* R0 = g.r0 + (size_t)z * g.sR;
+  const float* R1 = g.r1 + (size_t)z * g.sR;
+  const float* R2 = g.r2 + (size_t)z * g.sR;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    float p0[16], p1[16], p2[16];
+    if (EPI != kEpiStore) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = min(m0 + wm * MI * 32 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), M - 1);
+        p0[r] = R0[m];
+        if (EPI == kEpiAttn) {
+          p1[r] = R1[m];
+          p2[r] = R2[m];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int n = n0 + wn * NI * 32 + j * 32 + (lane & 31);
+      float hv[16];
+      if (EPI != kEpiStore) {  // all 16 score loads of the block before any use
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * MI * 32 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          hv[r] = H[(size_t)min(m, M - 1) * g.ldh + min(n, N - 1)];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * MI * 32 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m < M && n < N) {
+          if (EPI == kEpiStore) {
+            Cf[(size_t)m * ldc + n] = acc[i][j][r];
+          } else if (EPI == kEpiGate) {
+            const float c = hv[r] > p0[r] ? gelu_tanh(hv[r] - p0[r]) * acc[i][j][r] : 0.f;
+            Cb[(size_t)m * ldc + n] = f32_to_bf16(c);
+          } else {
+            const bool on = n <= m && hv[r] > p0[r];
+            const float c = on ? __expf(hv[r] - p1[r]) / p2[r] * softplus(acc[i][j][r]) : 0.f;
+            Cb[(size_t)m * ldc + n] = f32_to_bf16(c);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Y[m][n] = sum over s < S of P[s][m][n] (fixed order), fp32 [M][N] planes.
+static __global__ void sum_partials(const float* __restrict__ P, int S, int64_t plane, float* __restrict__ Y) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= plane) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(P + i);
+  for (int s = 1; s < S; ++s) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(P + (int64_t)s * plane + i);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *reinterpret_cast<f32x4*>(Y + i) = acc;
+}
+
+// Vt[n][k] = V[k][n] for a bf16 [K][N] matrix (Vt rows ldo apart), 64x64
+// tiles through LDS.
+static __global__ __launch_bounds__(256) void transpose_bf16(const bf16_t* __restrict__ V, int K, int N,
+                                                             bf16_t* __restrict__ Vt, int ldo) {
+  __shared__ bf16_t tile[64][66];
+  const int tiles_n = (N + 63) / 64;
+  const int tk = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int k0 = tk * 64, n0 = tn * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = tid + 256 * i, r = e >> 6, c = e & 63;
+    if (k0 + r < K && n0 + c < N) tile[r][c] = V[(size_t)(k0 + r) * N + n0 + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = tid + 256 * i, r = e >> 6, c = e & 63;  // r: n within tile, c: k within tile
+    if (n0 + r < N && k0 + c < K) Vt[(size_t)(n0 + r) * ldo + k0 + c] = tile[c][r];
+  }
+}
+
+// Tile configuration of the prefill products: 128 x 128 per workgroup, four
+// waves of 64 x 64.  (Two waves of 128 x 64, at one wave per SIMD, measured
+// slower: too little to hide the LDS and global latencies.)
+constexpr int kWM = 2, kWN = 2, kMI = 2, kNI = 2;
+constexpr int kBM = kWM * kMI * 32, kBN = kWN * kNI * 32;
+
+// Launch over batch `batch` (grid z) and `splits` K splits (grid y).
+template <int EPI>
+inline hipError_t launch_gemm(GemmArgs a, int splits, int batch, hipStream_t st) {
+  const int tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+  int ks = (a.K + splits - 1) / splits;
+  a.ksplit = (ks + GBK - 1) / GBK * GBK;
+  if (a.bgroup < 1) a.bgroup = 1;
+  hipLaunchKernelGGL((gemm_bf16_nt<EPI, kWM, kWN, kMI, kNI>), dim3(tiles, splits, batch), dim3(kWM * kWN * 64), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+// A GemmArgs with only the operands of a plain product set.
+inline GemmArgs gemm_args(const bf16_t* A, int lda, const bf16_t* B, int ldb, void* C, int ldc, int M, int N, int K) {
+  GemmArgs a{};
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.bgroup = 1;
+  a.causal = kCausalNone;
+  return a;
+}
+
+}  // namespace spark

@@ -202,6 +202,26 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
             att[str(n)]["cpu_baseline"] = _oracle_rate(lambda: oracle.spark_attn_decode(qb, k1b, k2b, vb, 256), 1,
                                                        "steps/s", f"one decode step at n_ctx {n}")
     res["attention_decode"] = att
+    # causal attention prefill over a 4096-position prompt, same heads
+    Tp = 4096
+    qp, k1p, k2p, vp = synth.attn_prefill_inputs(seed, Tp, 8, 4, 256, 128)
+    pargs = [bf(a) for a in (qp, k1p, k2p, vp)]
+    po, pc, _ = sf.spark_attn_prefill(*pargs, 256)
+    ms = _time_ms(torch, lambda: sf.spark_attn_prefill(*pargs, 256), reps=10)
+    flops = 2.0 * 8 * (Tp * (Tp + 1) / 2) * (128 + 128 + 256)  # causal S, gated K2 scores, W V
+    res["attention_prefill"] = {
+        "workload": "4096-position prompt, Hq 8, Hkv 4, hd 256, r 128, k_attn 256, causal", "ms": ms,
+        "positions_per_s": Tp / ms * 1e3, "mean_attended": float(pc.double().mean().item()),
+        "roofline": {"bound": "mfma", "achieved": flops / ms / 1e9, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+                     "note": "causal products S, gated K2 scores and W V over the whole call"}}
+    if with_cpu:
+        qs, k1s, k2s, vs = synth.attn_prefill_inputs(seed, 512, 8, 4, 256, 128)
+        res["attention_prefill"]["cpu_baseline"] = _oracle_rate(
+            lambda: oracle.spark_attn_prefill(qs, k1s, k2s, vs, 256), 512, "positions/s",
+            "a 512-position prompt with the same heads")
+    del pargs, po, pc
+    torch.cuda.empty_cache()
     return res
 
 

@@ -153,11 +153,32 @@ int spark_attn_decode(const void *q, const void *k1, const void *k2, const void 
                       int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn, float *out, int32_t *counts,
                       int32_t *idx, int64_t cap, float *theta, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Spark attention over a whole prompt, causal prefill ("Spark Attention"
+ * item, in causal form): the query of position t attends over positions
+ * 0..t of the same cache with its own statistical top-k over its t + 1
+ * predictor scores (every position while t + 1 <= k_attn), softmax over the
+ * selected set and softplus gates, as spark_attn_decode does for one query.
+ *   q [T][Hq][hd] bf16 (position-major); k1 [Hkv][T][r], k2 [Hkv][T][hd-r],
+ *   v [Hkv][T][hd] bf16; out [T][Hq][hd] fp32; counts [T][Hq] (may be NULL);
+ *   theta [T][Hq] (may be NULL; NaN where t + 1 <= k_attn).
+ * The scores and gated weights run as dense products on the matrix cores
+ * (unselected positions contribute exact zeros); the workspace holds
+ * Hq * T * T fp32 scores and bf16 weights.
+ * Requires Hq % Hkv == 0, hd <= 512 and a multiple of 8, 0 < r < hd with r and
+ * hd - r multiples of 8, 1 <= T <= 16384, k_attn >= 1.
+ */
+int spark_attn_prefill(const void *q, const void *k1, const void *k2, const void *v, int64_t T, int64_t Hq,
+                       int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float *out, int32_t *counts, float *theta,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace sizes (bytes) for the calls above with the same arguments. */
 int spark_ffn_decode_workspace_size(const spark_ffn_shape *s, int n_layers, int64_t T, size_t *bytes);
 int spark_ffn_prefill_workspace_size(const spark_ffn_shape *s, int64_t T, size_t *bytes);
 int spark_attn_workspace_size(int64_t Hq, int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn,
                               size_t *bytes);
+int spark_attn_prefill_workspace_size(int64_t T, int64_t Hq, int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn,
+                                      size_t *bytes);
 
 /* z = Q(1 - k/d), the standard-normal quantile the threshold uses (host fp64). */
 double spark_threshold_z(int64_t k, int64_t d);

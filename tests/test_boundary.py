@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["stat_topk", "spark_ffn_decode", "spark_ffn_prefill", "spark_attn_decode",
               "spark_ffn_decode_workspace_size", "spark_ffn_prefill_workspace_size", "spark_attn_workspace_size",
-              "spark_status_string", "spark_threshold_z"]:
+              "spark_attn_prefill", "spark_attn_prefill_workspace_size", "spark_status_string", "spark_threshold_z"]:
         assert n in names, n
 
 
@@ -126,3 +126,19 @@ def test_prefill_and_attention_reject_bad_arguments():
     assert st == sf.SPARK_EINVAL
     st = L.spark_attn_decode(vp, vp, vp, vp, 8, 4, 100, 256, 128, 256, vp, None, None, 0, None, None, 0, None)
     assert st == sf.SPARK_EWORKSPACE
+
+
+def test_attention_prefill_rejects_bad_arguments():
+    L = sf.lib()
+    n = ctypes.c_size_t(0)
+    P = L.spark_attn_prefill_workspace_size
+    assert P(64, 8, 3, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EINVAL  # Hq % Hkv
+    assert P(64, 8, 4, 256, 0, 256, ctypes.byref(n)) == sf.SPARK_EINVAL  # r
+    assert P(64, 8, 4, 256, 100, 256, ctypes.byref(n)) == sf.SPARK_EINVAL  # r % 8
+    assert P(0, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EINVAL  # T
+    assert P(1 << 15, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED  # T too long
+    assert P(64, 8, 4, 1024, 128, 256, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED  # hd
+    assert P(64, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_OK and n.value > 64 * 64 * 8 * 6
+    ws = ctypes.create_string_buffer(16)
+    assert L.spark_attn_prefill(None, None, None, None, 64, 8, 4, 256, 128, 256, None, None, None, ws, 16,
+                                None) == sf.SPARK_EINVAL
