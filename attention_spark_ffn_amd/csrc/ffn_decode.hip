@@ -197,7 +197,7 @@ __device__ __forceinline__ int own_first(int g, int d_ff, int G) {
 // Both roles execute exactly the same sequence of workgroup barriers:
 //   per token:  1 (input loaded) [+2 when the input needs normalising]
 //   per layer:  2 per K1 tile, then A, S, [T1, T2: workgroup 0, when a
-//               trace is asked for], V, and either Y (last layer) or C, R;
+//               trace is asked for], V, and either Y (last layer) or C;
 //               the failure flag is read after A, V and C.
 __device__ __forceinline__ void bar() { __syncthreads(); }
 
@@ -206,7 +206,7 @@ __device__ __forceinline__ void bar() { __syncthreads(); }
 // Per-neuron sums of one tile's chunk products.  Wave wv takes neurons
 // wv, wv + 8, ...; in the common case (one tile, rows of at most 192 chunks,
 // at most 64 neurons) all of a wave's LDS reads are issued before any sum.
-__device__ __forceinline__ void reduce_tile(const DecGeo& g, DecShared& S, int tile, int lane, int wv) {
+__device__ __forceinline__ void reduce_tile(const DecGeo& g, DecShared& S, int tile, int lane, int wv, float qs) {
   const int TILE = kStreamers * kDecMaxC;
   const int tb = tile * TILE, te = min(g.TC, tb + TILE);
   if (g.ntile == 1 && g.CK <= 192) {
@@ -228,7 +228,7 @@ __device__ __forceinline__ void reduce_tile(const DecGeo& g, DecShared& S, int t
     int u;
     const float s = wave_colsum<8>(t, lane, u);
     const int j = wv + 8 * u;
-    if ((lane & 7) == 0 && j < g.nown) S.h[j] = s;
+    if ((lane & 7) == 0 && j < g.nown) S.h[j] = s * qs;
     return;
   }
   for (int j = tb / g.CK + wv; j <= (te - 1) / g.CK; j += 8) {
@@ -236,7 +236,7 @@ __device__ __forceinline__ void reduce_tile(const DecGeo& g, DecShared& S, int t
     float s = 0.f;
     for (int c = a + lane; c < b; c += 64) s += S.u.part[c - tb];
     s = wave_sum_dpp(s);
-    if (lane == 0) S.h[j] += s;
+    if (lane == 0) S.h[j] += s * qs;
   }
 }
 
@@ -286,7 +286,9 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
   const bool qreg = g.ntile == 1 && (kStreamers * kQPer) % g.CK == 0;
   const bool trace_here = g.w == 0 && (p.tr_idx || p.tr_counts || p.tr_theta);
   load_tile(0, 0);
+  float qs = 1.f;  // scale of the q held in LDS (its RMS normalisation, applied to the products)
   for (int t = 0; t < g.T; ++t) {
+    qs = 1.f;
     bar();
     if (p.q_prenorm) {
       bar();
@@ -322,7 +324,7 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
           if (m % 3 == 2) __builtin_amdgcn_sched_barrier(0);  // keep few chunks' conversions live
         }
         bar();
-        reduce_tile(g, S, 0, lane, wv);
+        reduce_tile(g, S, 0, lane, wv, qs);
         bar();
       }
       for (int tile = 0; !qreg && tile < g.ntile; ++tile) {
@@ -348,7 +350,7 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
         }
         bar();
         // per-neuron sums of this tile's chunks (waves 4..7 take every other neuron)
-        reduce_tile(g, S, tile, lane, wv);
+        reduce_tile(g, S, tile, lane, wv, qs);
         bar();
       }
       bar();  // A
@@ -367,7 +369,7 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
       }
       bar();  // C
       if (S.fail) return;
-      bar();  // R
+      qs = 1.f / sqrtf((S.wred[0] + S.wred[1] + S.wred[2] + S.wred[3]) / (float)g.d_model + p.eps);
     }
   }
 }
@@ -507,7 +509,9 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
   const int nb_rec = own_first(tid < G ? tid : 0, g.d_ff, G);
   const bool trace_here = w == 0 && (p.tr_idx || p.tr_counts || p.tr_theta);
 
+  float qs = 1.f;  // scale of the q held in LDS (its RMS normalisation, applied to the products)
   for (int t = 0; t < g.T; ++t) {
+    qs = 1.f;
     for (int c = tid; c < d_model; c += kWorkers) S.q[c] = p.q_in[(size_t)t * d_model + c];
     bar();
     if (p.q_prenorm) {
@@ -526,13 +530,13 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       const size_t trow = (size_t)t * p.total_layers + p.layer_offset + l;
       const char* k2base = (const char*)tab_k2[l] + (size_t)g.n0 * k2row;
       if (p.tr_q && w == 0)
-        for (int c = tid; c < d_model; c += kWorkers) p.tr_q[trow * d_model + c] = S.q[c];
+        for (int c = tid; c < d_model; c += kWorkers) p.tr_q[trow * d_model + c] = S.q[c] * qs;
       if (tid < g.nown) S.h[tid] = 0.f;
 
       // ---------------- predictor: the streamers form chunk dots, all waves sum them
       for (int tile = 0; tile < g.ntile; ++tile) {
         bar();  // G1
-        reduce_tile(g, S, tile, lane, wv);
+        reduce_tile(g, S, tile, lane, wv, qs);
         bar();  // G2
       }
 
@@ -606,7 +610,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           const int jm = grp == 0 ? jsel[0] : grp == 1 ? jsel[1] : grp == 2 ? jsel[2] : jsel[3];
           const float d = k2_dot_row16<W>(k2base + (size_t)(jm >= 0 ? jm : jsel[0]) * k2row, S.q + g.r, g.K2C,
                                           lane & 15);
-          if ((lane & 15) == 0 && jm >= 0) S.g[jm] = d;
+          if ((lane & 15) == 0 && jm >= 0) S.g[jm] = d * qs;
         }
       }
       bar();  // A
@@ -622,7 +626,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           const int j = __builtin_ctzll(miss);
           miss &= miss - 1;
           const float d = k2_dot<W>(k2base + (size_t)j * k2row, S.q + g.r, g.K2C, lane);
-          if (lane == 0) S.g[j] = d;
+          if (lane == 0) S.g[j] = d * qs;
         }
         const float cval = on ? gelu_tanh(hj - theta) * S.g[lane < 64 ? lane : 0] : 0.f;
         const int e = __builtin_amdgcn_mbcnt_hi((uint32_t)(M >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)M, 0));
@@ -832,24 +836,9 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         if (tid == 0) raise_failure(p.hdr);
         return;
       }
-      {
-        const float inv = 1.f / sqrtf((S.wred[0] + S.wred[1] + S.wred[2] + S.wred[3]) / (float)d_model + p.eps);
-        // this thread's own columns: all reads issued before any write
-        for (int c0 = tid; c0 < d_model; c0 += kWorkers * 9) {
-          float v[9];
-#pragma unroll
-          for (int k = 0; k < 9; ++k) {
-            const int c = c0 + kWorkers * k;
-            v[k] = c < d_model ? S.q[c] : 0.f;
-          }
-#pragma unroll
-          for (int k = 0; k < 9; ++k) {
-            const int c = c0 + kWorkers * k;
-            if (c < d_model) S.q[c] = v[k] * inv;
-          }
-        }
-      }
-      bar();  // R
+      // the layer output stays in LDS as gathered; its RMS normalisation is the
+      // scale qs applied to every product formed with it in the next layer
+      qs = 1.f / sqrtf((S.wred[0] + S.wred[1] + S.wred[2] + S.wred[3]) / (float)d_model + p.eps);
     }
   }
   if (w == 0 && tid == 0) __hip_atomic_store(p.hdr, (uint64_t)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
