@@ -63,6 +63,25 @@ def ffn_stack(seed: int, n_layers: int, d_model: int, d_ff: int, r: int, dtype: 
         return list(ex.map(lambda l: ffn_layer(seed, l, d_model, d_ff, r, dtype), range(n_layers)))
 
 
+def ffn_layer_planted(seed: int, layer: int, d_model: int, d_ff: int, r: int, q: np.ndarray, blocks,
+                      dtype: str = "bf16"):
+    """ffn_layer with planted blocks of predictor keys: for each (t, lo, hi, s)
+    in `blocks`, K1 rows lo..hi-1 become s times the unit direction of
+    q[t, :r] plus N(0, (0.02 s)^2 / r) noise, so their scores for token t are
+    about s * |q[t, :r]| (far above or below the rest for |s| ~ 0.1)."""
+    k1t, k2t, v = ffn_layer(seed, layer, d_model, d_ff, r, "f32")
+    g = rng(seed, layer, K1_ID, 1)
+    for t, lo, hi, s in blocks:
+        u = q[t, :r].astype(np.float64)
+        u = (u / np.linalg.norm(u)).astype(np.float32)
+        k1t[lo:hi] = np.float32(s) * u + _normal(g, (hi - lo, r), 0.02 * abs(s) / np.sqrt(r))
+    if dtype == "bf16":
+        return f32_to_bf16_bits(k1t), f32_to_bf16_bits(k2t), f32_to_bf16_bits(v)
+    if dtype == "f32":
+        return k1t, k2t, v
+    raise ValueError(dtype)
+
+
 def queries(seed: int, T: int, d_model: int, dtype: str = "f32", stream: int = 0) -> np.ndarray:
     """T query vectors ~ N(0, 1)."""
     q = _normal(rng(seed, stream, Q_ID), (T, d_model), 1.0)

@@ -101,6 +101,26 @@ def test_decode_full_stack_config():
     run_stack(layers, q0, 1152, 737, tol=2e-2)
 
 
+def test_decode_clustered_selection():
+    """Workgroups whose neurons are nearly all selected.  Layer 0 plants blocks
+    of predictor keys along each token's query: token 0 gets 64 contiguous
+    neurons far above theta (more than a workgroup publishes as candidates
+    with 256 workgroups of 36 neurons), token 1 a block of 100; neurons
+    3600..3611 are far above theta and 3612..3635 far below for token 0 (with
+    256 workgroups: exactly the candidates selected, none beyond).  Any grid
+    must give the oracle's result."""
+    dm, dff, r, k = 2304, 9216, 1152, 737
+    q0 = synth.queries(11, 2, dm)
+    blocks = [(0, 0, 64, 0.1), (1, 4000, 4100, 0.1), (0, 3600, 3612, 0.1), (0, 3612, 3636, -0.1)]
+    layers = [synth.ffn_layer_planted(11, 0, dm, dff, r, q0, blocks, "bf16"),
+              synth.ffn_layer(11, 1, dm, dff, r, "bf16")]
+    y, tr = run_stack(layers, q0, r, k, tol=2e-2)
+    idx0 = set(tr["idx"][0, 0][: tr["counts"][0, 0]].tolist())
+    assert set(range(64)) | set(range(3600, 3612)) <= idx0 and not idx0 & set(range(3612, 3636))
+    idx1 = set(tr["idx"][1, 0][: tr["counts"][1, 0]].tolist())
+    assert set(range(4000, 4100)) <= idx1
+
+
 def test_decode_many_layers_segments():
     # more layers than one launch holds: the stack is split across launches
     L = 40
