@@ -2,6 +2,8 @@
 // epilogues that apply the Spark gates.  Included by ffn_prefill.hip and
 // attn_prefill.hip.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace spark {
@@ -41,8 +43,13 @@ struct GemmArgs {
 //
 // Workgroup tile (WM*MI*32) x (WN*NI*32): WM x WN waves, each holding MI x NI
 // accumulators of v_mfma_f32_32x32x16_bf16 (a 32*MI x 32*NI block).  A wave
-// reads MI + NI fragments from LDS per 16 of K for MI*NI MFMAs.  K in steps
-// of 64 through double-buffered LDS, staged through registers.
+// reads MI + NI fragments from LDS per 16 of K for MI*NI MFMAs, one step of
+// 16 ahead of the MFMAs that use them.  K in stages of 64 through two LDS
+// buffers: while the MFMAs of stage s run, stage s+1 (loaded into registers
+// during stage s-1) is written to the other buffer and stage s+2 is loaded,
+// both spread over the four steps of 16; one barrier per stage.  Tiles are
+// dealt to the eight XCDs in contiguous runs (eight M tiles at a time down
+// the N tiles), so the A and B panels a run shares stay in that XCD's L2.
 //   kEpiStore: C[m][n] (fp32, row stride ldc) = D; with a K split, split s
 //              writes its partial to C + s * M * ldc.
 //   kEpiGate:  C[m][n] (bf16) = GELU(H - r0[m]) * D where H = H[m][n] > r0[m]
@@ -64,8 +71,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
   __shared__ alignas(16) bf16_t Bs[2][BN * GLD];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int M = g.M, N = g.N;
-  const int MT = (M + BM - 1) / BM;
-  const int tm = blockIdx.x % MT, tn = blockIdx.x / MT;
+  const int MT = (M + BM - 1) / BM, NTN = (N + BN - 1) / BN;
+  // workgroups are dealt round-robin to the 8 XCDs (gridDim.x a multiple of
+  // 8): XCD x takes the tile indices [x * per, (x + 1) * per), ordered eight
+  // M tiles at a time down the N tiles
+  int tm, tn;
+  {
+    const int tiles = MT * NTN, per = (tiles + 7) / 8;
+    const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (t >= tiles) return;
+    constexpr int GM = 8;
+    const int grp = t / (GM * NTN), rem = t % (GM * NTN);
+    const int gm = min(GM, MT - grp * GM);
+    tm = grp * GM + rem % gm;
+    tn = rem / gm;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   if (g.causal == kCausalTiles && n0 > m0 + BM - 1) return;
   const int wm = wv / WN, wn = wv % WN;
@@ -76,38 +96,43 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
   const int kbeg = blockIdx.y * g.ksplit;
   int kend = min(g.K, kbeg + g.ksplit);
   if (g.causal == kCausalK) kend = min(kend, m0 + BM);
+  const int KT = kend > kbeg ? (kend - kbeg + GBK - 1) / GBK : 0;
 
-  // Chunks past K are loaded from column 0 and replaced by zeros only when
-  // stored to LDS, after the MFMAs of the current stage, so the loads stay in
-  // flight across those MFMAs.
-  u32x4 ra[CA], rb[CB];
-  int kload = 0;
-  auto gload = [&](int k0) {
-    kload = k0;
+  // Two register sets of staged 16-byte chunks (stage s in set s & 1).
+  // Chunk i of a stage belongs to step i % 4 of the stage that moves it.
+  // Chunks past K are loaded from column 0 and zeroed when stored to LDS.
+  static_assert(CA % 4 == 0 && CB % 4 == 0, "chunks split over the four steps of a stage");
+  u32x4 ra[2][CA], rb[2][CB];
+  auto gload_part = [&](int set, int k0, int part) {
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
+      if (i % 4 != part) continue;
       const int c = tid + NT * i, row = c >> 3, kc = c & 7;
       const int k = k0 + kc * 8;
-      ra[i] = load16(A + (size_t)min(m0 + row, M - 1) * lda + (k < kend ? k : 0));
+      ra[set][i] = load16(A + (size_t)min(m0 + row, M - 1) * lda + (k < kend ? k : 0));
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
+      if (i % 4 != part) continue;
       const int c = tid + NT * i, row = c >> 3, kc = c & 7;
       const int k = k0 + kc * 8;
-      rb[i] = load16(B + (size_t)min(n0 + row, N - 1) * ldb + (k < kend ? k : 0));
+      rb[set][i] = load16(B + (size_t)min(n0 + row, N - 1) * ldb + (k < kend ? k : 0));
     }
   };
-  auto sstore = [&](int buf) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto sstore_part = [&](int set, int buf, int k0, int part) {
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
+      if (i % 4 != part) continue;
       const int c = tid + NT * i, row = c >> 3, kc = c & 7;
-      *reinterpret_cast<u32x4*>(&As[buf][row * GLD + kc * 8]) = kload + kc * 8 < kend ? ra[i] : zero;
+      const uint32_t keep = k0 + kc * 8 < kend ? ~0u : 0u;
+      *reinterpret_cast<u32x4*>(&As[buf][row * GLD + kc * 8]) = ra[set][i] & keep;
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
+      if (i % 4 != part) continue;
       const int c = tid + NT * i, row = c >> 3, kc = c & 7;
-      *reinterpret_cast<u32x4*>(&Bs[buf][row * GLD + kc * 8]) = kload + kc * 8 < kend ? rb[i] : zero;
+      const uint32_t keep = k0 + kc * 8 < kend ? ~0u : 0u;
+      *reinterpret_cast<u32x4*>(&Bs[buf][row * GLD + kc * 8]) = rb[set][i] & keep;
     }
   };
 
@@ -119,32 +144,54 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = kend > kbeg ? (kend - kbeg + GBK - 1) / GBK : 0;
   if (KT > 0) {
-    gload(kbeg);
-    sstore(0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) gload_part(0, kbeg, p);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) gload_part(1, kbeg + min(1, KT - 1) * GBK, p);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) sstore_part(0, 0, kbeg, p);
   }
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kbeg + (kt + 1) * GBK);
+  const int ro = lane & 31, kh = (lane >> 5) * 8;  // lanes 0-31: k 0..7 of a step, lanes 32-63: k 8..15
+  // One stage; its register set and LDS buffer (kt & 1) are compile-time
+  // constants (the stage loop is unrolled by two).  Past the last stage the
+  // last one is loaded and stored again (never read).
+  auto stage = [&](auto setc, int kt) {
+    constexpr int set = decltype(setc)::value, buf = set;
+    const int k1 = kbeg + min(kt + 1, KT - 1) * GBK, k2 = kbeg + min(kt + 2, KT - 1) * GBK;
+    bf16x8 a[2][MI], b[2][NI];
 #pragma unroll
-    for (int kk = 0; kk < GBK; kk += 16) {
-      const int ko = kk + (lane >> 5) * 8;  // lanes 0-31: k 0..7, lanes 32-63: k 8..15
-      bf16x8 a[MI], b[NI];
+    for (int i = 0; i < MI; ++i)
+      a[0][i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * MI * 32 + i * 32 + ro) * GLD + kh]);
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      b[0][j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn * NI * 32 + j * 32 + ro) * GLD + kh]);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int cur = st & 1;
+      if (st < 3) {
+        const int ko = (st + 1) * 16 + kh;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          a[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * MI * 32 + i * 32 + ro) * GLD + ko]);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          b[cur ^ 1][j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn * NI * 32 + j * 32 + ro) * GLD + ko]);
+      }
+      sstore_part(set ^ 1, buf ^ 1, k1, st);
+      gload_part(set, k2, st);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * MI * 32 + i * 32 + (lane & 31)) * GLD + ko]);
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn * NI * 32 + j * 32 + (lane & 31)) * GLD + ko]);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    stage(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < KT) stage(std::integral_constant<int, 1>{}, kt + 1);
   }
   // D layout of the 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
   const int ldc = g.ldc;
@@ -245,10 +292,11 @@ constexpr int kBM = kWM * kMI * 32, kBN = kWN * kNI * 32;
 template <int EPI>
 inline hipError_t launch_gemm(GemmArgs a, int splits, int batch, hipStream_t st) {
   const int tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+  const int grid = (tiles + 7) / 8 * 8;  // a multiple of the XCD count (see gemm_bf16_nt)
   int ks = (a.K + splits - 1) / splits;
   a.ksplit = (ks + GBK - 1) / GBK * GBK;
   if (a.bgroup < 1) a.bgroup = 1;
-  hipLaunchKernelGGL((gemm_bf16_nt<EPI, kWM, kWN, kMI, kNI>), dim3(tiles, splits, batch), dim3(kWM * kWN * 64), 0,
+  hipLaunchKernelGGL((gemm_bf16_nt<EPI, kWM, kWN, kMI, kNI>), dim3(grid, splits, batch), dim3(kWM * kWN * 64), 0,
                      st, a);
   return hipGetLastError();
 }
