@@ -208,6 +208,17 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 // softplus log(1 + e^v) in the overflow-free form max(v,0) + log1p(e^-|v|).
 __device__ __forceinline__ float softplus(float v) { return fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v))); }
 
+// The same on the hardware exp2/log2/reciprocal (v_exp_f32, v_log_f32,
+// v_rcp_f32, about 1 ulp each): log1p(e) for e = e^-|v| in (0, 1] as
+// log(u) * e / (u - 1) with u = 1 + e in [1, 2] (the rounding of u cancels in
+// the ratio; u - 1 is exact), and e itself when u rounds to 1.
+__device__ __forceinline__ float softplus_fast(float v) {
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * fabsf(v));
+  const float u = 1.f + e;
+  const float l = u == 1.f ? e : (0.6931471805599453f * __builtin_amdgcn_logf(u)) * (e * __builtin_amdgcn_rcpf(u - 1.f));
+  return fmaxf(v, 0.f) + l;
+}
+
 // ---------------------------------------------------------------- tagged words
 // Cross-workgroup exchange inside one persistent kernel.  A published value is
 // a 64-bit word {value bits, 32-bit tag} written and read with device-scope

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
         p0[r] = R0[m];
         if (EPI == kEpiAttn) {
           p1[r] = R1[m];
-          p2[r] = R2[m];
+          p2[r] = __builtin_amdgcn_rcpf(R2[m]);  // one reciprocal per row of the block
         }
       }
     }
@@ -237,7 +237,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
             Cb[(size_t)m * ldc + n] = f32_to_bf16(c);
           } else {
             const bool on = n <= m && hv[r] > p0[r];
-            const float c = on ? __expf(hv[r] - p1[r]) / p2[r] * softplus(acc[i][j][r]) : 0.f;
+            const float c = on ? __builtin_amdgcn_exp2f(1.4426950408889634f * (hv[r] - p1[r])) * p2[r] *
+                                        softplus_fast(acc[i][j][r])
+                                  : 0.f;
             Cb[(size_t)m * ldc + n] = f32_to_bf16(c);
           }
         }
