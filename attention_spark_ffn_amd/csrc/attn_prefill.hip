@@ -10,8 +10,8 @@
 // gfx950 mapping: three dense bf16 products on the matrix cores, causal at
 // tile granularity, with the selection applied in an epilogue:
 //   1. S = Q[:, h, :r] K1[g]^T (fp32 scores), tiles above the diagonal skipped;
-//   2. attn_prefill_rows, one workgroup per (h, t): theta over the t + 1
-//      scores (two exact passes, z = Q(1 - k_attn/(t+1)) from a table
+//   2. attn_prefill_rows, one workgroup per (h, t), the row in registers:
+//      theta over the t + 1 scores (two exact passes, z = Q(1 - k_attn/(t+1)) from a table
 //      computed on the device in fp64), then the largest selected score and
 //      the sum of e^(s - max) over the selected;
 //   3. W = Q[:, h, r:] K2[g]^T with the epilogue
@@ -75,7 +75,10 @@ __device__ __forceinline__ float rows_max(float v, float* red) {
   return t;
 }
 
-// One workgroup per (h, t): row t of head h's scores, positions 0..t.
+// One workgroup per (h, t): row t of head h's scores, positions 0..t, held
+// in registers (thread i takes the 16-byte chunks i, i + 256, ...; PER values
+// per thread cover rows up to 1024 PER), read from memory once.
+template <int PER>
 __global__ __launch_bounds__(256) void attn_prefill_rows(const float* __restrict__ S, int T, int ldt, int Hq,
                                                          int k_attn,
                                                          const float* __restrict__ ztab, float* __restrict__ rth,
@@ -86,34 +89,48 @@ __global__ __launch_bounds__(256) void attn_prefill_rows(const float* __restrict
   const int h = blockIdx.x / T, t = blockIdx.x % T, n = t + 1;
   const float* s = S + ((size_t)h * T + t) * ldt;
   const bool dense = n <= k_attn;
+  // chunks start below n <= ldt (a multiple of 8), so a whole chunk is inside the row
+  float v[PER];
+  bool ok[PER];
+#pragma unroll
+  for (int c = 0; c < PER / 4; ++c) {
+    const int j = 4 * (tid + 256 * c);
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (j < n) x = *reinterpret_cast<const f32x4*>(s + j);
+    v[4 * c] = x.x;
+    v[4 * c + 1] = x.y;
+    v[4 * c + 2] = x.z;
+    v[4 * c + 3] = x.w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ok[4 * c + e] = j + e < n;
+  }
   float th = -INFINITY;
   if (!dense) {
     float a = 0.f;
-    for (int j = tid; j < n; j += 256) a += s[j];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) a += ok[i] ? v[i] : 0.f;
     const float mean = rows_sum(a, red) / (float)n;
     float b = 0.f;
-    for (int j = tid; j < n; j += 256) {
-      const float d = s[j] - mean;
-      b += d * d;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const float d = v[i] - mean;
+      b += ok[i] ? d * d : 0.f;
     }
     const float m2 = rows_sum(b, red);
     th = mean + sqrtf(m2 / (float)n) * ztab[n];
   }
   float mx = -INFINITY;
   int c = 0;
-  for (int j = tid; j < n; j += 256) {
-    const float v = s[j];
-    if (v > th) {
-      mx = fmaxf(mx, v);
-      ++c;
-    }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool on = ok[i] && v[i] > th;
+    mx = on ? fmaxf(mx, v[i]) : mx;
+    c += on ? 1 : 0;
   }
   mx = rows_max(mx, red);
   float l = 0.f;
-  for (int j = tid; j < n; j += 256) {
-    const float v = s[j];
-    l += v > th ? __expf(v - mx) : 0.f;
-  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) l += (ok[i] && v[i] > th) ? __expf(v[i] - mx) : 0.f;
   l = rows_sum(l, red);
   const int cnt = (int)rows_sum((float)c, red);  // exact: counts stay far below 2^24
   if (tid == 0) {
@@ -198,8 +215,24 @@ hipError_t launch_attn_prefill(const void* q, const void* k1, const void* k2, co
     if (e != hipSuccess) return e;
   }
   // 2. per-row threshold, largest selected score, softmax denominator
-  hipLaunchKernelGGL(attn_prefill_rows, dim3((unsigned)(H * T)), dim3(256), 0, st, S, Ti, LT, H, (int)k_attn, ztab,
-                     rth, rmx, rl, counts, theta);
+  {
+    const dim3 g((unsigned)(H * T)), b(256);
+    if (Ti <= 1024)
+      hipLaunchKernelGGL(attn_prefill_rows<4>, g, b, 0, st, S, Ti, LT, H, (int)k_attn, ztab, rth, rmx, rl, counts,
+                         theta);
+    else if (Ti <= 2048)
+      hipLaunchKernelGGL(attn_prefill_rows<8>, g, b, 0, st, S, Ti, LT, H, (int)k_attn, ztab, rth, rmx, rl, counts,
+                         theta);
+    else if (Ti <= 4096)
+      hipLaunchKernelGGL(attn_prefill_rows<16>, g, b, 0, st, S, Ti, LT, H, (int)k_attn, ztab, rth, rmx, rl, counts,
+                         theta);
+    else if (Ti <= 8192)
+      hipLaunchKernelGGL(attn_prefill_rows<32>, g, b, 0, st, S, Ti, LT, H, (int)k_attn, ztab, rth, rmx, rl, counts,
+                         theta);
+    else
+      hipLaunchKernelGGL(attn_prefill_rows<64>, g, b, 0, st, S, Ti, LT, H, (int)k_attn, ztab, rth, rmx, rl, counts,
+                         theta);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 3. gated weights
