@@ -14,12 +14,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  return (bf16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
+// fp32 -> bf16, round to nearest even (NaN stays NaN): gfx950's
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // 16 bytes of weights widened to fp32: 8 bf16 or 4 fp32 values.
 template <typename W>

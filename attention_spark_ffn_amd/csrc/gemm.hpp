@@ -226,22 +226,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
           hv[r] = H[(size_t)min(m, M - 1) * g.ldh + min(n, N - 1)];
         }
       }
+      // row of register r: mb + 8 (r / 4) + r % 4; one address per block,
+      // constant row offsets per register; the gates are selects (the
+      // arithmetic runs for every element, as a wave with any selected lane
+      // would run it anyway)
+      const int mb = m0 + wm * MI * 32 + i * 32 + 4 * (lane >> 5);
+      float* frow = Cf + (size_t)mb * ldc + n;
+      bf16_t* brow = Cb + (size_t)mb * ldc + n;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * MI * 32 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < M && n < N) {
-          if (EPI == kEpiStore) {
-            Cf[(size_t)m * ldc + n] = acc[i][j][r];
-          } else if (EPI == kEpiGate) {
-            const float c = hv[r] > p0[r] ? gelu_tanh(hv[r] - p0[r]) * acc[i][j][r] : 0.f;
-            Cb[(size_t)m * ldc + n] = f32_to_bf16(c);
-          } else {
-            const bool on = n <= m && hv[r] > p0[r];
-            const float c = on ? __builtin_amdgcn_exp2f(1.4426950408889634f * (hv[r] - p1[r])) * p2[r] *
-                                        softplus_fast(acc[i][j][r])
-                                  : 0.f;
-            Cb[(size_t)m * ldc + n] = f32_to_bf16(c);
-          }
+        const int dm = 8 * (r >> 2) + (r & 3), m = mb + dm;
+        const bool in = m < M && n < N;
+        if (EPI == kEpiStore) {
+          if (in) frow[(size_t)dm * ldc] = acc[i][j][r];
+        } else if (EPI == kEpiGate) {
+          const float gv = gelu_tanh(hv[r] - p0[r]) * acc[i][j][r];
+          const float c = hv[r] > p0[r] ? gv : 0.f;
+          if (in) brow[(size_t)dm * ldc] = f32_to_bf16(c);
+        } else {
+          const float gv =
+              __builtin_amdgcn_exp2f(1.4426950408889634f * (hv[r] - p1[r])) * p2[r] * softplus_fast(acc[i][j][r]);
+          const float c = (n <= m && hv[r] > p0[r]) ? gv : 0.f;
+          if (in) brow[(size_t)dm * ldc] = f32_to_bf16(c);
         }
       }
     }
