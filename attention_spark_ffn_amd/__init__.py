@@ -9,6 +9,7 @@ RuntimeError is raised.
 Entry points (same names as the C ABI):
   stat_topk(x, k, cap=None)                         -> (vals, idx, counts, theta)
   spark_ffn_decode(q, layers, k, r, eps, ...)       -> y  (and a trace dict)
+  spark_ffn_decode_batched(q, layers, k, r, eps, ...)  -> the same, B <= 8 tokens layer by layer
   spark_ffn_prefill(Q, layer, k, r, ...)            -> Y  (and a trace dict)
   spark_attn_decode(q, k1, k2, v, k_attn, cap=None) -> (out, counts, idx, theta)
   spark_attn_prefill(q, k1, k2, v, k_attn)          -> (out, counts, theta)
@@ -65,6 +66,12 @@ def lib() -> ctypes.CDLL:
                 L.spark_ffn_decode.restype = _ci
                 L.spark_ffn_decode.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _ci, _vp, _i64, _vp,
                                                _f, ctypes.POINTER(TraceC), _vp, _sz, _vp]
+                L.spark_ffn_decode_batched.restype = _ci
+                L.spark_ffn_decode_batched.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _ci, _vp,
+                                                       _i64, _vp, _f, ctypes.POINTER(TraceC), _vp, _sz, _vp]
+                L.spark_ffn_decode_batched_workspace_size.restype = _ci
+                L.spark_ffn_decode_batched_workspace_size.argtypes = [ctypes.POINTER(ShapeC), _i64,
+                                                                      ctypes.POINTER(_sz)]
                 L.spark_ffn_prefill.restype = _ci
                 L.spark_ffn_prefill.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _vp, _i64, _vp,
                                                 ctypes.POINTER(TraceC), _vp, _sz, _vp]
@@ -166,17 +173,8 @@ def _shape(d_model, d_ff, r, k, wd) -> ShapeC:
     return ShapeC(int(d_model), int(d_ff), int(r), int(k), int(wd))
 
 
-def spark_ffn_decode(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6, trace: bool = False,
-                     cap: int | None = None, ws: torch.Tensor | None = None):
-    """Run the stack of Spark FFN layers on T independent tokens.
-
-    q [T][d_model] fp32; layers: list of (k1t [d_ff][r], k2t [d_ff][d_model-r],
-    v [d_ff][d_model]) tensors, all bf16 or all fp32.  Returns y [T][d_model]
-    fp32 (last layer, before normalisation).  With trace=True also returns a
-    dict with counts [T][L], idx [T][L][cap], theta [T][L], q_in [T][L][d_model].
-    ws: optional zero-initialised uint8 workspace to use (and carry) instead of
-    the module's cached one.
-    """
+def _stack_args(q: torch.Tensor, layers, k: int, r: int):
+    """Shape checks of a layer stack; the C shape and weight-table structs."""
     _need_cuda(q)
     T, d_model = q.shape
     L = len(layers)
@@ -191,6 +189,31 @@ def spark_ffn_decode(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6,
             raise ValueError("weight shapes do not match q / r")
     shape = _shape(d_model, d_ff, r, k, wd)
     wts = (WeightsC * L)(*[WeightsC(a.data_ptr(), b.data_ptr(), c.data_ptr()) for (a, b, c) in layers])
+    return T, d_model, L, d_ff, shape, wts
+
+
+def _trace_buffers(T: int, L: int, d_ff: int, d_model: int, cap, dev):
+    cap = d_ff if cap is None else int(cap)
+    tr = dict(counts=torch.zeros((T, L), dtype=torch.int32, device=dev),
+              idx=torch.full((T, L, cap), -1, dtype=torch.int32, device=dev),
+              theta=torch.zeros((T, L), dtype=torch.float32, device=dev),
+              q_in=torch.zeros((T, L, d_model), dtype=torch.float32, device=dev))
+    trc = TraceC(tr["counts"].data_ptr(), tr["idx"].data_ptr(), tr["theta"].data_ptr(), tr["q_in"].data_ptr(), cap)
+    return tr, trc
+
+
+def spark_ffn_decode(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6, trace: bool = False,
+                     cap: int | None = None, ws: torch.Tensor | None = None):
+    """Run the stack of Spark FFN layers on T independent tokens.
+
+    q [T][d_model] fp32; layers: list of (k1t [d_ff][r], k2t [d_ff][d_model-r],
+    v [d_ff][d_model]) tensors, all bf16 or all fp32.  Returns y [T][d_model]
+    fp32 (last layer, before normalisation).  With trace=True also returns a
+    dict with counts [T][L], idx [T][L][cap], theta [T][L], q_in [T][L][d_model].
+    ws: optional zero-initialised uint8 workspace to use (and carry) instead of
+    the module's cached one.
+    """
+    T, d_model, L, d_ff, shape, wts = _stack_args(q, layers, k, r)
     need = ctypes.c_size_t(0)
     _check(lib().spark_ffn_decode_workspace_size(ctypes.byref(shape), L, T, ctypes.byref(need)),
            "spark_ffn_decode_workspace_size")
@@ -201,15 +224,31 @@ def spark_ffn_decode(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6,
     tr = None
     trc = None
     if trace:
-        cap = d_ff if cap is None else int(cap)
-        tr = dict(counts=torch.zeros((T, L), dtype=torch.int32, device=dev),
-                  idx=torch.full((T, L, cap), -1, dtype=torch.int32, device=dev),
-                  theta=torch.zeros((T, L), dtype=torch.float32, device=dev),
-                  q_in=torch.zeros((T, L, d_model), dtype=torch.float32, device=dev))
-        trc = TraceC(tr["counts"].data_ptr(), tr["idx"].data_ptr(), tr["theta"].data_ptr(), tr["q_in"].data_ptr(), cap)
+        tr, trc = _trace_buffers(T, L, d_ff, d_model, cap, dev)
     st = lib().spark_ffn_decode(ctypes.byref(shape), wts, L, _p(q), T, _p(y), float(eps),
                                 ctypes.byref(trc) if trc is not None else None, _p(ws), ws.numel(), _stream(dev))
     _check(st, "spark_ffn_decode")
+    return (y, tr) if trace else y
+
+
+def spark_ffn_decode_batched(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6, trace: bool = False,
+                             cap: int | None = None):
+    """The computation of spark_ffn_decode for a batch of B <= 8 tokens, run
+    layer by layer for the whole batch (one K1 read per layer, K2 and V rows
+    read once for all the tokens that select them).  Same arguments, results
+    and trace as spark_ffn_decode with T = B."""
+    B, d_model, L, d_ff, shape, wts = _stack_args(q, layers, k, r)
+    need = ctypes.c_size_t(0)
+    _check(lib().spark_ffn_decode_batched_workspace_size(ctypes.byref(shape), B, ctypes.byref(need)),
+           "spark_ffn_decode_batched_workspace_size")
+    dev = q.device
+    ws = _cached_workspace("decode_batched", dev, need.value)
+    y = torch.empty((B, d_model), dtype=torch.float32, device=dev)
+    tr, trc = _trace_buffers(B, L, d_ff, d_model, cap, dev) if trace else (None, None)
+    st = lib().spark_ffn_decode_batched(ctypes.byref(shape), wts, L, _p(q), B, _p(y), float(eps),
+                                        ctypes.byref(trc) if trc is not None else None, _p(ws), ws.numel(),
+                                        _stream(dev))
+    _check(st, "spark_ffn_decode_batched")
     return (y, tr) if trace else y
 
 

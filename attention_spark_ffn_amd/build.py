@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quantile.cpp", "stat_topk.hip", "ffn_decode.hip", "ffn_prefill.hip", "attn_decode.hip",
+SOURCES = ["api.cpp", "quantile.cpp", "stat_topk.hip", "ffn_decode.hip", "ffn_decode_batched.hip", "ffn_prefill.hip", "attn_decode.hip",
            "attn_prefill.hip"]
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

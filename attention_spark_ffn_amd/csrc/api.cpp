@@ -120,6 +120,37 @@ int spark_ffn_decode(const spark_ffn_shape* s, const spark_ffn_weights* layers, 
   return hip_status(spark::launch_decode(*s, layers, n_layers, q, T, y, rms_eps, z, trace, ws, stream));
 }
 
+int spark_ffn_decode_batched_workspace_size(const spark_ffn_shape* s, int64_t B, size_t* bytes) {
+  if (!bytes) return SPARK_EINVAL;
+  int st = check_ffn_shape(s);
+  if (st != SPARK_OK) return st;
+  if (B < 0) return SPARK_EINVAL;
+  if (B > spark::kBatchMax || s->d_model > spark::kDecodeMaxDModel || s->d_ff > 65536) return SPARK_EUNSUPPORTED;
+  const int64_t wide = s->r > s->d_model - s->r ? s->r : s->d_model - s->r;
+  if (B * wide * 4 > spark::kBatchMaxLds) return SPARK_EUNSUPPORTED;
+  *bytes = spark::decode_batched_workspace_bytes(s->d_model, s->d_ff, B > 0 ? B : 1);
+  return SPARK_OK;
+}
+
+int spark_ffn_decode_batched(const spark_ffn_shape* s, const spark_ffn_weights* layers, int n_layers,
+                             const float* q, int64_t B, float* y, float rms_eps, const spark_ffn_trace* trace,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  size_t need = 0;
+  int st = spark_ffn_decode_batched_workspace_size(s, B, &need);
+  if (st != SPARK_OK) return st;
+  if (n_layers < 1 || !layers || !(rms_eps >= 0.f) || !std::isfinite(rms_eps)) return SPARK_EINVAL;
+  for (int l = 0; l < n_layers; ++l) {
+    st = check_weights(layers[l]);
+    if (st != SPARK_OK) return st;
+  }
+  if (B > 0 && (!q || !y || !aligned(q, 16) || !aligned(y, 16))) return SPARK_EINVAL;
+  if (trace && trace->idx && trace->cap < 0) return SPARK_EINVAL;
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return SPARK_EWORKSPACE;
+  if (B == 0) return SPARK_OK;
+  const double z = spark_threshold_z(s->k, s->d_ff);
+  return hip_status(spark::launch_decode_batched(*s, layers, n_layers, q, B, y, rms_eps, z, trace, ws, stream));
+}
+
 int spark_ffn_prefill_workspace_size(const spark_ffn_shape* s, int64_t T, size_t* bytes) {
   if (!bytes) return SPARK_EINVAL;
   int st = check_ffn_shape(s);

@@ -84,6 +84,11 @@ __device__ __forceinline__ int wave_incl_scan_dpp(int v) {
   return v;
 }
 
+// Set bits of the wave mask m that belong to lanes below this one.
+__device__ __forceinline__ int mbcnt64(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
 // Sum over each row of 16 lanes (DPP within rows); every lane of a row gets
 // its row's total.
 __device__ __forceinline__ float row16_sum(float v) {

@@ -117,6 +117,23 @@ int spark_ffn_decode(const spark_ffn_shape *s, const spark_ffn_weights *layers, 
                      hipStream_t stream);
 
 /*
+ * Batched Spark FFN decode: the computation of spark_ffn_decode for B
+ * independent tokens (q [B][d_model] fp32 in, y [B][d_model] fp32 out, the
+ * same trace layout with T = B), with the batch processed layer by layer: one
+ * read of K1 per layer serves all B tokens, and the K2 and V rows of a neuron
+ * are read once for all the tokens that select it (the union of the
+ * per-token selected sets).  Three kernels per layer on `stream` (a fourth
+ * when a trace is asked for); results equal spark_ffn_decode's up to the
+ * order of fp32 sums.
+ * Requires 0 <= B <= 8, d_model <= 8192, d_ff <= 65536,
+ * B * max(r, d_model - r) * 4 <= 65536, q and y 16-byte aligned, and the
+ * weight conditions of spark_ffn_decode.  The workspace needs no clearing.
+ */
+int spark_ffn_decode_batched(const spark_ffn_shape *s, const spark_ffn_weights *layers, int n_layers,
+                             const float *q, int64_t B, float *y, float rms_eps, const spark_ffn_trace *trace,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Spark FFN prefill: the same layer (one layer) applied to T tokens at once
  * (same result as spark_ffn_decode of one layer per token, without the
  * normalisation).  The predictor scores K1^T Q[:, :r] are a dense GEMM on the
@@ -174,6 +191,7 @@ int spark_attn_prefill(const void *q, const void *k1, const void *k2, const void
 
 /* Workspace sizes (bytes) for the calls above with the same arguments. */
 int spark_ffn_decode_workspace_size(const spark_ffn_shape *s, int n_layers, int64_t T, size_t *bytes);
+int spark_ffn_decode_batched_workspace_size(const spark_ffn_shape *s, int64_t B, size_t *bytes);
 int spark_ffn_prefill_workspace_size(const spark_ffn_shape *s, int64_t T, size_t *bytes);
 int spark_attn_workspace_size(int64_t Hq, int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn,
                               size_t *bytes);

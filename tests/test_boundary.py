@@ -23,8 +23,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["stat_topk", "spark_ffn_decode", "spark_ffn_prefill", "spark_attn_decode",
-              "spark_ffn_decode_workspace_size", "spark_ffn_prefill_workspace_size", "spark_attn_workspace_size",
+    for n in ["stat_topk", "spark_ffn_decode", "spark_ffn_decode_batched", "spark_ffn_prefill", "spark_attn_decode",
+              "spark_ffn_decode_workspace_size", "spark_ffn_decode_batched_workspace_size",
+              "spark_ffn_prefill_workspace_size", "spark_attn_workspace_size",
               "spark_attn_prefill", "spark_attn_prefill_workspace_size", "spark_status_string", "spark_threshold_z"]:
         assert n in names, n
 
@@ -102,6 +103,32 @@ def test_decode_rejects_bad_arguments():
     assert L.spark_ffn_decode(None, w, 1, None, 1, None, 1e-6, None, None, 0, None) == sf.SPARK_EINVAL
     assert L.spark_ffn_decode(ctypes.byref(_shape(wdtype=7)), w, 1, None, 1, None, 1e-6, None, None, 0,
                               None) == sf.SPARK_EUNSUPPORTED
+
+
+def test_batched_decode_rejects_bad_arguments():
+    L = sf.lib()
+    n = ctypes.c_size_t(0)
+    W = L.spark_ffn_decode_batched_workspace_size
+    assert W(ctypes.byref(_shape()), 4, ctypes.byref(n)) == sf.SPARK_OK and n.value > 0
+    assert W(ctypes.byref(_shape()), -1, ctypes.byref(n)) == sf.SPARK_EINVAL
+    assert W(ctypes.byref(_shape()), 9, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED  # more than 8 tokens
+    big = _shape(d_model=8192, r=4096)
+    assert W(ctypes.byref(big), 8, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED  # q slices beyond the LDS budget
+    assert W(ctypes.byref(_shape(r=0)), 1, ctypes.byref(n)) == sf.SPARK_EINVAL
+    s = _shape()
+    w = (sf.WeightsC * 1)(sf.WeightsC(256, 256, 256))
+    D = L.spark_ffn_decode_batched
+    ws = ctypes.c_void_p(256)
+    assert D(ctypes.byref(s), w, 0, ctypes.c_void_p(256), 1, ctypes.c_void_p(256), 1e-6, None, ws, 1 << 30,
+             None) == sf.SPARK_EINVAL  # no layers
+    assert D(ctypes.byref(s), w, 1, ctypes.c_void_p(260), 1, ctypes.c_void_p(256), 1e-6, None, ws, 1 << 30,
+             None) == sf.SPARK_EINVAL  # q not 16-byte aligned
+    assert D(ctypes.byref(s), w, 1, None, 1, ctypes.c_void_p(256), 1e-6, None, ws, 1 << 30,
+             None) == sf.SPARK_EINVAL  # no q
+    assert D(ctypes.byref(s), w, 1, ctypes.c_void_p(256), 1, ctypes.c_void_p(256), 1e-6, None, ws, 16,
+             None) == sf.SPARK_EWORKSPACE
+    assert D(ctypes.byref(s), w, 1, ctypes.c_void_p(256), 0, ctypes.c_void_p(256), 1e-6, None, ws, 1 << 30,
+             None) == sf.SPARK_OK  # empty batch: nothing enqueued
 
 
 def test_prefill_and_attention_reject_bad_arguments():

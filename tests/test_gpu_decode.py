@@ -32,13 +32,15 @@ def layer_parity(q_in, lw, r, k, gpu_idx, gpu_count, gpu_theta, y_next_gpu, eps,
     return flips, y
 
 
-def run_stack(layers_np, q0, r, k, eps=1e-6, tol=1e-4, check_layers=None):
+def run_stack(layers_np, q0, r, k, eps=1e-6, tol=1e-4, check_layers=None, fn=None):
+    """fn: the decode entry point under test (spark_ffn_decode by default)."""
     layers = [tuple(to_dev(a) for a in lw) for lw in layers_np]
     q = torch.from_numpy(q0).to(DEV)
     d_ff = layers_np[0][2].shape[0]
-    y, tr = sf.spark_ffn_decode(q, layers, k, r, eps, trace=True)
+    y, tr = (fn or sf.spark_ffn_decode)(q, layers, k, r, eps, trace=True)
     torch.cuda.synchronize()
-    assert not sf.decode_workspace_failed(device=torch.device(DEV))
+    if fn is None:
+        assert not sf.decode_workspace_failed(device=torch.device(DEV))
     y = y.cpu().numpy()
     tr = {key: v.cpu().numpy() for key, v in tr.items()}
     T, L = tr["counts"].shape
