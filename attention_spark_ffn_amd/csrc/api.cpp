@@ -127,7 +127,8 @@ int spark_ffn_decode_batched_workspace_size(const spark_ffn_shape* s, int64_t B,
   if (B < 0) return SPARK_EINVAL;
   if (B > spark::kBatchMax || s->d_model > spark::kDecodeMaxDModel || s->d_ff > 65536) return SPARK_EUNSUPPORTED;
   const int64_t wide = s->r > s->d_model - s->r ? s->r : s->d_model - s->r;
-  if (B * wide * 4 > spark::kBatchMaxLds) return SPARK_EUNSUPPORTED;
+  const int64_t slots = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8;  // token slots of the kernels
+  if (slots * wide * 4 > spark::kBatchMaxLds) return SPARK_EUNSUPPORTED;
   *bytes = spark::decode_batched_workspace_bytes(s->d_model, s->d_ff, B > 0 ? B : 1);
   return SPARK_OK;
 }

@@ -19,12 +19,13 @@
 //   bgate: theta per token from all workgroups' (mean, M2) (two plain sums,
 //          fixed order), then per owned neuron the tokens that select it; the
 //          K2 row of a neuron selected by any token is read once and dotted
-//          with each selecting token's q[r:]; the neurons selected by any
-//          token are listed with their B gated values GELU(h - theta) * dot
-//          (0 for the tokens that do not select them);
-//   bv:    workgroup w owns a range of output columns; it walks every list
-//          entry, reads that neuron's V row segment once and accumulates it
-//          into the B outputs, then sums over threads in a fixed order.
+//          with each selecting token's q[r:]; it writes the B gated values
+//          GELU(h - theta) * dot of its neurons (0 for the tokens that do not
+//          select them) and the mask of its neurons selected by any token;
+//   bv:    workgroup w owns a range of output columns; its threads share out
+//          the union of the selected sets, read each union neuron's V row
+//          segment once and accumulate it into the B outputs, then sum over
+//          threads in a fixed order.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -44,9 +45,8 @@ struct BatchArgs {
   float* P;          // [G][B][2] per-workgroup (mean, M2) of the scores
   float* scale;      // [B] RMS scale of the layer input
   float* theta;      // [B]
-  int32_t* lcount;   // [G] entries of each workgroup's list
-  int32_t* lidx;     // [G][kBNeur] neurons selected by any token
-  float* lval;       // [G][kBNeur][B] their gated values
+  uint32_t* umask;   // [G] neurons of each workgroup selected by any token (bit j: neuron 32 g + j)
+  float* C;          // [d_ff][B] gated values (0 for a token that does not select the neuron), + kBatchMax pad
   float* yout;       // [B][d_model] layer output
 };
 
@@ -54,6 +54,50 @@ struct BatchArgs {
 __device__ __forceinline__ float half_sum(float v) {
   v = row16_sum(v);
   return v + __shfl_xor(v, 16, kWave);
+}
+
+// Columns [c0, c0 + n) of every token's input row (n a multiple of 4) into
+// LDS at dst[b * n + j], times scale[b] (scale null: unscaled); with ss, the
+// per-wave sums of squares of the whole rows (all d columns) into ss[wave][b].
+// Every load of a thread is issued before any is used.
+template <int BM>
+__device__ __forceinline__ void load_tokens(const float* __restrict__ yin, int B, int d, int c0, int n,
+                                            float* __restrict__ dst, const float* scale, float (*ss)[BM]) {
+  constexpr int KMAX = 3;  // 16-byte loads per thread and token per round
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int lo = ss ? 0 : c0, hi = ss ? d : c0 + n;  // columns read
+  for (int base = lo; base < hi; base += 4 * 256 * KMAX) {
+    f32x4 x[BM][KMAX];
+#pragma unroll
+    for (int b = 0; b < BM; ++b)
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        const int c = base + 4 * (tid + 256 * k);
+        if (b < B && c < hi) x[b][k] = *reinterpret_cast<const f32x4*>(yin + (size_t)b * d + c);
+      }
+#pragma unroll
+    for (int b = 0; b < BM; ++b) {
+      if (b >= B) continue;
+      const float s = scale ? scale[b] : 1.f;
+      float sq = 0.f;
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        const int c = base + 4 * (tid + 256 * k);
+        if (c < hi) {
+          const f32x4 v = x[b][k];
+          if (c >= c0 && c < c0 + n) {
+            const f32x4 w = {v.x * s, v.y * s, v.z * s, v.w * s};
+            *reinterpret_cast<f32x4*>(dst + (size_t)b * n + (c - c0)) = w;
+          }
+          sq += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+        }
+      }
+      if (ss) {
+        sq = wave_sum_dpp(sq);
+        if (lane == 0) ss[wv][b] += sq;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- bpred
@@ -67,17 +111,10 @@ __global__ __launch_bounds__(256) void bpred(const BatchArgs a) {
   const int B = a.B, d = a.d_model, r = a.r;
   const int n0 = blockIdx.x * kBNeur;
   // token inputs: q[:r] to LDS, sum of squares of the whole row
-  for (int b = 0; b < B; ++b) {
-    const float* y = a.yin + (size_t)b * d;
-    float ss = 0.f;
-    for (int c = 4 * tid; c < d; c += 4 * 256) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(y + c);
-      if (c < r) *reinterpret_cast<f32x4*>(qs + (size_t)b * r + c) = x;
-      ss += (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w);
-    }
-    ss = wave_sum_dpp(ss);
-    if (lane == 0) red[wv][b] = ss;
-  }
+  if (tid < 4 * BM) red[tid / BM][tid % BM] = 0.f;
+  for (int i = B * r + tid; i < BM * r; i += 256) qs[i] = 0.f;  // empty token slots
+  __syncthreads();
+  load_tokens<BM>(a.yin, B, d, 0, r, qs, nullptr, red);
   __syncthreads();
   float sc[BM];
 #pragma unroll
@@ -103,17 +140,33 @@ __global__ __launch_bounds__(256) void bpred(const BatchArgs a) {
   int nv[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) nv[u] = min(n0 + 4 * gi + u, a.d_ff - 1);  // rows past d_ff: read a valid row, not stored
-  for (int c = l32; c < CK; c += 32) {
-    float wf[4][CN];
+  // the chunks of a thread in rounds of kRound per neuron, all loads of a
+  // round issued before any is used
+  const f32x4* q4 = reinterpret_cast<const f32x4*>(qs);  // r is a multiple of 4
+  constexpr int kRound = 5;
+  for (int c0 = l32; c0 < CK; c0 += 32 * kRound) {
+    u32x4 raw[kRound][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) Chunk<W>::widen(load16(k1 + (size_t)nv[u] * rowb + (size_t)c * 16), wf[u]);
+    for (int k = 0; k < kRound; ++k)
 #pragma unroll
-    for (int b = 0; b < BM; ++b) {
-      if (b < B) {
+      for (int u = 0; u < 4; ++u) {
+        const int c = min(c0 + 32 * k, CK - 1);
+        raw[k][u] = load16(k1 + (size_t)nv[u] * rowb + (size_t)c * 16);
+      }
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) {
+      const int c = c0 + 32 * k;
+      if (c >= CK) break;
+      float wf[4][CN];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Chunk<W>::widen(raw[k][u], wf[u]);
+      // every token slot up to BM (slots past B hold zeros: no branches)
+#pragma unroll
+      for (int b = 0; b < BM; ++b) {
         float qv[CN];
 #pragma unroll
         for (int e4 = 0; e4 < CN / 4; ++e4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(qs + (size_t)b * r + c * CN + 4 * e4);
+          const f32x4 x = q4[(b * r + c * CN) / 4 + e4];
           qv[4 * e4] = x.x;
           qv[4 * e4 + 1] = x.y;
           qv[4 * e4 + 2] = x.z;
@@ -121,10 +174,10 @@ __global__ __launch_bounds__(256) void bpred(const BatchArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          float s = 0.f;
+          float sd = 0.f;
 #pragma unroll
-          for (int e = 0; e < CN; ++e) s += wf[u][e] * qv[e];
-          acc[u][b] += s;
+          for (int e = 0; e < CN; ++e) sd += wf[u][e] * qv[e];
+          acc[u][b] += sd;
         }
       }
     }
@@ -159,40 +212,52 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
   constexpr int CN = Chunk<W>::N;
   extern __shared__ float qs[];  // [B][d - r]: q[r:] of every token, scaled
   __shared__ float th[BM];
-  __shared__ float cs[BM][kBNeur];
-  __shared__ int sel[kBNeur];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ uint32_t sel[kBNeur];
+  const int tid = threadIdx.x, lane = tid & 63;
   const int B = a.B, d = a.d_model, r = a.r, rc = d - r;
   const int n0 = blockIdx.x * kBNeur, G = gridDim.x;
   // theta of every token: the mean over all d_ff scores, then their sum of
-  // squared deviations, from the per-workgroup (mean, M2) (fixed order)
-  for (int b = wv; b < B; b += 4) {
-    float s1 = 0.f;
-    for (int g = lane; g < G; g += 64) {
-      const float n = (float)min(kBNeur, a.d_ff - g * kBNeur);
-      s1 += n * a.P[((size_t)g * B + b) * 2];
+  // squared deviations, from the per-workgroup (mean, M2); token b is taken by
+  // the half-wave b (lanes over workgroups, fixed order), all loads first
+  {
+    const int b = tid >> 5, l32 = tid & 31;
+    constexpr int KG = 8;  // workgroups per lane and round, loads issued together
+    if (b < B) {
+      float s1 = 0.f;
+      for (int g0 = l32; g0 < G; g0 += 32 * KG) {
+        float mn[KG], nn[KG];
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+          const int g = g0 + 32 * k;
+          mn[k] = g < G ? a.P[((size_t)g * B + b) * 2] : 0.f;
+          nn[k] = g < G ? (float)min(kBNeur, a.d_ff - g * kBNeur) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < KG; ++k) s1 += nn[k] * mn[k];
+      }
+      const float mu = half_sum(s1) / (float)a.d_ff;
+      float s2 = 0.f;
+      for (int g0 = l32; g0 < G; g0 += 32 * KG) {
+        float mn[KG], m2v[KG], nn[KG];
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+          const int g = g0 + 32 * k;
+          mn[k] = g < G ? a.P[((size_t)g * B + b) * 2] : 0.f;
+          m2v[k] = g < G ? a.P[((size_t)g * B + b) * 2 + 1] : 0.f;
+          nn[k] = g < G ? (float)min(kBNeur, a.d_ff - g * kBNeur) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+          const float dm = mn[k] - mu;
+          s2 += nn[k] > 0.f ? m2v[k] + nn[k] * dm * dm : 0.f;
+        }
+      }
+      s2 = half_sum(s2);
+      if (l32 == 0) th[b] = mu + sqrtf(s2 / (float)a.d_ff) * a.z;
     }
-    const float mu = wave_sum_dpp(s1) / (float)a.d_ff;
-    float s2 = 0.f;
-    for (int g = lane; g < G; g += 64) {
-      const float n = (float)min(kBNeur, a.d_ff - g * kBNeur);
-      const float dm = a.P[((size_t)g * B + b) * 2] - mu;
-      s2 += a.P[((size_t)g * B + b) * 2 + 1] + n * dm * dm;
-    }
-    const float m2 = wave_sum_dpp(s2);
-    if (lane == 0) th[b] = mu + sqrtf(m2 / (float)a.d_ff) * a.z;
   }
-  for (int b = 0; b < B; ++b) {
-    const float s = a.scale[b];
-    for (int c = 4 * tid; c < rc; c += 4 * 256) {
-      f32x4 x = *reinterpret_cast<const f32x4*>(a.yin + (size_t)b * d + r + c);
-      x.x *= s;
-      x.y *= s;
-      x.z *= s;
-      x.w *= s;
-      *reinterpret_cast<f32x4*>(qs + (size_t)b * rc + c) = x;
-    }
-  }
+  for (int i = B * rc + tid; i < BM * rc; i += 256) qs[i] = 0.f;  // empty token slots
+  load_tokens<BM>(a.yin, B, d, r, rc, qs, a.scale, nullptr);
   __syncthreads();
   if (blockIdx.x == 0 && tid < B) a.theta[tid] = th[tid];
   // group gi: neurons n0 + 4 gi + u; the tokens selecting each, then one read
@@ -206,14 +271,16 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
   int nv[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int n = n0 + 4 * gi + u;
-    nv[u] = min(n, a.d_ff - 1);
+    nv[u] = min(n0 + 4 * gi + u, a.d_ff - 1);
+#pragma unroll
+    for (int b = 0; b < BM; ++b) hv[u][b] = (b < B) ? a.H[(size_t)b * a.d_ff + nv[u]] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
     sm[u] = 0;
 #pragma unroll
-    for (int b = 0; b < BM; ++b) {
-      hv[u][b] = (b < B) ? a.H[(size_t)b * a.d_ff + nv[u]] : 0.f;
-      sm[u] |= (b < B && n < a.d_ff && hv[u][b] > th[b]) ? 1u << b : 0u;
-    }
+    for (int b = 0; b < BM; ++b)
+      sm[u] |= (b < B && n0 + 4 * gi + u < a.d_ff && hv[u][b] > th[b]) ? 1u << b : 0u;
   }
   float acc[4][BM];
 #pragma unroll
@@ -222,18 +289,32 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
     for (int b = 0; b < BM; ++b) acc[u][b] = 0.f;
   const uint32_t any = sm[0] | sm[1] | sm[2] | sm[3];
   if (any) {
-    for (int c = l32; c < CK; c += 32) {
-      float wf[4][CN];
+    const f32x4* q4 = reinterpret_cast<const f32x4*>(qs);  // d - r is a multiple of 4
+    constexpr int kRound = 5;
+    for (int c0 = l32; c0 < CK; c0 += 32 * kRound) {
+      u32x4 raw[kRound][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (sm[u]) Chunk<W>::widen(load16(k2 + (size_t)nv[u] * rowb + (size_t)c * 16), wf[u]);
+      for (int k = 0; k < kRound; ++k)
 #pragma unroll
-      for (int b = 0; b < BM; ++b) {
-        if ((any >> b) & 1u) {
+        for (int u = 0; u < 4; ++u) {
+          raw[k][u] = u32x4{0u, 0u, 0u, 0u};
+          if (sm[u]) raw[k][u] = load16(k2 + (size_t)nv[u] * rowb + (size_t)min(c0 + 32 * k, CK - 1) * 16);
+        }
+#pragma unroll
+      for (int k = 0; k < kRound; ++k) {
+        const int c = c0 + 32 * k;
+        if (c >= CK) break;
+        float wf[4][CN];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Chunk<W>::widen(raw[k][u], wf[u]);
+        // every (neuron, token) pair of the group; unselected pairs are
+        // dropped at the end (no branches here; unread K2 rows are zeros)
+#pragma unroll
+        for (int b = 0; b < BM; ++b) {
           float qv[CN];
 #pragma unroll
           for (int e4 = 0; e4 < CN / 4; ++e4) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(qs + (size_t)b * rc + c * CN + 4 * e4);
+            const f32x4 x = q4[(b * rc + c * CN) / 4 + e4];
             qv[4 * e4] = x.x;
             qv[4 * e4 + 1] = x.y;
             qv[4 * e4 + 2] = x.z;
@@ -241,51 +322,68 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            if ((sm[u] >> b) & 1u) {
-              float s = 0.f;
+            float sd = 0.f;
 #pragma unroll
-              for (int e = 0; e < CN; ++e) s += wf[u][e] * qv[e];
-              acc[u][b] += s;
-            }
+            for (int e = 0; e < CN; ++e) sd += wf[u][e] * qv[e];
+            acc[u][b] += sd;
           }
         }
       }
     }
   }
+  // gated values of the owned neurons: C[n][b] (exact 0 for the tokens that
+  // do not select n); the union mask of the workgroup
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
+    const int n = n0 + 4 * gi + u;
 #pragma unroll
     for (int b = 0; b < BM; ++b) {
       const float t = half_sum(acc[u][b]);
-      if (l32 == 0 && b < B) cs[b][4 * gi + u] = ((sm[u] >> b) & 1u) ? gelu_tanh(hv[u][b] - th[b]) * t : 0.f;
+      if (l32 == 0 && b < B && n < a.d_ff)
+        a.C[(size_t)n * B + b] = ((sm[u] >> b) & 1u) ? gelu_tanh(hv[u][b] - th[b]) * t : 0.f;
     }
-    if (l32 == 0) sel[4 * gi + u] = (int)sm[u];
+    if (l32 == 0) sel[4 * gi + u] = sm[u];
   }
   __syncthreads();
-  // the workgroup's list: the neurons selected by any token, ascending
-  if (wv == 0) {
-    const bool on = lane < kBNeur && sel[lane < kBNeur ? lane : 0] != 0;
-    const uint64_t m = __builtin_amdgcn_ballot_w64(on);
-    const int pos = mbcnt64(m);
-    if (on) {
-      a.lidx[(size_t)blockIdx.x * kBNeur + pos] = n0 + lane;
-      for (int b = 0; b < B; ++b) a.lval[((size_t)blockIdx.x * kBNeur + pos) * B + b] = cs[b][lane];
-    }
-    if (lane == 0) a.lcount[blockIdx.x] = __builtin_popcountll(m);
+  if (tid < 64) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(lane < kBNeur && sel[lane < kBNeur ? lane : 0] != 0);
+    if (lane == 0) a.umask[blockIdx.x] = (uint32_t)m;
   }
 }
 
 // ---------------------------------------------------------------- bv
+// Index of the n-th set bit of w (n < popcount(w)).
+__device__ __forceinline__ int nth_bit(uint32_t w, int n) {
+  int pos = 0;
+#pragma unroll
+  for (int sft = 16; sft >= 1; sft >>= 1) {
+    const int c = __builtin_popcount(w & ((1u << sft) - 1u));
+    if (n >= c) {
+      n -= c;
+      w >>= sft;
+      pos += sft;
+    }
+  }
+  return pos;
+}
+
 // Workgroup w owns the 16-byte column chunks [w NCH, (w + 1) NCH) of the
-// output.  Thread t walks the lists of workgroups t, t + 256, ... of bgate
-// and accumulates its share of each token's columns; the shares are summed
-// over lanes (transposing reduction) and waves in a fixed order.
+// output.  The union of the selected sets (bgate's masks, prefix counts in
+// LDS) is dealt round-robin to the threads: thread t takes the union neurons
+// t, t + 256, ... in ascending order, kBvRound at a time with all their loads
+// (the B gated values and the V row chunks) issued before any is used; the
+// per-thread sums are then added over lanes (transposing reduction) and waves
+// in a fixed order.
+constexpr int kBvRound = 4;
 template <typename W, int BM, int NCH>
 __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   constexpr int CN = Chunk<W>::N;
   constexpr int NV = BM * NCH * CN;  // accumulators per thread: token-major, then column
   static_assert(NV <= 64 && (NV & (NV - 1)) == 0, "one transposing reduction of at most 64 columns");
   __shared__ float part[4][NV];
+  __shared__ uint32_t um[2048];
+  __shared__ int pre[2049];
+  __shared__ int wtot[4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int B = a.B, d = a.d_model;
   const int nchunks = d / CN;
@@ -293,45 +391,82 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   const int nch = min(NCH, nchunks - ch0);
   const size_t rowb = (size_t)d * sizeof(W);
   const char* vb = (const char*)a.v + (size_t)ch0 * 16;
+  // union masks and their exclusive prefix counts (thread t: words 8t .. 8t+7)
+  int cnt8 = 0;
+  uint32_t w8[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int g = 8 * tid + k;
+    w8[k] = g < G2 ? a.umask[g] : 0u;
+    cnt8 += __builtin_popcount(w8[k]);
+  }
+  const int incl = wave_incl_scan_dpp(cnt8);
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  int run = incl - cnt8;
+  for (int w2 = 0; w2 < wv; ++w2) run += wtot[w2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int g = 8 * tid + k;
+    if (g < 2048) {
+      um[g] = w8[k];
+      pre[g] = run;
+    }
+    run += __builtin_popcount(w8[k]);
+  }
+  if (tid == 255) pre[2048] = run;
+  __syncthreads();
+  const int U = pre[2048];
   float acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-  for (int g = tid; g < G2; g += 256) {
-    const int cnt = a.lcount[g];
-    for (int e0 = 0; e0 < cnt; e0 += 4) {
-      u32x4 raw[4][NCH];
-      int n[4];
+  for (int e0 = tid; e0 < U; e0 += 256 * kBvRound) {
+    int n[kBvRound];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) n[k] = e0 + k < cnt ? a.lidx[(size_t)g * kBNeur + e0 + k] : -1;
+    for (int k = 0; k < kBvRound; ++k) {
+      const int e = e0 + 256 * k;
+      n[k] = -1;
+      if (e < U) {
+        int lo = 0, hi = G2 - 1;  // last workgroup g with pre[g] <= e
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= e) lo = mid; else hi = mid - 1;
+        }
+        n[k] = lo * kBNeur + nth_bit(um[lo], e - pre[lo]);
+      }
+    }
+    float cv[kBvRound][BM];
+    u32x4 raw[kBvRound][NCH];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < kBvRound; ++k) {
+      if (n[k] < 0) continue;
 #pragma unroll
-        for (int hh = 0; hh < NCH; ++hh)
-          if (n[k] >= 0 && hh < nch) raw[k][hh] = load16(vb + (size_t)n[k] * rowb + hh * 16);
+      for (int b = 0; b < BM; ++b) cv[k][b] = a.C[(size_t)n[k] * B + b];  // row padded to kBatchMax
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (n[k] < 0) continue;
-        const float* val = a.lval + ((size_t)g * kBNeur + e0 + k) * B;
+      for (int hh = 0; hh < NCH; ++hh)
+        if (hh < nch) raw[k][hh] = load16(vb + (size_t)n[k] * rowb + hh * 16);
+    }
 #pragma unroll
-        for (int hh = 0; hh < NCH; ++hh) {
-          if (hh >= nch) continue;
-          float wf[CN];
-          Chunk<W>::widen(raw[k][hh], wf);
+    for (int k = 0; k < kBvRound; ++k) {
+      if (n[k] < 0) continue;
 #pragma unroll
-          for (int b = 0; b < BM; ++b) {
-            if (b < B) {
-              const float c = val[b];
+      for (int hh = 0; hh < NCH; ++hh) {
+        if (hh >= nch) continue;
+        float wf[CN];
+        Chunk<W>::widen(raw[k][hh], wf);
 #pragma unroll
-              for (int i = 0; i < CN; ++i) acc[(b * NCH + hh) * CN + i] += c * wf[i];
-            }
+        for (int b = 0; b < BM; ++b) {
+          if (b < B) {
+#pragma unroll
+            for (int i = 0; i < CN; ++i) acc[(b * NCH + hh) * CN + i] += cv[k][b] * wf[i];
           }
         }
       }
     }
   }
   int col;
-  const float s = wave_colsum<NV>(acc, lane, col);
-  if ((lane & (64 / NV - 1)) == 0) part[wv][col] = s;
+  const float sum = wave_colsum<NV>(acc, lane, col);
+  if ((lane & (64 / NV - 1)) == 0) part[wv][col] = sum;
   __syncthreads();
   if (tid < NV) {
     const int b = tid / (NCH * CN), rem = tid % (NCH * CN);
@@ -385,7 +520,7 @@ __global__ __launch_bounds__(256) void btrace(const BatchArgs a, int32_t* counts
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct BatchLayout {
-  size_t H, P, scale, theta, lcount, lidx, lval, ybuf, total;
+  size_t H, P, scale, theta, umask, C, ybuf, total;
 };
 
 static BatchLayout batch_layout(int64_t d_model, int64_t d_ff, int64_t B) {
@@ -401,9 +536,8 @@ static BatchLayout batch_layout(int64_t d_model, int64_t d_ff, int64_t B) {
   L.P = take((size_t)G * B * 2 * 4);
   L.scale = take((size_t)B * 4);
   L.theta = take((size_t)B * 4);
-  L.lcount = take((size_t)G * 4);
-  L.lidx = take((size_t)G * kBNeur * 4);
-  L.lval = take((size_t)G * kBNeur * B * 4);
+  L.umask = take((size_t)G * 4);
+  L.C = take(((size_t)d_ff * B + kBatchMax) * 4);
   L.ybuf = take((size_t)B * d_model * 4);
   L.total = off;
   return L;
@@ -425,8 +559,9 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
   const int G = (int)((s.d_ff + kBNeur - 1) / kBNeur);
   const int nchunks = (int)(s.d_model / CN);
   const int G3 = (nchunks + NCH - 1) / NCH;
-  // (the entry point keeps both at most kBatchMaxLds bytes)
-  const size_t lds1 = (size_t)B * s.r * 4, lds2 = (size_t)B * (s.d_model - s.r) * 4;
+  // (BM token slots; the entry point keeps BM x max(r, d - r) x 4 within
+  // kBatchMaxLds)
+  const size_t lds1 = (size_t)BM * s.r * 4, lds2 = (size_t)BM * (s.d_model - s.r) * 4;
   hipError_t e = hipSuccess;
   BatchArgs a;
   a.d_model = (int)s.d_model;
@@ -439,9 +574,8 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
   a.P = (float*)(base + Lo.P);
   a.scale = (float*)(base + Lo.scale);
   a.theta = (float*)(base + Lo.theta);
-  a.lcount = (int32_t*)(base + Lo.lcount);
-  a.lidx = (int32_t*)(base + Lo.lidx);
-  a.lval = (float*)(base + Lo.lval);
+  a.umask = (uint32_t*)(base + Lo.umask);
+  a.C = (float*)(base + Lo.C);
   float* ybuf = (float*)(base + Lo.ybuf);
   for (int l = 0; l < n_layers; ++l) {
     a.k1t = layers[l].k1t;

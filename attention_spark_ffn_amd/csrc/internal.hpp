@@ -29,7 +29,7 @@ hipError_t launch_decode(const spark_ffn_shape& s, const spark_ffn_weights* laye
 
 // ---------------------------------------------------------------- batched decode
 constexpr int kBatchMax = 8;          // tokens per batch
-constexpr int kBatchMaxLds = 65536;   // bytes of q held in LDS per kernel (B x max(r, d_model - r) x 4)
+constexpr int kBatchMaxLds = 65536;   // bytes of q held in LDS per kernel (slots x max(r, d_model - r) x 4)
 size_t decode_batched_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t B);
 hipError_t launch_decode_batched(const spark_ffn_shape& s, const spark_ffn_weights* layers, int n_layers,
                                  const float* q, int64_t B, float* y, float eps, double z,

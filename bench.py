@@ -113,6 +113,26 @@ def _oracle_rate(fn, n_units: int, unit: str, sample: str) -> dict:
             "sample": f"{sample}, {dt:.1f} s"}
 
 
+def batched_decode(torch, sf, layers, qs):
+    """The same 26-layer stack decoded B tokens at a time (one K1 read per
+    layer for the batch; K2 and V rows read once per union of the selected
+    sets), for B in 1, 4, 8.  Algorithmic bytes per call: per layer K1, the
+    union's K2 and V rows, the fp32 input and output vectors of the batch."""
+    res = {}
+    for B in (1, 4, 8):
+        q = qs[:B].contiguous()
+        ms = _time_ms(torch, lambda: sf.spark_ffn_decode_batched(q, layers, K, R), reps=20)
+        _, tr = sf.spark_ffn_decode_batched(q, layers, K, R, trace=True)
+        idx, cnt = tr["idx"].cpu().numpy(), tr["counts"].cpu().numpy()
+        union = [len(set().union(*[set(idx[b, l, :cnt[b, l]].tolist()) for b in range(B)])) for l in range(LAYERS)]
+        moved = sum(R * D_FF * 2 + u * ((D_MODEL - R) * 2 + D_MODEL * 2) + 2 * B * D_MODEL * 4 for u in union)
+        res[str(B)] = {"ms_per_call": ms, "tokens_per_s": B / ms * 1e3, "mean_union_per_layer": float(np.mean(union)),
+                       "algorithmic_bytes_per_call": float(moved),
+                       "roofline": {"bound": "hbm", "achieved": moved / ms / 1e6, "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": moved / ms / 1e6 / HBM_PEAK_GBS}}
+    return {"workload": "spark_ffn_decode_batched: the 26-layer decode stack, B tokens per call", "batch": res}
+
+
 def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
     """The other workloads of the hot path, each timed on its own, with its
     roofline and (with_cpu) the oracle timed on a bounded sample."""
@@ -327,9 +347,11 @@ def main():
         "kernel_failed": bool(failed),
     }
     if not args.no_extra:
+        bd = batched_decode(torch, sf, layers, qs)
         del layers, qs
         torch.cuda.empty_cache()
         out["extra"] = extra_workloads(torch, sf, synth, dev, args.seed, not args.no_cpu)
+        out["extra"]["decode_batched"] = bd
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layers_np)
     print(json.dumps(out), flush=True)

@@ -126,7 +126,8 @@ int spark_ffn_decode(const spark_ffn_shape *s, const spark_ffn_weights *layers, 
  * when a trace is asked for); results equal spark_ffn_decode's up to the
  * order of fp32 sums.
  * Requires 0 <= B <= 8, d_model <= 8192, d_ff <= 65536,
- * B * max(r, d_model - r) * 4 <= 65536, q and y 16-byte aligned, and the
+ * P * max(r, d_model - r) * 4 <= 65536 with P = B rounded up to a power of
+ * two (the token slots of the kernels), q and y 16-byte aligned, and the
  * weight conditions of spark_ffn_decode.  The workspace needs no clearing.
  */
 int spark_ffn_decode_batched(const spark_ffn_shape *s, const spark_ffn_weights *layers, int n_layers,
