@@ -46,7 +46,7 @@ struct BatchArgs {
   float* scale;      // [B] RMS scale of the layer input
   float* theta;      // [B]
   uint32_t* umask;   // [G] neurons of each workgroup selected by any token (bit j: neuron 32 g + j)
-  float* C;          // [d_ff][B] gated values (0 for a token that does not select the neuron), + kBatchMax pad
+  float* C;          // [d_ff][BM] gated values (0 for a token that does not select the neuron; slots >= B unused)
   float* yout;       // [B][d_model] layer output
 };
 
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
     for (int b = 0; b < BM; ++b) {
       const float t = half_sum(acc[u][b]);
       if (l32 == 0 && b < B && n < a.d_ff)
-        a.C[(size_t)n * B + b] = ((sm[u] >> b) & 1u) ? gelu_tanh(hv[u][b] - th[b]) * t : 0.f;
+        a.C[(size_t)n * BM + b] = ((sm[u] >> b) & 1u) ? gelu_tanh(hv[u][b] - th[b]) * t : 0.f;
     }
     if (l32 == 0) sel[4 * gi + u] = sm[u];
   }
@@ -352,29 +352,13 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
 }
 
 // ---------------------------------------------------------------- bv
-// Index of the n-th set bit of w (n < popcount(w)).
-__device__ __forceinline__ int nth_bit(uint32_t w, int n) {
-  int pos = 0;
-#pragma unroll
-  for (int sft = 16; sft >= 1; sft >>= 1) {
-    const int c = __builtin_popcount(w & ((1u << sft) - 1u));
-    if (n >= c) {
-      n -= c;
-      w >>= sft;
-      pos += sft;
-    }
-  }
-  return pos;
-}
-
 // Workgroup w owns the 16-byte column chunks [w NCH, (w + 1) NCH) of the
 // output.  The union of the selected sets (bgate's masks, prefix counts in
-// LDS) is dealt round-robin to the threads: thread t takes the union neurons
-// t, t + 256, ... in ascending order, kBvRound at a time with all their loads
-// (the B gated values and the V row chunks) issued before any is used; the
-// per-thread sums are then added over lanes (transposing reduction) and waves
-// in a fixed order.
-constexpr int kBvRound = 4;
+// LDS) is split into 256 contiguous runs, one per thread, each walked
+// kBvRound neurons at a time with all their loads (the gated values and the
+// V row chunks) issued before any is used; the per-thread sums are then added
+// over lanes (transposing reduction) and waves in a fixed order.
+constexpr int kBvRound = 8;
 template <typename W, int BM, int NCH>
 __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   constexpr int CN = Chunk<W>::N;
@@ -387,7 +371,12 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int B = a.B, d = a.d_model;
   const int nchunks = d / CN;
-  const int ch0 = blockIdx.x * NCH;
+  // column owner index: the workgroups of one XCD (w = x + 8 j, dealt
+  // round-robin) own one contiguous run of chunks, so each cache line of a V
+  // row is fetched by one XCD
+  const int G3 = gridDim.x;
+  const int o = (G3 % 8 == 0) ? (blockIdx.x & 7) * (G3 / 8) + (blockIdx.x >> 3) : blockIdx.x;
+  const int ch0 = o * NCH;
   const int nch = min(NCH, nchunks - ch0);
   const size_t rowb = (size_t)d * sizeof(W);
   const char* vb = (const char*)a.v + (size_t)ch0 * 16;
@@ -420,28 +409,44 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   float acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-  for (int e0 = tid; e0 < U; e0 += 256 * kBvRound) {
+  // thread t takes the union entries [t U / 256, (t + 1) U / 256): one search
+  // for the first, then a walk along the set bits of the masks
+  const int e_begin = (int)((int64_t)tid * U / 256), e_end = (int)((int64_t)(tid + 1) * U / 256);
+  int g = 0;
+  uint32_t wbits = 0;
+  if (e_begin < e_end) {
+    int lo = 0, hi = G2 - 1;  // last workgroup g with pre[g] <= e_begin
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= e_begin) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    wbits = um[g];
+    for (int k = e_begin - pre[g]; k > 0; --k) wbits &= wbits - 1;  // drop the entries before e_begin
+  }
+  for (int e0 = e_begin; e0 < e_end; e0 += kBvRound) {
     int n[kBvRound];
 #pragma unroll
     for (int k = 0; k < kBvRound; ++k) {
-      const int e = e0 + 256 * k;
       n[k] = -1;
-      if (e < U) {
-        int lo = 0, hi = G2 - 1;  // last workgroup g with pre[g] <= e
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (pre[mid] <= e) lo = mid; else hi = mid - 1;
-        }
-        n[k] = lo * kBNeur + nth_bit(um[lo], e - pre[lo]);
+      if (e0 + k < e_end) {
+        while (wbits == 0) wbits = um[++g];
+        n[k] = g * kBNeur + __builtin_ctz(wbits);
+        wbits &= wbits - 1;
       }
     }
-    float cv[kBvRound][BM];
+    f32x4 cv[kBvRound][(BM + 3) / 4];
     u32x4 raw[kBvRound][NCH];
 #pragma unroll
     for (int k = 0; k < kBvRound; ++k) {
       if (n[k] < 0) continue;
+      if (BM >= 4) {
 #pragma unroll
-      for (int b = 0; b < BM; ++b) cv[k][b] = a.C[(size_t)n[k] * B + b];  // row padded to kBatchMax
+        for (int j = 0; j < BM / 4; ++j) cv[k][j] = reinterpret_cast<const f32x4*>(a.C + (size_t)n[k] * BM)[j];
+      } else {
+#pragma unroll
+        for (int b = 0; b < BM; ++b) cv[k][0][b] = a.C[(size_t)n[k] * BM + b];
+      }
 #pragma unroll
       for (int hh = 0; hh < NCH; ++hh)
         if (hh < nch) raw[k][hh] = load16(vb + (size_t)n[k] * rowb + hh * 16);
@@ -456,10 +461,9 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
         Chunk<W>::widen(raw[k][hh], wf);
 #pragma unroll
         for (int b = 0; b < BM; ++b) {
-          if (b < B) {
+          const float c = cv[k][b / 4][b % 4];
 #pragma unroll
-            for (int i = 0; i < CN; ++i) acc[(b * NCH + hh) * CN + i] += cv[k][b] * wf[i];
-          }
+          for (int i = 0; i < CN; ++i) acc[(b * NCH + hh) * CN + i] += c * wf[i];
         }
       }
     }
@@ -537,7 +541,7 @@ static BatchLayout batch_layout(int64_t d_model, int64_t d_ff, int64_t B) {
   L.scale = take((size_t)B * 4);
   L.theta = take((size_t)B * 4);
   L.umask = take((size_t)G * 4);
-  L.C = take(((size_t)d_ff * B + kBatchMax) * 4);
+  L.C = take((size_t)d_ff * kBatchMax * 4);
   L.ybuf = take((size_t)B * d_model * 4);
   L.total = off;
   return L;
