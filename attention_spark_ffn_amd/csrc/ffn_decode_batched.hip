@@ -31,7 +31,11 @@
 
 namespace spark {
 
-constexpr int kBNeur = 32;  // neurons per workgroup of bpred and bgate (eight groups of four)
+constexpr int kBSlots = 40;    // neurons per workgroup of bpred and bgate at most (ten groups of four)
+constexpr int kBThreads = 320;  // threads of bpred and bgate: ten half-waves
+
+// First neuron of workgroup g of G (the G workgroups split d_ff evenly).
+__device__ __forceinline__ int nfirst(int g, int d_ff, int G) { return (int)((int64_t)g * d_ff / G); }
 
 struct BatchArgs {
   const void* k1t;
@@ -45,7 +49,7 @@ struct BatchArgs {
   float* P;          // [G][B][2] per-workgroup (mean, M2) of the scores
   float* scale;      // [B] RMS scale of the layer input
   float* theta;      // [B]
-  uint32_t* umask;   // [G] neurons of each workgroup selected by any token (bit j: neuron 32 g + j)
+  uint64_t* umask;   // [G] neurons of each workgroup selected by any token (bit j: its neuron j)
   float* C;          // [d_ff][BM] gated values (0 for a token that does not select the neuron; slots >= B unused)
   float* yout;       // [B][d_model] layer output
 };
@@ -60,19 +64,19 @@ __device__ __forceinline__ float half_sum(float v) {
 // LDS at dst[b * n + j], times scale[b] (scale null: unscaled); with ss, the
 // per-wave sums of squares of the whole rows (all d columns) into ss[wave][b].
 // Every load of a thread is issued before any is used.
-template <int BM>
+template <int BM, int NT>
 __device__ __forceinline__ void load_tokens(const float* __restrict__ yin, int B, int d, int c0, int n,
                                             float* __restrict__ dst, const float* scale, float (*ss)[BM]) {
   constexpr int KMAX = 3;  // 16-byte loads per thread and token per round
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lo = ss ? 0 : c0, hi = ss ? d : c0 + n;  // columns read
-  for (int base = lo; base < hi; base += 4 * 256 * KMAX) {
+  for (int base = lo; base < hi; base += 4 * NT * KMAX) {
     f32x4 x[BM][KMAX];
 #pragma unroll
     for (int b = 0; b < BM; ++b)
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
-        const int c = base + 4 * (tid + 256 * k);
+        const int c = base + 4 * (tid + NT * k);
         if (b < B && c < hi) x[b][k] = *reinterpret_cast<const f32x4*>(yin + (size_t)b * d + c);
       }
 #pragma unroll
@@ -82,7 +86,7 @@ __device__ __forceinline__ void load_tokens(const float* __restrict__ yin, int B
       float sq = 0.f;
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
-        const int c = base + 4 * (tid + 256 * k);
+        const int c = base + 4 * (tid + NT * k);
         if (c < hi) {
           const f32x4 v = x[b][k];
           if (c >= c0 && c < c0 + n) {
@@ -102,25 +106,25 @@ __device__ __forceinline__ void load_tokens(const float* __restrict__ yin, int B
 
 // ---------------------------------------------------------------- bpred
 template <typename W, int BM>
-__global__ __launch_bounds__(256) void bpred(const BatchArgs a) {
+__global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
   constexpr int CN = Chunk<W>::N;
   extern __shared__ float qs[];  // [B][r]: q[:r] of every token (unscaled)
-  __shared__ float red[4][BM];
-  __shared__ float hs[BM][kBNeur];
+  __shared__ float red[kBThreads / 64][BM];
+  __shared__ float hs[BM][kBSlots];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int B = a.B, d = a.d_model, r = a.r;
-  const int n0 = blockIdx.x * kBNeur;
+  const int n0 = nfirst(blockIdx.x, a.d_ff, gridDim.x), n1 = nfirst(blockIdx.x + 1, a.d_ff, gridDim.x);
   // token inputs: q[:r] to LDS, sum of squares of the whole row
-  if (tid < 4 * BM) red[tid / BM][tid % BM] = 0.f;
-  for (int i = B * r + tid; i < BM * r; i += 256) qs[i] = 0.f;  // empty token slots
+  if (tid < (kBThreads / 64) * BM) red[tid / BM][tid % BM] = 0.f;
+  for (int i = B * r + tid; i < BM * r; i += kBThreads) qs[i] = 0.f;  // empty token slots
   __syncthreads();
-  load_tokens<BM>(a.yin, B, d, 0, r, qs, nullptr, red);
+  load_tokens<BM, kBThreads>(a.yin, B, d, 0, r, qs, nullptr, red);
   __syncthreads();
   float sc[BM];
 #pragma unroll
   for (int b = 0; b < BM; ++b)
     sc[b] = (b < B && a.prenorm)
-                ? 1.f / sqrtf((((red[0][b] + red[1][b]) + red[2][b]) + red[3][b]) / (float)d + a.eps)
+                ? 1.f / sqrtf(((((red[0][b] + red[1][b]) + red[2][b]) + red[3][b]) + red[4][b]) / (float)d + a.eps)
                 : 1.f;
   if (blockIdx.x == 0 && tid == 0)
 #pragma unroll
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(256) void bpred(const BatchArgs a) {
   const char* k1 = (const char*)a.k1t;
   int nv[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) nv[u] = min(n0 + 4 * gi + u, a.d_ff - 1);  // rows past d_ff: read a valid row, not stored
+  for (int u = 0; u < 4; ++u) nv[u] = min(n0 + 4 * gi + u, n1 - 1);  // slots past the range: a valid row, not stored
   // the chunks of a thread in rounds of kRound per neuron, all loads of a
   // round issued before any is used
   const f32x4* q4 = reinterpret_cast<const f32x4*>(qs);  // r is a multiple of 4
@@ -191,8 +195,8 @@ __global__ __launch_bounds__(256) void bpred(const BatchArgs a) {
     }
   __syncthreads();
   // scores out, and each token's (mean, M2) over the owned neurons
-  const int nown = min(kBNeur, a.d_ff - n0);
-  for (int b = wv; b < B; b += 4) {
+  const int nown = n1 - n0;  // at most kBSlots
+  for (int b = wv; b < B; b += kBThreads / 64) {
     const bool own = lane < nown;
     const float h = own ? hs[b][lane] : 0.f;
     if (own) a.H[(size_t)b * a.d_ff + n0 + lane] = h;
@@ -208,14 +212,15 @@ __global__ __launch_bounds__(256) void bpred(const BatchArgs a) {
 
 // ---------------------------------------------------------------- bgate
 template <typename W, int BM>
-__global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
+__global__ __launch_bounds__(kBThreads) void bgate(const BatchArgs a) {
   constexpr int CN = Chunk<W>::N;
   extern __shared__ float qs[];  // [B][d - r]: q[r:] of every token, scaled
   __shared__ float th[BM];
-  __shared__ uint32_t sel[kBNeur];
+  __shared__ uint32_t sel[kBSlots];
   const int tid = threadIdx.x, lane = tid & 63;
   const int B = a.B, d = a.d_model, r = a.r, rc = d - r;
-  const int n0 = blockIdx.x * kBNeur, G = gridDim.x;
+  const int G = gridDim.x;
+  const int n0 = nfirst(blockIdx.x, a.d_ff, G), n1 = nfirst(blockIdx.x + 1, a.d_ff, G);
   // theta of every token: the mean over all d_ff scores, then their sum of
   // squared deviations, from the per-workgroup (mean, M2); token b is taken by
   // the half-wave b (lanes over workgroups, fixed order), all loads first
@@ -230,7 +235,7 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
         for (int k = 0; k < KG; ++k) {
           const int g = g0 + 32 * k;
           mn[k] = g < G ? a.P[((size_t)g * B + b) * 2] : 0.f;
-          nn[k] = g < G ? (float)min(kBNeur, a.d_ff - g * kBNeur) : 0.f;
+          nn[k] = g < G ? (float)(nfirst(g + 1, a.d_ff, G) - nfirst(g, a.d_ff, G)) : 0.f;
         }
 #pragma unroll
         for (int k = 0; k < KG; ++k) s1 += nn[k] * mn[k];
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
           const int g = g0 + 32 * k;
           mn[k] = g < G ? a.P[((size_t)g * B + b) * 2] : 0.f;
           m2v[k] = g < G ? a.P[((size_t)g * B + b) * 2 + 1] : 0.f;
-          nn[k] = g < G ? (float)min(kBNeur, a.d_ff - g * kBNeur) : 0.f;
+          nn[k] = g < G ? (float)(nfirst(g + 1, a.d_ff, G) - nfirst(g, a.d_ff, G)) : 0.f;
         }
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
@@ -256,8 +261,8 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
       if (l32 == 0) th[b] = mu + sqrtf(s2 / (float)a.d_ff) * a.z;
     }
   }
-  for (int i = B * rc + tid; i < BM * rc; i += 256) qs[i] = 0.f;  // empty token slots
-  load_tokens<BM>(a.yin, B, d, r, rc, qs, a.scale, nullptr);
+  for (int i = B * rc + tid; i < BM * rc; i += kBThreads) qs[i] = 0.f;  // empty token slots
+  load_tokens<BM, kBThreads>(a.yin, B, d, r, rc, qs, a.scale, nullptr);
   __syncthreads();
   if (blockIdx.x == 0 && tid < B) a.theta[tid] = th[tid];
   // group gi: neurons n0 + 4 gi + u; the tokens selecting each, then one read
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
   int nv[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    nv[u] = min(n0 + 4 * gi + u, a.d_ff - 1);
+    nv[u] = min(n0 + 4 * gi + u, n1 - 1);
 #pragma unroll
     for (int b = 0; b < BM; ++b) hv[u][b] = (b < B) ? a.H[(size_t)b * a.d_ff + nv[u]] : 0.f;
   }
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
     sm[u] = 0;
 #pragma unroll
     for (int b = 0; b < BM; ++b)
-      sm[u] |= (b < B && n0 + 4 * gi + u < a.d_ff && hv[u][b] > th[b]) ? 1u << b : 0u;
+      sm[u] |= (b < B && n0 + 4 * gi + u < n1 && hv[u][b] > th[b]) ? 1u << b : 0u;
   }
   float acc[4][BM];
 #pragma unroll
@@ -339,15 +344,15 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
 #pragma unroll
     for (int b = 0; b < BM; ++b) {
       const float t = half_sum(acc[u][b]);
-      if (l32 == 0 && b < B && n < a.d_ff)
+      if (l32 == 0 && b < B && n < n1)
         a.C[(size_t)n * BM + b] = ((sm[u] >> b) & 1u) ? gelu_tanh(hv[u][b] - th[b]) * t : 0.f;
     }
     if (l32 == 0) sel[4 * gi + u] = sm[u];
   }
   __syncthreads();
   if (tid < 64) {
-    const uint64_t m = __builtin_amdgcn_ballot_w64(lane < kBNeur && sel[lane < kBNeur ? lane : 0] != 0);
-    if (lane == 0) a.umask[blockIdx.x] = (uint32_t)m;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(lane < kBSlots && sel[lane < kBSlots ? lane : 0] != 0);
+    if (lane == 0) a.umask[blockIdx.x] = m;
   }
 }
 
@@ -358,14 +363,15 @@ __global__ __launch_bounds__(256) void bgate(const BatchArgs a) {
 // kBvRound neurons at a time with all their loads (the gated values and the
 // V row chunks) issued before any is used; the per-thread sums are then added
 // over lanes (transposing reduction) and waves in a fixed order.
-constexpr int kBvRound = 8;
-template <typename W, int BM, int NCH>
+template <typename W, int BM>
 __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   constexpr int CN = Chunk<W>::N;
-  constexpr int NV = BM * NCH * CN;  // accumulators per thread: token-major, then column
-  static_assert(NV <= 64 && (NV & (NV - 1)) == 0, "one transposing reduction of at most 64 columns");
-  __shared__ float part[4][NV];
-  __shared__ uint32_t um[2048];
+  constexpr int kBvRound = BM >= 8 ? 4 : 8;  // union neurons per round of loads
+  constexpr int NCH = 2;             // output chunks per workgroup at most
+  constexpr int NV1 = BM * CN;       // accumulators per thread and chunk: token-major, then column
+  static_assert(NV1 <= 64 && (NV1 & (NV1 - 1)) == 0, "one transposing reduction of at most 64 columns per chunk");
+  __shared__ float part[4][NCH][NV1];
+  __shared__ uint64_t um[2048];
   __shared__ int pre[2049];
   __shared__ int wtot[4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -374,20 +380,20 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   // column owner index: the workgroups of one XCD (w = x + 8 j, dealt
   // round-robin) own one contiguous run of chunks, so each cache line of a V
   // row is fetched by one XCD
-  const int G3 = gridDim.x;
+  const int G3 = gridDim.x;  // at least nchunks / 2: one or two chunks each
   const int o = (G3 % 8 == 0) ? (blockIdx.x & 7) * (G3 / 8) + (blockIdx.x >> 3) : blockIdx.x;
-  const int ch0 = o * NCH;
-  const int nch = min(NCH, nchunks - ch0);
+  const int ch0 = (int)((int64_t)o * nchunks / G3);
+  const int nch = (int)((int64_t)(o + 1) * nchunks / G3) - ch0;
   const size_t rowb = (size_t)d * sizeof(W);
   const char* vb = (const char*)a.v + (size_t)ch0 * 16;
   // union masks and their exclusive prefix counts (thread t: words 8t .. 8t+7)
   int cnt8 = 0;
-  uint32_t w8[8];
+  uint64_t w8[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int g = 8 * tid + k;
-    w8[k] = g < G2 ? a.umask[g] : 0u;
-    cnt8 += __builtin_popcount(w8[k]);
+    w8[k] = g < G2 ? a.umask[g] : 0ull;
+    cnt8 += __builtin_popcountll(w8[k]);
   }
   const int incl = wave_incl_scan_dpp(cnt8);
   if (lane == 63) wtot[wv] = incl;
@@ -401,19 +407,21 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
       um[g] = w8[k];
       pre[g] = run;
     }
-    run += __builtin_popcount(w8[k]);
+    run += __builtin_popcountll(w8[k]);
   }
   if (tid == 255) pre[2048] = run;
   __syncthreads();
   const int U = pre[2048];
-  float acc[NV];
+  float acc[NCH][NV1];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+  for (int hh = 0; hh < NCH; ++hh)
+#pragma unroll
+    for (int i = 0; i < NV1; ++i) acc[hh][i] = 0.f;
   // thread t takes the union entries [t U / 256, (t + 1) U / 256): one search
   // for the first, then a walk along the set bits of the masks
   const int e_begin = (int)((int64_t)tid * U / 256), e_end = (int)((int64_t)(tid + 1) * U / 256);
   int g = 0;
-  uint32_t wbits = 0;
+  uint64_t wbits = 0;
   if (e_begin < e_end) {
     int lo = 0, hi = G2 - 1;  // last workgroup g with pre[g] <= e_begin
     while (lo < hi) {
@@ -431,7 +439,7 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
       n[k] = -1;
       if (e0 + k < e_end) {
         while (wbits == 0) wbits = um[++g];
-        n[k] = g * kBNeur + __builtin_ctz(wbits);
+        n[k] = nfirst(g, a.d_ff, G2) + __builtin_ctzll(wbits);
         wbits &= wbits - 1;
       }
     }
@@ -463,20 +471,22 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
         for (int b = 0; b < BM; ++b) {
           const float c = cv[k][b / 4][b % 4];
 #pragma unroll
-          for (int i = 0; i < CN; ++i) acc[(b * NCH + hh) * CN + i] += c * wf[i];
+          for (int i = 0; i < CN; ++i) acc[hh][b * CN + i] += c * wf[i];
         }
       }
     }
   }
-  int col;
-  const float sum = wave_colsum<NV>(acc, lane, col);
-  if ((lane & (64 / NV - 1)) == 0) part[wv][col] = sum;
+#pragma unroll
+  for (int hh = 0; hh < NCH; ++hh) {
+    int col;
+    const float sum = wave_colsum<NV1>(acc[hh], lane, col);
+    if ((lane & (64 / NV1 - 1)) == 0) part[wv][hh][col] = sum;
+  }
   __syncthreads();
-  if (tid < NV) {
-    const int b = tid / (NCH * CN), rem = tid % (NCH * CN);
-    const int hh = rem / CN;
+  if (tid < NCH * NV1) {
+    const int hh = tid / NV1, rem = tid % NV1, b = rem / CN;
     if (b < B && hh < nch) {
-      const float y = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+      const float y = ((part[0][hh][rem] + part[1][hh][rem]) + part[2][hh][rem]) + part[3][hh][rem];
       a.yout[(size_t)b * d + (size_t)(ch0 + hh) * CN + rem % CN] = y;
     }
   }
@@ -527,8 +537,18 @@ struct BatchLayout {
   size_t H, P, scale, theta, umask, C, ybuf, total;
 };
 
+// Workgroups of bpred and bgate: one per CU, more when a CU's share of the
+// neurons would exceed kBSlots, fewer when it would fall below 4.
+static int batch_groups(int64_t d_ff) {
+  int64_t G = device_cu_count();
+  if (G < 1) G = 256;
+  if (G > d_ff / 4) G = d_ff / 4 > 0 ? d_ff / 4 : 1;
+  if ((d_ff + G - 1) / G > kBSlots) G = (d_ff + kBSlots - 1) / kBSlots;
+  return (int)G;
+}
+
 static BatchLayout batch_layout(int64_t d_model, int64_t d_ff, int64_t B) {
-  const int64_t G = (d_ff + kBNeur - 1) / kBNeur;
+  const int64_t G = batch_groups(d_ff);
   BatchLayout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -540,7 +560,7 @@ static BatchLayout batch_layout(int64_t d_model, int64_t d_ff, int64_t B) {
   L.P = take((size_t)G * B * 2 * 4);
   L.scale = take((size_t)B * 4);
   L.theta = take((size_t)B * 4);
-  L.umask = take((size_t)G * 4);
+  L.umask = take((size_t)G * 8);
   L.C = take((size_t)d_ff * kBatchMax * 4);
   L.ybuf = take((size_t)B * d_model * 4);
   L.total = off;
@@ -557,12 +577,14 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
                                    const float* q, int64_t B, float* y, float eps, double z,
                                    const spark_ffn_trace* trace, void* ws, hipStream_t st) {
   constexpr int CN = Chunk<W>::N;
-  constexpr int NCH = (BM * 2 * CN <= 64) ? 2 : 1;  // output chunks per bv workgroup
   const BatchLayout Lo = batch_layout(s.d_model, s.d_ff, B);
   char* base = (char*)ws;
-  const int G = (int)((s.d_ff + kBNeur - 1) / kBNeur);
+  const int G = batch_groups(s.d_ff);
   const int nchunks = (int)(s.d_model / CN);
-  const int G3 = (nchunks + NCH - 1) / NCH;
+  int G3 = device_cu_count();  // bv: one or two output chunks per workgroup
+  if (G3 < 1) G3 = 256;
+  if (G3 > nchunks) G3 = nchunks;
+  if (2 * G3 < nchunks) G3 = (nchunks + 1) / 2;
   // (BM token slots; the entry point keeps BM x max(r, d - r) x 4 within
   // kBatchMaxLds)
   const size_t lds1 = (size_t)BM * s.r * 4, lds2 = (size_t)BM * (s.d_model - s.r) * 4;
@@ -578,7 +600,7 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
   a.P = (float*)(base + Lo.P);
   a.scale = (float*)(base + Lo.scale);
   a.theta = (float*)(base + Lo.theta);
-  a.umask = (uint32_t*)(base + Lo.umask);
+  a.umask = (uint64_t*)(base + Lo.umask);
   a.C = (float*)(base + Lo.C);
   float* ybuf = (float*)(base + Lo.ybuf);
   for (int l = 0; l < n_layers; ++l) {
@@ -588,14 +610,14 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
     a.yin = l == 0 ? q : ybuf;
     a.prenorm = l == 0 ? 0 : 1;
     a.yout = l == n_layers - 1 ? y : ybuf;
-    hipLaunchKernelGGL((bpred<W, BM>), dim3(G), dim3(256), lds1, st, a);
-    hipLaunchKernelGGL((bgate<W, BM>), dim3(G), dim3(256), lds2, st, a);
+    hipLaunchKernelGGL((bpred<W, BM>), dim3(G), dim3(kBThreads), lds1, st, a);
+    hipLaunchKernelGGL((bgate<W, BM>), dim3(G), dim3(kBThreads), lds2, st, a);
     if (trace && (trace->counts || trace->idx || trace->theta || trace->q_in))
       hipLaunchKernelGGL(btrace, dim3((unsigned)B), dim3(256), 0, st, a, trace->counts, trace->idx,
                          trace->idx ? trace->cap : 0, trace->theta, trace->q_in, (int64_t)l, (int64_t)n_layers);
     // bv overwrites ybuf (the input of this layer) only after bpred, bgate and
     // the trace have read it: they precede it on the stream
-    hipLaunchKernelGGL((bv<W, BM, NCH>), dim3(G3), dim3(256), 0, st, a, G);
+    hipLaunchKernelGGL((bv<W, BM>), dim3(G3), dim3(256), 0, st, a, G);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
