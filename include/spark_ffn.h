@@ -111,6 +111,11 @@ int stat_topk(const float *x, int64_t rows, int64_t d, int64_t ldx, int64_t k, f
  * r, d_model - r, d_model multiples of 8 elements).
  * The kernel is a cooperative (co-resident) grid; it returns SPARK_EHIP if the
  * device cannot host it.
+ * Workspace: zero-filled before its first use, then kept between calls (it
+ * carries the tags of the grid-wide exchanges from call to call); calls that
+ * overlap on one workspace race.  A timed-out exchange (a kernel that could not
+ * make progress) ends the call early and sets the 8-byte word at offset 8 of
+ * the workspace to nonzero.
  */
 int spark_ffn_decode(const spark_ffn_shape *s, const spark_ffn_weights *layers, int n_layers, const float *q,
                      int64_t T, float *y, float rms_eps, const spark_ffn_trace *trace, void *ws, size_t ws_bytes,
