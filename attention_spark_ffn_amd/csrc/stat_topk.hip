@@ -152,9 +152,10 @@ __device__ __forceinline__ void process_row(const float (&v)[E][4], int64_t row,
   if (idx != nullptr || vals != nullptr) {
     __syncthreads();
     const int nst = (int)min((int64_t)min(base, kStage), cap);
+    // streaming (nontemporal) stores: the lists are not read back here
     for (int i = tid; i < nst; i += NT) {
-      if (idx) idx[row * cap + i] = S.s_idx[i];
-      if (vals) vals[row * cap + i] = S.s_val[i];
+      if (idx) __builtin_nontemporal_store(S.s_idx[i], idx + row * cap + i);
+      if (vals) __builtin_nontemporal_store(S.s_val[i], vals + row * cap + i);
     }
   }
 }
