@@ -52,6 +52,8 @@ struct BatchArgs {
   uint64_t* umask;   // [G] neurons of each workgroup selected by any token (bit j: its neuron j)
   float* C;          // [d_ff][BM] gated values (0 for a token that does not select the neuron; slots >= B unused)
   float* yout;       // [B][d_model] layer output
+  float* ssp;        // [G3][BM] each V workgroup's sum of squares of its output columns, per token
+  int G3;            // V workgroups
 };
 
 // Sum over the 32 lanes of each half-wave; every lane of the half gets it.
@@ -114,18 +116,29 @@ __global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int B = a.B, d = a.d_model, r = a.r;
   const int n0 = nfirst(blockIdx.x, a.d_ff, gridDim.x), n1 = nfirst(blockIdx.x + 1, a.d_ff, gridDim.x);
-  // token inputs: q[:r] to LDS, sum of squares of the whole row
-  if (tid < (kBThreads / 64) * BM) red[tid / BM][tid % BM] = 0.f;
+  // each token's RMS scale from the previous layer's per-workgroup sums of
+  // squares (half-wave b, fixed order), and q[:r] of every token to LDS
+  if (a.prenorm) {
+    const int b = tid >> 5, l32 = tid & 31;
+    if (b < B) {
+      float ss = 0.f;
+      for (int w0 = l32; w0 < a.G3; w0 += 32 * 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = w0 + 32 * k < a.G3 ? a.ssp[(size_t)(w0 + 32 * k) * BM + b] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ss += v[k];
+      }
+      ss = half_sum(ss);
+      if (l32 == 0) red[0][b] = 1.f / sqrtf(ss / (float)d + a.eps);
+    }
+  }
   for (int i = B * r + tid; i < BM * r; i += kBThreads) qs[i] = 0.f;  // empty token slots
-  __syncthreads();
-  load_tokens<BM, kBThreads>(a.yin, B, d, 0, r, qs, nullptr, red);
+  load_tokens<BM, kBThreads>(a.yin, B, d, 0, r, qs, nullptr, nullptr);
   __syncthreads();
   float sc[BM];
 #pragma unroll
-  for (int b = 0; b < BM; ++b)
-    sc[b] = (b < B && a.prenorm)
-                ? 1.f / sqrtf(((((red[0][b] + red[1][b]) + red[2][b]) + red[3][b]) + red[4][b]) / (float)d + a.eps)
-                : 1.f;
+  for (int b = 0; b < BM; ++b) sc[b] = (b < B && a.prenorm) ? red[0][b] : 1.f;
   if (blockIdx.x == 0 && tid == 0)
 #pragma unroll
     for (int b = 0; b < BM; ++b)
@@ -226,35 +239,53 @@ __global__ __launch_bounds__(kBThreads) void bgate(const BatchArgs a) {
   // the half-wave b (lanes over workgroups, fixed order), all loads first
   {
     const int b = tid >> 5, l32 = tid & 31;
-    constexpr int KG = 8;  // workgroups per lane and round, loads issued together
+    constexpr int KG = 8;  // workgroups per lane held in registers (one pass when G <= 256)
     if (b < B) {
-      float s1 = 0.f;
-      for (int g0 = l32; g0 < G; g0 += 32 * KG) {
-        float mn[KG], nn[KG];
-#pragma unroll
-        for (int k = 0; k < KG; ++k) {
-          const int g = g0 + 32 * k;
-          mn[k] = g < G ? a.P[((size_t)g * B + b) * 2] : 0.f;
-          nn[k] = g < G ? (float)(nfirst(g + 1, a.d_ff, G) - nfirst(g, a.d_ff, G)) : 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < KG; ++k) s1 += nn[k] * mn[k];
-      }
-      const float mu = half_sum(s1) / (float)a.d_ff;
-      float s2 = 0.f;
-      for (int g0 = l32; g0 < G; g0 += 32 * KG) {
+      float s1 = 0.f, s2 = 0.f, mu;
+      if (G <= 32 * KG) {
         float mn[KG], m2v[KG], nn[KG];
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
-          const int g = g0 + 32 * k;
+          const int g = l32 + 32 * k;
           mn[k] = g < G ? a.P[((size_t)g * B + b) * 2] : 0.f;
           m2v[k] = g < G ? a.P[((size_t)g * B + b) * 2 + 1] : 0.f;
           nn[k] = g < G ? (float)(nfirst(g + 1, a.d_ff, G) - nfirst(g, a.d_ff, G)) : 0.f;
         }
 #pragma unroll
+        for (int k = 0; k < KG; ++k) s1 += nn[k] * mn[k];
+        mu = half_sum(s1) / (float)a.d_ff;
+#pragma unroll
         for (int k = 0; k < KG; ++k) {
           const float dm = mn[k] - mu;
           s2 += nn[k] > 0.f ? m2v[k] + nn[k] * dm * dm : 0.f;
+        }
+      } else {  // two passes over the partials, KG per lane at a time
+        for (int g0 = l32; g0 < G; g0 += 32 * KG) {
+          float mn[KG], nn[KG];
+#pragma unroll
+          for (int k = 0; k < KG; ++k) {
+            const int g = g0 + 32 * k;
+            mn[k] = g < G ? a.P[((size_t)g * B + b) * 2] : 0.f;
+            nn[k] = g < G ? (float)(nfirst(g + 1, a.d_ff, G) - nfirst(g, a.d_ff, G)) : 0.f;
+          }
+#pragma unroll
+          for (int k = 0; k < KG; ++k) s1 += nn[k] * mn[k];
+        }
+        mu = half_sum(s1) / (float)a.d_ff;
+        for (int g0 = l32; g0 < G; g0 += 32 * KG) {
+          float mn[KG], m2v[KG], nn[KG];
+#pragma unroll
+          for (int k = 0; k < KG; ++k) {
+            const int g = g0 + 32 * k;
+            mn[k] = g < G ? a.P[((size_t)g * B + b) * 2] : 0.f;
+            m2v[k] = g < G ? a.P[((size_t)g * B + b) * 2 + 1] : 0.f;
+            nn[k] = g < G ? (float)(nfirst(g + 1, a.d_ff, G) - nfirst(g, a.d_ff, G)) : 0.f;
+          }
+#pragma unroll
+          for (int k = 0; k < KG; ++k) {
+            const float dm = mn[k] - mu;
+            s2 += nn[k] > 0.f ? m2v[k] + nn[k] * dm * dm : 0.f;
+          }
         }
       }
       s2 = half_sum(s2);
@@ -359,21 +390,25 @@ __global__ __launch_bounds__(kBThreads) void bgate(const BatchArgs a) {
 // ---------------------------------------------------------------- bv
 // Workgroup w owns the 16-byte column chunks [w NCH, (w + 1) NCH) of the
 // output.  The union of the selected sets (bgate's masks, prefix counts in
-// LDS) is split into 256 contiguous runs, one per thread, each walked
+// LDS) is split into contiguous runs, one per thread, each walked
 // kBvRound neurons at a time with all their loads (the gated values and the
 // V row chunks) issued before any is used; the per-thread sums are then added
 // over lanes (transposing reduction) and waves in a fixed order.
+constexpr int kBvThreads = 512;  // two waves per SIMD: one walks while the other waits on its loads
 template <typename W, int BM>
-__global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
+__global__ __launch_bounds__(kBvThreads) void bv(const BatchArgs a, int G2) {
   constexpr int CN = Chunk<W>::N;
   constexpr int kBvRound = BM >= 8 ? 4 : 8;  // union neurons per round of loads
   constexpr int NCH = 2;             // output chunks per workgroup at most
   constexpr int NV1 = BM * CN;       // accumulators per thread and chunk: token-major, then column
   static_assert(NV1 <= 64 && (NV1 & (NV1 - 1)) == 0, "one transposing reduction of at most 64 columns per chunk");
-  __shared__ float part[4][NCH][NV1];
+  constexpr int NWV = kBvThreads / 64;
+  constexpr int WPT = 2048 / kBvThreads;  // mask words per thread in the prefix count
+  __shared__ float part[NWV][NCH][NV1];
+  __shared__ float yy[NCH][NV1];
   __shared__ uint64_t um[2048];
   __shared__ int pre[2049];
-  __shared__ int wtot[4];
+  __shared__ int wtot[NWV];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int B = a.B, d = a.d_model;
   const int nchunks = d / CN;
@@ -386,12 +421,12 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   const int nch = (int)((int64_t)(o + 1) * nchunks / G3) - ch0;
   const size_t rowb = (size_t)d * sizeof(W);
   const char* vb = (const char*)a.v + (size_t)ch0 * 16;
-  // union masks and their exclusive prefix counts (thread t: words 8t .. 8t+7)
+  // union masks and their exclusive prefix counts (thread t: words WPT t ..)
   int cnt8 = 0;
-  uint64_t w8[8];
+  uint64_t w8[WPT];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int g = 8 * tid + k;
+  for (int k = 0; k < WPT; ++k) {
+    const int g = WPT * tid + k;
     w8[k] = g < G2 ? a.umask[g] : 0ull;
     cnt8 += __builtin_popcountll(w8[k]);
   }
@@ -401,15 +436,15 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   int run = incl - cnt8;
   for (int w2 = 0; w2 < wv; ++w2) run += wtot[w2];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int g = 8 * tid + k;
+  for (int k = 0; k < WPT; ++k) {
+    const int g = WPT * tid + k;
     if (g < 2048) {
       um[g] = w8[k];
       pre[g] = run;
     }
     run += __builtin_popcountll(w8[k]);
   }
-  if (tid == 255) pre[2048] = run;
+  if (tid == kBvThreads - 1) pre[2048] = run;
   __syncthreads();
   const int U = pre[2048];
   float acc[NCH][NV1];
@@ -417,9 +452,9 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   for (int hh = 0; hh < NCH; ++hh)
 #pragma unroll
     for (int i = 0; i < NV1; ++i) acc[hh][i] = 0.f;
-  // thread t takes the union entries [t U / 256, (t + 1) U / 256): one search
+  // thread t takes the union entries [t U / NT, (t + 1) U / NT): one search
   // for the first, then a walk along the set bits of the masks
-  const int e_begin = (int)((int64_t)tid * U / 256), e_end = (int)((int64_t)(tid + 1) * U / 256);
+  const int e_begin = (int)((int64_t)tid * U / kBvThreads), e_end = (int)((int64_t)(tid + 1) * U / kBvThreads);
   int g = 0;
   uint64_t wbits = 0;
   if (e_begin < e_end) {
@@ -485,10 +520,23 @@ __global__ __launch_bounds__(256) void bv(const BatchArgs a, int G2) {
   __syncthreads();
   if (tid < NCH * NV1) {
     const int hh = tid / NV1, rem = tid % NV1, b = rem / CN;
+    float y = 0.f;
     if (b < B && hh < nch) {
-      const float y = ((part[0][hh][rem] + part[1][hh][rem]) + part[2][hh][rem]) + part[3][hh][rem];
+      for (int w2 = 0; w2 < NWV; ++w2) y += part[w2][hh][rem];
       a.yout[(size_t)b * d + (size_t)(ch0 + hh) * CN + rem % CN] = y;
     }
+    yy[hh][rem] = y * y;
+  }
+  __syncthreads();
+  // each token's sum of squares over the owned columns (fixed order), for the
+  // RMS scale of the next layer
+  if (tid < BM) {
+    float ss = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < NCH; ++hh)
+#pragma unroll
+      for (int i = 0; i < CN; ++i) ss += yy[hh][tid * CN + i];
+    a.ssp[(size_t)blockIdx.x * BM + tid] = ss;
   }
 }
 
@@ -534,7 +582,7 @@ __global__ __launch_bounds__(256) void btrace(const BatchArgs a, int32_t* counts
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct BatchLayout {
-  size_t H, P, scale, theta, umask, C, ybuf, total;
+  size_t H, P, scale, theta, umask, C, ybuf, ssp, total;
 };
 
 // Workgroups of bpred and bgate: one per CU, more when a CU's share of the
@@ -563,6 +611,7 @@ static BatchLayout batch_layout(int64_t d_model, int64_t d_ff, int64_t B) {
   L.umask = take((size_t)G * 8);
   L.C = take((size_t)d_ff * kBatchMax * 4);
   L.ybuf = take((size_t)B * d_model * 4);
+  L.ssp = take((size_t)8192 * kBatchMax * 4);  // V workgroups (at most 8192) x token slots
   L.total = off;
   return L;
 }
@@ -590,6 +639,7 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
   const size_t lds1 = (size_t)BM * s.r * 4, lds2 = (size_t)BM * (s.d_model - s.r) * 4;
   hipError_t e = hipSuccess;
   BatchArgs a;
+  a.G3 = G3;
   a.d_model = (int)s.d_model;
   a.d_ff = (int)s.d_ff;
   a.r = (int)s.r;
@@ -602,6 +652,7 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
   a.theta = (float*)(base + Lo.theta);
   a.umask = (uint64_t*)(base + Lo.umask);
   a.C = (float*)(base + Lo.C);
+  a.ssp = (float*)(base + Lo.ssp);
   float* ybuf = (float*)(base + Lo.ybuf);
   for (int l = 0; l < n_layers; ++l) {
     a.k1t = layers[l].k1t;
@@ -617,7 +668,7 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
                          trace->idx ? trace->cap : 0, trace->theta, trace->q_in, (int64_t)l, (int64_t)n_layers);
     // bv overwrites ybuf (the input of this layer) only after bpred, bgate and
     // the trace have read it: they precede it on the stream
-    hipLaunchKernelGGL((bv<W, BM>), dim3(G3), dim3(256), 0, st, a, G);
+    hipLaunchKernelGGL((bv<W, BM>), dim3(G3), dim3(kBvThreads), 0, st, a, G);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
