@@ -62,6 +62,36 @@ __device__ __forceinline__ float half_sum(float v) {
   return v + __shfl_xor(v, 16, kWave);
 }
 
+// Column sums of NV per-lane values (NV a power of two, at most 32) over the
+// 32 lanes of each half-wave, all columns at once: at each step a lane hands
+// half of its remaining columns to the lane m apart and adds the other half of
+// that lane's; after log2(NV) steps each lane holds the partial of one column
+// (col = l32 / (32 / NV)) and the remaining steps add over the lanes that
+// share it.
+template <int NV>
+__device__ __forceinline__ float half_colsum(float (&v)[NV], int lane, int& col) {
+  constexpr int S = NV >= 32 ? 5 : NV >= 16 ? 4 : NV >= 8 ? 3 : NV >= 4 ? 2 : NV >= 2 ? 1 : 0;
+  static_assert((1 << S) == NV, "NV must be a power of two");
+  col = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int m = 16 >> s, h = NV >> (s + 1);
+    const uint32_t upm = (lane & m) ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const uint32_t x = __float_as_uint(v[i]), y = __float_as_uint(v[i + h]);
+      const float give = __uint_as_float((x & upm) | (y & ~upm));
+      const float keep = __uint_as_float((y & upm) | (x & ~upm));
+      v[i] = keep + __shfl_xor(give, m, kWave);
+    }
+    col += (lane & m) ? h : 0;
+  }
+  float t = v[0];
+#pragma unroll
+  for (int m = 16 >> S; m >= 1; m >>= 1) t += __shfl_xor(t, m, kWave);
+  return t;
+}
+
 // Columns [c0, c0 + n) of every token's input row (n a multiple of 4) into
 // LDS at dst[b * n + j], times scale[b] (scale null: unscaled); with ss, the
 // per-wave sums of squares of the whole rows (all d columns) into ss[wave][b].
@@ -199,13 +229,17 @@ __global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
       }
     }
   }
+  {
+    float flat[4 * BM];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int b = 0; b < BM; ++b) {
-      const float t = half_sum(acc[u][b]);
-      if (l32 == 0 && b < B) hs[b][4 * gi + u] = t * sc[b];
-    }
+      for (int b = 0; b < BM; ++b) flat[u * BM + b] = acc[u][b];
+    int col;
+    const float t = half_colsum<4 * BM>(flat, lane, col);
+    const int u = col / BM, b = col % BM;
+    if ((l32 & (32 / (4 * BM) - 1)) == 0 && b < B) hs[b][4 * gi + u] = t * sc[b];
+  }
   __syncthreads();
   // scores out, and each token's (mean, M2) over the owned neurons
   const int nown = n1 - n0;  // at most kBSlots
@@ -369,17 +403,32 @@ __global__ __launch_bounds__(kBThreads) void bgate(const BatchArgs a) {
   }
   // gated values of the owned neurons: C[n][b] (exact 0 for the tokens that
   // do not select n); the union mask of the workgroup
+  {
+    float flat[4 * BM];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int n = n0 + 4 * gi + u;
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int b = 0; b < BM; ++b) {
-      const float t = half_sum(acc[u][b]);
-      if (l32 == 0 && b < B && n < n1)
-        a.C[(size_t)n * BM + b] = ((sm[u] >> b) & 1u) ? gelu_tanh(hv[u][b] - th[b]) * t : 0.f;
-    }
-    if (l32 == 0) sel[4 * gi + u] = sm[u];
+      for (int b = 0; b < BM; ++b) flat[u * BM + b] = acc[u][b];
+    int col;
+    const float t = half_colsum<4 * BM>(flat, lane, col);
+    const int u = col / BM, b = col % BM, n = n0 + 4 * gi + u;
+    // this lane's (neuron, token) pair: its score and selection bit (the
+    // registers of pair (u, b) are picked with selects, not indexed)
+    float h = 0.f;
+    uint32_t smu = 0;
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+      for (int bb = 0; bb < BM; ++bb) {
+        h = (uu == u && bb == b) ? hv[uu][bb] : h;
+        smu = uu == u ? sm[uu] : smu;
+      }
+    if ((l32 & (32 / (4 * BM) - 1)) == 0 && b < B && n < n1)
+      a.C[(size_t)n * BM + b] = ((smu >> b) & 1u) ? gelu_tanh(h - th[b]) * t : 0.f;
   }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (l32 == 0) sel[4 * gi + u] = sm[u];
   __syncthreads();
   if (tid < 64) {
     const uint64_t m = __builtin_amdgcn_ballot_w64(lane < kBSlots && sel[lane < kBSlots ? lane : 0] != 0);
