@@ -213,7 +213,7 @@ int spark_attn_prefill_workspace_size(int64_t T, int64_t Hq, int64_t Hkv, int64_
     return SPARK_EINVAL;
   if (r % 8 != 0 || (hd - r) % 8 != 0) return SPARK_EINVAL;
   if (hd > 512 || T > 16384 || Hq > 1024) return SPARK_EUNSUPPORTED;
-  *bytes = spark::attn_prefill_workspace_bytes(T, Hq, Hkv, hd);
+  *bytes = spark::attn_prefill_workspace_bytes(T, Hq, Hkv, hd, r);
   return SPARK_OK;
 }
 

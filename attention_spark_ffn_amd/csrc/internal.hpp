@@ -42,7 +42,7 @@ hipError_t launch_prefill(const spark_ffn_shape& s, const spark_ffn_weights& w, 
 
 // ---------------------------------------------------------------- attention
 size_t attn_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn);
-size_t attn_prefill_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t hd);
+size_t attn_prefill_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t hd, int64_t r);
 hipError_t launch_attn_prefill(const void* q, const void* k1, const void* k2, const void* v, int64_t T, int64_t Hq,
                                int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float* out, int32_t* counts,
                                float* theta, void* ws, hipStream_t st);

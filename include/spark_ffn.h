@@ -185,9 +185,13 @@ int spark_attn_decode(const void *q, const void *k1, const void *k2, const void 
  *   q [T][Hq][hd] bf16 (position-major); k1 [Hkv][T][r], k2 [Hkv][T][hd-r],
  *   v [Hkv][T][hd] bf16; out [T][Hq][hd] fp32; counts [T][Hq] (may be NULL);
  *   theta [T][Hq] (may be NULL; NaN where t + 1 <= k_attn).
- * The scores and gated weights run as dense products on the matrix cores
- * (unselected positions contribute exact zeros); the workspace holds
- * Hq * T * T fp32 scores and bf16 weights.
+ * All products run on the matrix cores.  With r = hd - r in {32, 64, 128}
+ * two fused kernels walk the keys of each query twice (moments and maximum
+ * of the scores, then the gated weights and their product with V) and the
+ * workspace holds V^T, two floats per (head, position) and the threshold
+ * table; other head splits materialise Hq * T * T fp32 scores and bf16
+ * weights in the workspace (unselected positions contribute exact zeros).
+ * spark_attn_prefill_workspace_size gives the size for either.
  * Requires Hq % Hkv == 0, hd <= 512 and a multiple of 8, 0 < r < hd with r and
  * hd - r multiples of 8, 1 <= T <= 16384, k_attn >= 1.
  */

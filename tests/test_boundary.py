@@ -165,7 +165,11 @@ def test_attention_prefill_rejects_bad_arguments():
     assert P(0, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EINVAL  # T
     assert P(1 << 15, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED  # T too long
     assert P(64, 8, 4, 1024, 128, 256, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED  # hd
-    assert P(64, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_OK and n.value > 64 * 64 * 8 * 6
+    # r = hd - r: the fused kernels need only V^T and the threshold table
+    assert P(64, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_OK
+    assert 4 * 256 * 64 * 2 <= n.value < 64 * 64 * 8 * 6
+    # other head splits materialise fp32 scores and bf16 weights
+    assert P(64, 8, 4, 96, 32, 16, ctypes.byref(n)) == sf.SPARK_OK and n.value > 64 * 64 * 8 * 6
     ws = ctypes.create_string_buffer(16)
     assert L.spark_attn_prefill(None, None, None, None, 64, 8, 4, 256, 128, 256, None, None, None, ws, 16,
                                 None) == sf.SPARK_EINVAL

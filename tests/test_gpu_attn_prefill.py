@@ -48,6 +48,9 @@ def run_prefill(T, Hq, Hkv, hd, r, ka, seed, tol=2e-2, scale=None):
     (130, 2, 1, 128, 64, 200),    # every row dense (T <= k_attn)
     (1000, 8, 4, 256, 128, 256),
     (1, 1, 1, 16, 8, 4),          # one position
+    (200, 4, 2, 96, 32, 32),      # r != hd - r: the materialised-scores path
+    (150, 6, 2, 64, 32, 16),      # three heads per KV head: 64-query row sets of one head
+    (257, 2, 2, 32, 16, 300),     # one head per KV head, every row dense
 ])
 def test_attn_prefill_shapes(T, Hq, Hkv, hd, r, ka):
     run_prefill(T, Hq, Hkv, hd, r, ka, seed=T + hd)
