@@ -110,7 +110,7 @@ def _oracle_rate(fn, n_units: int, unit: str, sample: str) -> dict:
     fn()
     dt = time.perf_counter() - t0
     return {"value": n_units / dt, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{sample}, {dt:.1f} s"}
+            "sample": f"{sample}, {dt:.3f} s"}
 
 
 def batched_decode(torch, sf, layers, qs):
@@ -234,7 +234,8 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
         "positions_per_s": Tp / ms * 1e3, "mean_attended": float(pc.double().mean().item()),
         "roofline": {"bound": "mfma", "achieved": flops / ms / 1e9, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
-                     "note": "causal products S, gated K2 scores and W V over the whole call"}}
+                     "note": "algorithmic causal products (scores, gate products, weights x V) over the "
+                             "whole call; the moments pass recomputes the scores and is not counted"}}
     if with_cpu:
         qs, k1s, k2s, vs = synth.attn_prefill_inputs(seed, 512, 8, 4, 256, 128)
         res["attention_prefill"]["cpu_baseline"] = _oracle_rate(
