@@ -95,7 +95,8 @@ hipError_t launch_prefill(const spark_ffn_shape& s, const spark_ffn_weights& w, 
   }
   if (e != hipSuccess) return e;
   // 4. Y = C V
-  hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)(((F + 63) / 64) * ((dm + 63) / 64))), dim3(256), 0, st,
+  // (d_ff is a multiple of 256 and d_model of 8: whole 16-byte chunks both ways)
+  hipLaunchKernelGGL(transpose_bf16_x8, dim3((unsigned)((F + 63) / 64), (unsigned)((dm + 63) / 64)), dim3(256), 0, st,
                      (const bf16_t*)w.v, F, dm, Vt, F);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

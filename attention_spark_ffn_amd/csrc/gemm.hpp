@@ -290,6 +290,33 @@ static __global__ __launch_bounds__(256) void transpose_bf16(const bf16_t* __res
   }
 }
 
+// The same for K and N multiples of 8: 16-byte loads along N and 16-byte
+// stores along K.
+static __global__ __launch_bounds__(256) void transpose_bf16_x8(const bf16_t* __restrict__ V, int K, int N,
+                                                                bf16_t* __restrict__ Vt, int ldo) {
+  __shared__ bf16_t tile[64][72];  // [k][n]
+  const int k0 = blockIdx.x * 64, n0 = blockIdx.y * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 256 * i, kr = e >> 3, cc = e & 7;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (k0 + kr < K && n0 + 8 * cc < N) x = load16(V + (size_t)(k0 + kr) * N + n0 + 8 * cc);
+    *reinterpret_cast<u32x4*>(&tile[kr][8 * cc]) = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 256 * i, nr = e >> 3, kc = e & 7;
+    if (n0 + nr < N && k0 + 8 * kc < K) {
+      u32x4 x;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        x[w] = (uint32_t)tile[8 * kc + 2 * w][nr] | ((uint32_t)tile[8 * kc + 2 * w + 1][nr] << 16);
+      *reinterpret_cast<u32x4*>(Vt + (size_t)(n0 + nr) * ldo + k0 + 8 * kc) = x;
+    }
+  }
+}
+
 // Tile configuration of the prefill products: 128 x 128 per workgroup, four
 // waves of 64 x 64.  (Two waves of 128 x 64, at one wave per SIMD, measured
 // slower: too little to hide the LDS and global latencies.)
