@@ -9,7 +9,8 @@
 //   s_j = q_h[:r] . k1[g][j];  S = stat top-k of s (all j when n_ctx <= k_attn)
 //   out_h = sum_{j in S} softmax_S(s)_j * softplus(q_h[r:] . k2[g][j]) * v[g][j]
 //
-// gfx950 mapping: the context is cut into chunks of 256 tokens, and every
+// gfx950 mapping: the context is cut into chunks of CK tokens (64, 128 or 256:
+// the largest that still gives the scan at least 256 workgroups), and every
 // step runs over (head, chunk) pairs so that the whole chip works on one
 // decode step:
 //   attn_scores (KV head, chunk): the predictor scan, the only pass over all
@@ -33,9 +34,21 @@
 
 namespace spark {
 
-constexpr int kChunk = 256;   // tokens per chunk (one workgroup of the scan and of the selection)
-constexpr int kMaxGroup = 8;  // query heads per KV head handled in registers
+constexpr int kMaxGroup = 8;      // query heads per KV head handled in registers
+constexpr int kMaxChunks = 4096;  // chunks per head (n_ctx <= 2^20)
 
+// Chunk length of a context: 64, 128 or 256 tokens, the largest giving the
+// scan at least 256 workgroups.  A shorter chunk is only taken while n_ctx <
+// 256 * 128, so a head never has more than kMaxChunks chunks for n_ctx <=
+// 2^20 (the interface's limit).  The workspace layout and the launch both
+// take the length from here.
+static int chunk_tokens(int64_t Hkv, int64_t n_ctx) {
+  int ck = 256;
+  while (ck > 64 && Hkv * ((n_ctx + ck - 1) / ck) < 256) ck >>= 1;
+  return ck;
+}
+
+template <int kChunk>
 __global__ __launch_bounds__(256) void attn_scores(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k1,
                                                    int Hq, int Hkv, int n_ctx, int hd, int r,
                                                    float* __restrict__ scores, float2* __restrict__ cstat) {
@@ -126,6 +139,7 @@ __device__ __forceinline__ float block_max256(float v, float* red) {
 // theta of head h from its chunk statistics: mean = sum n_c mean_c / n, then
 // M2 = sum (M2_c + n_c (mean_c - mean)^2) (two plain sums in a fixed order,
 // Chan et al.'s combination).  Called by one wave; every lane gets the result.
+template <int kChunk>
 __device__ __forceinline__ float head_theta(const float2* __restrict__ cst, int nch, int n_ctx, float z, int lane) {
   float s1 = 0.f;
   for (int c = lane; c < nch; c += 64) s1 += (float)min(kChunk, n_ctx - c * kChunk) * cst[c].x;
@@ -143,6 +157,7 @@ __device__ __forceinline__ float head_theta(const float2* __restrict__ cst, int 
 // Partial of one (query head, chunk): m_c, l_c, count, then o_c[hd].
 constexpr int kPartHead = 4;
 
+template <int kChunk>
 __global__ __launch_bounds__(256) void attn_chunk(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k2,
                                                   const bf16_t* __restrict__ v, int Hq, int Hkv, int n_ctx, int hd,
                                                   int r, int dense, float z, const float* __restrict__ scores,
@@ -162,7 +177,7 @@ __global__ __launch_bounds__(256) void attn_chunk(const bf16_t* __restrict__ q, 
   const int g = h / (Hq / Hkv), rc = hd - r;
   for (int c = tid; c < rc; c += 256) qc[c] = bf16_to_f32(q[(size_t)h * hd + r + c]);
   if (wv == 0) {
-    const float th = dense ? -INFINITY : head_theta(cstat + (size_t)h * nch, nch, n_ctx, z, lane);
+    const float th = dense ? -INFINITY : head_theta<kChunk>(cstat + (size_t)h * nch, nch, n_ctx, z, lane);
     if (lane == 0) th_s = th;
   }
   const float s = tid < nc ? scores[(size_t)h * n_ctx + j0 + tid] : -INFINITY;
@@ -236,12 +251,11 @@ __global__ __launch_bounds__(256) void attn_chunk(const bf16_t* __restrict__ q, 
     for (int e = tid; e < cnt; e += 256) lidx[(size_t)h * n_ctx + j0 + e] = j0 + loc[e];
 }
 
-constexpr int kMaxChunks = 4096;  // n_ctx <= 2^20
-
 // One 1024-thread workgroup per query head.  The chunk statistics are read in
 // parallel; the weighted column sums run in four quarters of the chunks (chunk
 // c in quarter c % 4, eight loads in flight per thread) combined in a fixed
 // order.
+template <int kChunk>
 __global__ __launch_bounds__(1024) void attn_merge(int n_ctx, int hd, const float* __restrict__ part,
                                                    const int32_t* __restrict__ lidx, float* __restrict__ out,
                                                    int32_t* __restrict__ counts, int32_t* __restrict__ idx_out,
@@ -362,8 +376,7 @@ static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct AttnLayout {
   size_t scores, cstat, part, lidx, total;
 };
-static AttnLayout attn_layout(int64_t Hq, int64_t n_ctx, int64_t hd) {
-  const int64_t nch = (n_ctx + kChunk - 1) / kChunk;
+static AttnLayout attn_layout(int64_t Hq, int64_t nch, int64_t n_ctx, int64_t hd) {
   AttnLayout L;
   size_t off = 0;
   L.scores = off;
@@ -379,33 +392,52 @@ static AttnLayout attn_layout(int64_t Hq, int64_t n_ctx, int64_t hd) {
 }
 
 size_t attn_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn) {
-  (void)Hkv, (void)r, (void)k_attn;
-  return attn_layout(Hq, n_ctx, hd).total;
+  (void)r, (void)k_attn;
+  const int ck = chunk_tokens(Hkv, n_ctx);
+  return attn_layout(Hq, (n_ctx + ck - 1) / ck, n_ctx, hd).total;
 }
 
-hipError_t launch_attn_decode(const void* q, const void* k1, const void* k2, const void* v, int64_t Hq, int64_t Hkv,
-                              int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn, double z, float* out,
-                              int32_t* counts, int32_t* idx, int64_t cap, float* theta, void* ws, hipStream_t st) {
-  const AttnLayout L = attn_layout(Hq, n_ctx, hd);
+template <int CK>
+static hipError_t launch_attn_decode_t(const void* q, const void* k1, const void* k2, const void* v, int64_t Hq,
+                                       int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn, double z,
+                                       float* out, int32_t* counts, int32_t* idx, int64_t cap, float* theta, void* ws,
+                                       hipStream_t st) {
+  const int nch = (int)((n_ctx + CK - 1) / CK);
+  const AttnLayout L = attn_layout(Hq, nch, n_ctx, hd);
   char* base = (char*)ws;
   float* scores = (float*)(base + L.scores);
   float2* cstat = (float2*)(base + L.cstat);
   float* part = (float*)(base + L.part);
   int32_t* lidx = idx ? (int32_t*)(base + L.lidx) : nullptr;
-  const int nch = (int)((n_ctx + kChunk - 1) / kChunk);
-  hipLaunchKernelGGL(attn_scores, dim3((unsigned)(Hkv * nch)), dim3(256), 0, st, (const bf16_t*)q,
+  hipLaunchKernelGGL(attn_scores<CK>, dim3((unsigned)(Hkv * nch)), dim3(256), 0, st, (const bf16_t*)q,
                      (const bf16_t*)k1, (int)Hq, (int)Hkv, (int)n_ctx, (int)hd, (int)r, scores, cstat);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int dense = n_ctx <= k_attn ? 1 : 0;
-  hipLaunchKernelGGL(attn_chunk, dim3((unsigned)(Hq * nch)), dim3(256), 0, st, (const bf16_t*)q, (const bf16_t*)k2,
-                     (const bf16_t*)v, (int)Hq, (int)Hkv, (int)n_ctx, (int)hd, (int)r, dense, (float)z, scores,
-                     cstat, part, lidx);
+  hipLaunchKernelGGL(attn_chunk<CK>, dim3((unsigned)(Hq * nch)), dim3(256), 0, st, (const bf16_t*)q,
+                     (const bf16_t*)k2, (const bf16_t*)v, (int)Hq, (int)Hkv, (int)n_ctx, (int)hd, (int)r, dense,
+                     (float)z, scores, cstat, part, lidx);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge, dim3((unsigned)Hq), dim3(1024), 0, st, (int)n_ctx, (int)hd, part, lidx, out, counts,
-                     idx, cap, theta);
+  hipLaunchKernelGGL(attn_merge<CK>, dim3((unsigned)Hq), dim3(1024), 0, st, (int)n_ctx, (int)hd, part, lidx, out,
+                     counts, idx, cap, theta);
   return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const void* q, const void* k1, const void* k2, const void* v, int64_t Hq, int64_t Hkv,
+                              int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn, double z, float* out,
+                              int32_t* counts, int32_t* idx, int64_t cap, float* theta, void* ws, hipStream_t st) {
+  switch (chunk_tokens(Hkv, n_ctx)) {
+    case 64:
+      return launch_attn_decode_t<64>(q, k1, k2, v, Hq, Hkv, n_ctx, hd, r, k_attn, z, out, counts, idx, cap, theta, ws,
+                                      st);
+    case 128:
+      return launch_attn_decode_t<128>(q, k1, k2, v, Hq, Hkv, n_ctx, hd, r, k_attn, z, out, counts, idx, cap, theta,
+                                       ws, st);
+    default:
+      return launch_attn_decode_t<256>(q, k1, k2, v, Hq, Hkv, n_ctx, hd, r, k_attn, z, out, counts, idx, cap, theta,
+                                       ws, st);
+  }
 }
 
 }  // namespace spark
