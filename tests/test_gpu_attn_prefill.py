@@ -81,3 +81,32 @@ def test_attn_prefill_deterministic():
     a = sf.spark_attn_prefill(*args, 256)
     b = sf.spark_attn_prefill(*args, 256)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_attn_prefill_bench_workload_sampled_rows():
+    """The timed attention-prefill workload (a 4096-position prompt, Hq 8, Hkv 4,
+    hd 256, r 128, k_attn 256, the bench's inputs): row t of a causal prefill
+    is a decode step over positions 0..t, so sampled rows are checked one by
+    one against the oracle's decode on that prefix, all heads, including dense
+    rows, the first thresholded row and the last."""
+    T, Hq, Hkv, hd, r, ka = 4096, 8, 4, 256, 128, 256
+    qb, k1b, k2b, vb = synth.attn_prefill_inputs(0, T, Hq, Hkv, hd, r)
+    out, counts, theta = sf.spark_attn_prefill(to_dev(qb), to_dev(k1b), to_dev(k2b), to_dev(vb), ka)
+    torch.cuda.synchronize()
+    out, counts, theta = (t.cpu().numpy() for t in (out, counts, theta))
+    for t in (0, 37, 255, 256, 257, 1023, 2048, 2049, 3333, 4094, 4095):
+        n = t + 1
+        ref = oracle.spark_attn_decode(np.ascontiguousarray(qb[t]), np.ascontiguousarray(k1b[:, :n]),
+                                       np.ascontiguousarray(k2b[:, :n]), np.ascontiguousarray(vb[:, :n]), ka)
+        for h in range(Hq):
+            if n <= ka:
+                assert counts[t, h] == n and np.isnan(theta[t, h]), (t, h)
+            else:
+                s = ref["scores"][h]
+                sd = s.std()
+                th = ref["theta"][h]
+                assert abs(theta[t, h] - th) <= 1e-5 * (abs(th) + sd), (t, h, theta[t, h], th)
+                if counts[t, h] != ref["counts"][h]:
+                    near = int(np.sum(np.abs(s - th) <= TIE_BAND * sd))
+                    assert abs(int(counts[t, h]) - int(ref["counts"][h])) <= near, (t, h)
+            assert rel_err(out[t, h], ref["out"][h]) <= 2e-2, (t, h, rel_err(out[t, h], ref["out"][h]))
