@@ -341,13 +341,19 @@ __device__ __forceinline__ float softplus_gate(float g) {
 }  // namespace
 
 // Pass 1: per row the threshold and the largest score.  Eight waves: the two
-// row sets times four key phases (tile 4 s + p of step s for phase p),
-// register-staged buffer loads one step ahead (keys outside the head read as
-// zeros; their scores are masked).
+// row sets times four key phases (tile 4 s + p of step s for phase p).  The
+// four key tiles of a step go straight from memory to LDS (buffer loads with
+// the LDS destination; keys outside the head read as zeros and are masked),
+// double-buffered as in the fused kernel.
 template <int R>
 __global__ __launch_bounds__(kMomentThreads) void attn_prefill_moments(const FusedArgs a) {
-  constexpr int KA = R / 16, K1S = R + 8, C = 16 * R, PK = (C + kMomentThreads - 1) / kMomentThreads;
-  __shared__ alignas(16) bf16_t k1s[4 * 32 * K1S];
+  constexpr int KA = R / 16, K1S = R + 8;
+  constexpr int JM = 2 * (R / 8 + 1);  // 1 KB load jobs per step: four padded tiles of 32 rows
+  constexpr int NW = kMomentThreads / 64, NJ = (JM + NW - 1) / NW;
+  constexpr int BUF = 1024 * JM;
+  static_assert(4 * 32 * K1S * 2 == BUF, "four tiles are whole jobs");
+  __shared__ alignas(16) char mb0[BUF];
+  __shared__ alignas(16) char mb1[BUF];
   __shared__ float st[4][2][32][4];  // [phase][row set][query]: n, mean, M2, max
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rs = wv & 1, par = wv >> 1, col = lane & 31, hl = lane >> 5;
@@ -358,46 +364,29 @@ __global__ __launch_bounds__(kMomentThreads) void attn_prefill_moments(const Fus
     const int h = F.head(rs), q0 = F.first(rs), diag = q0 >> 5, tq = q0 + col;
     const bool live = q0 < T;
     const int nsteps = F.steps<4>();
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.k1 + (size_t)(F.head(0) / a.G) * T * R), (short)0,
-                                          T * R * 2, 0x00020000);
+    const rsrc_t rk = make_rsrc(a.k1 + (size_t)(F.head(0) / a.G) * T * R, (uint32_t)T * R * 2);
+    // this wave's jobs j = wv + NW i: per-lane byte offsets at step 0 (a step
+    // moves the keys by 128)
+    int o1[NJ];
+#pragma unroll
+    for (int i = 0; i < NJ; ++i) o1[i] = key_job_offset<R>(wv + NW * i, lane, F);
+    const int dstep = (F.down ? -128 : 128) * 2 * R;
+    auto issue = [&](char* buf, int s) {
+#pragma unroll
+      for (int i = 0; i < NJ; ++i)
+        if (wv + NW * i < JM) load_lds16(rk, buf + 1024 * (wv + NW * i), (uint32_t)(o1[i] + s * dstep));
+    };
     bf16x8 qa[KA];
     load_qfrag(qa, a.q + ((size_t)min(tq, T - 1) * Hq + h) * (2 * R) + 8 * hl);
-    // chunk i of this thread: key row `row` of the four tiles of a step, 16
-    // bytes at kc; its byte offset at step 0 and per step
-    int boff[PK];
-#pragma unroll
-    for (int i = 0; i < PK; ++i) {
-      const int c = tid + kMomentThreads * i, row = c / (R / 8), kc = c % (R / 8);
-      const int key0 = F.down ? 32 * (F.last - (row >> 5)) + (row & 31) : row;
-      boff[i] = key0 * 2 * R + 16 * kc;
-    }
-    const int bstep = (F.down ? -128 : 128) * 2 * R;
-    u32x4 sk[PK];
-    auto gload = [&](int s) {
-#pragma unroll
-      for (int i = 0; i < PK; ++i)
-        if (C % kMomentThreads == 0 || tid + kMomentThreads * i < C)
-          sk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, boff[i] + s * bstep, 0, 0));
-    };
     Moments mo = {0.f, 0.f, 0.f};
     float mx = -INFINITY;
-    gload(0);
-    for (int s = 0; s < nsteps; ++s) {
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < PK; ++i) {
-        const int c = tid + kMomentThreads * i;
-        if (C % kMomentThreads == 0 || c < C) {
-          const int row = c / (R / 8), kc = c % (R / 8);
-          *reinterpret_cast<u32x4*>(k1s + (row >> 5) * 32 * K1S + tile_perm(row & 31) * K1S + 8 * kc) = sk[i];
-        }
-      }
-      __syncthreads();
-      if (s + 1 < nsteps) gload(s + 1);
+    auto step = [&](const char* cur, char* nxt, int s) {
+      wait_vmcnt0();
+      __syncthreads();  // step s is in LDS; every wave is done with step s - 1
+      if (s + 1 < nsteps) issue(nxt, s + 1);
       const int kt = F.tile<4>(s, par);
       if (live && kt >= 0 && kt <= diag) {
-        const f32x16 sc = tile_scores<KA>(k1s + par * 32 * K1S, K1S, qa, col, hl);
+        const f32x16 sc = tile_scores<KA>(reinterpret_cast<const bf16_t*>(cur) + par * 32 * K1S, K1S, qa, col, hl);
         if (kt < diag) {
           // a whole tile: sixteen scores per lane
           float s0 = 0.f, s1 = 0.f, x0 = sc[0], x1 = sc[1];
@@ -447,7 +436,14 @@ __global__ __launch_bounds__(kMomentThreads) void attn_prefill_moments(const Fus
           }
         }
       }
+    };
+    wait_vmcnt0();  // the fragments above are in registers before the step loop
+    issue(mb0, 0);
+    for (int s = 0; s < nsteps; s += 2) {
+      step(mb0, mb1, s);
+      if (s + 1 < nsteps) step(mb1, mb0, s + 1);
     }
+    __syncthreads();  // every wave is done with the tiles before the next phase's loads
     // the two lane halves hold the same query (lower half on the left)
     Moments o;
     o.n = __shfl_xor(mo.n, 32, kWave);
