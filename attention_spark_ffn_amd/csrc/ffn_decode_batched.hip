@@ -52,8 +52,8 @@ struct BatchArgs {
   uint64_t* umask;   // [G] neurons of each workgroup selected by any token (bit j: its neuron j)
   float* C;          // [d_ff][BM] gated values (0 for a token that does not select the neuron; slots >= B unused)
   float* yout;       // [B][d_model] layer output
-  float* ssp;        // [G3][BM] each V workgroup's sum of squares of its output columns, per token
-  int G3;            // V workgroups
+  float* ssp;        // [G3][BM] each reduce workgroup's sum of squares of its output columns, per token
+  int G3;            // reduce workgroups (column segments)
 };
 
 // Sum over the 32 lanes of each half-wave; every lane of the half gets it.
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kBThreads) void bgate(const BatchArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- bv
+// ---------------------------------------------------------------- bv (one token)
 // Workgroup w owns the 16-byte column chunks [w NCH, (w + 1) NCH) of the
 // output.  The union of the selected sets (bgate's masks, prefix counts in
 // LDS) is split into contiguous runs, one per thread, each walked
@@ -589,6 +589,196 @@ __global__ __launch_bounds__(kBvThreads) void bv(const BatchArgs a, int G2) {
   }
 }
 
+// ---------------------------------------------------------------- bv2 + breduce (two or more tokens)
+// The V product by (column block, union slice): workgroup (cb, sp) takes the
+// 128-byte line cb of every V row it needs (eight 16-byte chunks) and the
+// union entries [sp U / S, (sp + 1) U / S).  Eight lanes read one row's line
+// together (lane l: row l / 8 of the wave's eight rows, chunk l % 8), so a
+// wave's load instruction covers eight whole lines, and each V row is read by
+// one workgroup per line instead of one per 16-byte chunk.  The slice sums go
+// to P2[sp][b][column]; breduce adds the slices in a fixed order and forms
+// each token's sum of squares for the next layer's RMS scale.
+constexpr int kBv2Threads = 256;
+constexpr int kBv2Round = 4;      // rows per lane in flight
+constexpr int kBv2Rows = 1024;    // union entries whose neurons are resolved into LDS at a time
+
+// Slices per column block: about two workgroups per CU over the whole grid.
+static int bv2_slices(int64_t d_model, int cn) {
+  const int64_t nblocks = (d_model / cn + 7) / 8;
+  int64_t cus = device_cu_count();
+  if (cus < 1) cus = 256;
+  int64_t S = (2 * cus + nblocks - 1) / nblocks;
+  return (int)(S < 1 ? 1 : S > 64 ? 64 : S);
+}
+
+// One halving step of octet_colsum: lanes with bit M of the lane index set
+// keep the upper K / 2 of their K values, the others the lower, each adding
+// the partner's (lane ^ M) matching half.
+template <int M, int K, int NV>
+__device__ __forceinline__ void octet_step(float (&v)[NV], int lane) {
+  const bool up = (lane & M) != 0;
+#pragma unroll
+  for (int j = 0; j < K / 2; ++j) {
+    const float send = up ? v[j] : v[j + K / 2];
+    const float recv = __shfl_xor(send, M, kWave);
+    v[j] = (up ? v[j + K / 2] : v[j]) + recv;
+  }
+}
+// v[0 .. NV) summed over the eight lanes that share lane % 8, transposing:
+// afterwards lane l holds in v[0 .. NV / 8) the sums of the values
+// (NV / 8) (l / 8) + j.
+template <int NV>
+__device__ __forceinline__ void octet_colsum(float (&v)[NV], int lane) {
+  static_assert(NV >= 8 && (NV & (NV - 1)) == 0, "a power of two, at least 8");
+  octet_step<32, NV, NV>(v, lane);
+  octet_step<16, NV / 2, NV>(v, lane);
+  octet_step<8, NV / 4, NV>(v, lane);
+}
+
+template <typename W, int BM>
+__global__ __launch_bounds__(kBv2Threads) void bv2(const BatchArgs a, int G2, int S, float* __restrict__ P2) {
+  constexpr int CN = Chunk<W>::N;
+  constexpr int NV = BM * CN < 8 ? 8 : BM * CN;  // accumulators per lane (padded to eight)
+  constexpr int NWV = kBv2Threads / 64;
+  constexpr int WPT = 2048 / kBv2Threads;  // mask words per thread in the prefix count
+  __shared__ uint64_t um[2048];
+  __shared__ int pre[2049];
+  __shared__ int wtot[NWV];
+  __shared__ int rows[kBv2Rows];
+  __shared__ float part[NWV][8][NV];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int B = a.B, d = a.d_model, nchunks = d / CN;
+  const int cb = blockIdx.x / S, sp = blockIdx.x % S;
+  // union masks and their exclusive prefix counts (thread t: words WPT t ..)
+  int cnt8 = 0;
+  uint64_t w8[WPT];
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int g = WPT * tid + k;
+    w8[k] = g < G2 ? a.umask[g] : 0ull;
+    cnt8 += __builtin_popcountll(w8[k]);
+  }
+  const int incl = wave_incl_scan_dpp(cnt8);
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  int run = incl - cnt8;
+  for (int w2 = 0; w2 < wv; ++w2) run += wtot[w2];
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int g = WPT * tid + k;
+    um[g] = w8[k];
+    pre[g] = run;
+    run += __builtin_popcountll(w8[k]);
+  }
+  if (tid == kBv2Threads - 1) pre[2048] = run;
+  __syncthreads();
+  const int U = pre[2048];
+  const int e0 = (int)((int64_t)sp * U / S), e1 = (int)((int64_t)(sp + 1) * U / S);
+  // this lane: row rl of each group of eight, chunk c of the block's line
+  const int rl = lane >> 3, c = lane & 7, gc = cb * 8 + c;
+  const size_t rowb = (size_t)d * sizeof(W);
+  const char* vb = (const char*)a.v + (size_t)(gc < nchunks ? gc : nchunks - 1) * 16;
+  float acc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+  for (int s0 = e0; s0 < e1; s0 += kBv2Rows) {
+    const int ns = min(kBv2Rows, e1 - s0);
+    // neuron of each entry: the workgroup g holding it (last g with pre[g] <= e),
+    // then the (e - pre[g])-th set bit of its mask
+    __syncthreads();  // the previous sub-slice's rows are read
+    for (int i = tid; i < ns; i += kBv2Threads) {
+      const int e = s0 + i;
+      int lo = 0, hi = G2 - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= e) lo = mid; else hi = mid - 1;
+      }
+      uint64_t w = um[lo];
+      for (int k = e - pre[lo]; k > 0; --k) w &= w - 1;
+      rows[i] = nfirst(lo, a.d_ff, G2) + __builtin_ctzll(w);
+    }
+    __syncthreads();
+    // rows (k NWV + wv) 8 + rl of each pass; a slot past the sub-slice repeats
+    // row 0 (in bounds) with weight zero, so a pass has no branches
+    for (int p0 = 0; p0 < ns; p0 += kBv2Round * NWV * 8) {
+      int n[kBv2Round];
+      bool ok[kBv2Round];
+#pragma unroll
+      for (int k = 0; k < kBv2Round; ++k) {
+        const int i = p0 + (k * NWV + wv) * 8 + rl;
+        ok[k] = i < ns;
+        n[k] = rows[ok[k] ? i : 0];
+      }
+      f32x4 cv[kBv2Round][(BM + 3) / 4];
+      u32x4 raw[kBv2Round];
+#pragma unroll
+      for (int k = 0; k < kBv2Round; ++k) {
+        if (BM >= 4) {
+#pragma unroll
+          for (int j = 0; j < BM / 4; ++j) cv[k][j] = reinterpret_cast<const f32x4*>(a.C + (size_t)n[k] * BM)[j];
+        } else {
+#pragma unroll
+          for (int b = 0; b < BM; ++b) cv[k][0][b] = a.C[(size_t)n[k] * BM + b];
+        }
+        raw[k] = load16(vb + (size_t)n[k] * rowb);
+      }
+#pragma unroll
+      for (int k = 0; k < kBv2Round; ++k) {
+        float wf[CN];
+        Chunk<W>::widen(raw[k], wf);
+#pragma unroll
+        for (int b = 0; b < BM; ++b) {
+          const float cb_ = ok[k] ? cv[k][b / 4][b % 4] : 0.f;
+#pragma unroll
+          for (int i = 0; i < CN; ++i) acc[b * CN + i] += cb_ * wf[i];
+        }
+      }
+    }
+  }
+  // sums over the eight rows of a wave, then over the waves (fixed order)
+  octet_colsum<NV>(acc, lane);
+#pragma unroll
+  for (int j = 0; j < NV / 8; ++j) part[wv][c][(lane >> 3) * (NV / 8) + j] = acc[j];
+  __syncthreads();
+  for (int t = tid; t < 8 * NV; t += kBv2Threads) {
+    const int cc = t / NV, idx = t % NV, b = idx / CN, i = idx % CN, gcc = cb * 8 + cc;
+    float sum = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NWV; ++w2) sum += part[w2][cc][idx];
+    if (b < B && gcc < nchunks) P2[((size_t)sp * B + b) * d + (size_t)gcc * CN + i] = sum;
+  }
+}
+
+// y[b][:] = sum over the S slices (fixed order), and each token's sum of
+// squares over the workgroup's 256 columns (for the next layer's RMS scale).
+// One wave per (column segment, token); four slices' loads in flight.
+constexpr int kRedCols = 256;
+template <int BM>
+__global__ __launch_bounds__(64) void breduce(const BatchArgs a, int S, const float* __restrict__ P2) {
+  const int b = blockIdx.y, seg = blockIdx.x, lane = threadIdx.x;
+  const int B = a.B, d = a.d_model;
+  const int c0 = seg * kRedCols + 4 * lane;
+  float ss = 0.f;
+  if (c0 < d) {  // d is a multiple of 4
+    const size_t step = (size_t)B * d;
+    const float* p = P2 + (size_t)b * d + c0;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 4 <= S; s += 4) {
+      f32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const f32x4*>(p + (size_t)(s + k) * step);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y += v[k];
+    }
+    for (; s < S; ++s) y += *reinterpret_cast<const f32x4*>(p + (size_t)s * step);
+    *reinterpret_cast<f32x4*>(a.yout + (size_t)b * d + c0) = y;
+    ss = ((y.x * y.x + y.y * y.y) + y.z * y.z) + y.w * y.w;
+  }
+  ss = wave_sum_dpp(ss);
+  if (lane == 0) a.ssp[(size_t)seg * BM + b] = ss;
+}
+
 // ---------------------------------------------------------------- trace
 // One workgroup per token: the selected list of the layer (scores above
 // theta, ascending), its length, theta and the normalised layer input.
@@ -631,7 +821,7 @@ __global__ __launch_bounds__(256) void btrace(const BatchArgs a, int32_t* counts
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct BatchLayout {
-  size_t H, P, scale, theta, umask, C, ybuf, ssp, total;
+  size_t H, P, scale, theta, umask, C, ybuf, ssp, P2, total;
 };
 
 // Workgroups of bpred and bgate: one per CU, more when a CU's share of the
@@ -660,7 +850,12 @@ static BatchLayout batch_layout(int64_t d_model, int64_t d_ff, int64_t B) {
   L.umask = take((size_t)G * 8);
   L.C = take((size_t)d_ff * kBatchMax * 4);
   L.ybuf = take((size_t)B * d_model * 4);
-  L.ssp = take((size_t)8192 * kBatchMax * 4);  // V workgroups (at most 8192) x token slots
+  L.ssp = take((size_t)8192 * kBatchMax * 4);  // reduce workgroups (at most 8192) x token slots
+  // bv2's slices x tokens x columns, for more than one token (bf16's wider
+  // chunks make fewer column blocks, hence more slices)
+  const int s4 = bv2_slices(d_model, 4), s8 = bv2_slices(d_model, 8);
+  const int64_t S = B <= 1 ? 0 : (s4 > s8 ? s4 : s8);
+  L.P2 = take((size_t)S * B * d_model * 4);
   L.total = off;
   return L;
 }
@@ -679,10 +874,22 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
   char* base = (char*)ws;
   const int G = batch_groups(s.d_ff);
   const int nchunks = (int)(s.d_model / CN);
-  int G3 = device_cu_count();  // bv: one or two output chunks per workgroup
-  if (G3 < 1) G3 = 256;
-  if (G3 > nchunks) G3 = nchunks;
-  if (2 * G3 < nchunks) G3 = (nchunks + 1) / 2;
+  // one token: bv, each workgroup one or two 16-byte output chunks;
+  // more: bv2 by (128-byte column block, union slice), then breduce by
+  // 256-column segment.  G3 counts the workgroups that leave a sum of
+  // squares per token.
+  constexpr bool kSmall = BM <= 1;
+  const int nblocks = (nchunks + 7) / 8;      // bv2 column blocks (128-byte lines)
+  const int S = bv2_slices(s.d_model, CN);    // bv2 union slices per block
+  int G3;
+  if (kSmall) {
+    G3 = device_cu_count();
+    if (G3 < 1) G3 = 256;
+    if (G3 > nchunks) G3 = nchunks;
+    if (2 * G3 < nchunks) G3 = (nchunks + 1) / 2;
+  } else {
+    G3 = (int)((s.d_model + kRedCols - 1) / kRedCols);
+  }
   // (BM token slots; the entry point keeps BM x max(r, d - r) x 4 within
   // kBatchMaxLds)
   const size_t lds1 = (size_t)BM * s.r * 4, lds2 = (size_t)BM * (s.d_model - s.r) * 4;
@@ -715,9 +922,16 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
     if (trace && (trace->counts || trace->idx || trace->theta || trace->q_in))
       hipLaunchKernelGGL(btrace, dim3((unsigned)B), dim3(256), 0, st, a, trace->counts, trace->idx,
                          trace->idx ? trace->cap : 0, trace->theta, trace->q_in, (int64_t)l, (int64_t)n_layers);
-    // bv overwrites ybuf (the input of this layer) only after bpred, bgate and
-    // the trace have read it: they precede it on the stream
-    hipLaunchKernelGGL((bv<W, BM>), dim3(G3), dim3(kBvThreads), 0, st, a, G);
+    // bv (or breduce) overwrites ybuf (the input of this layer) only after
+    // bpred, bgate and the trace have read it: they precede it on the stream
+    if constexpr (kSmall) {
+      hipLaunchKernelGGL((bv<W, BM>), dim3(G3), dim3(kBvThreads), 0, st, a, G);
+    } else {
+      hipLaunchKernelGGL((bv2<W, BM>), dim3((unsigned)(nblocks * S)), dim3(kBv2Threads), 0, st, a, G, S,
+                         (float*)(base + Lo.P2));
+      hipLaunchKernelGGL((breduce<BM>), dim3((unsigned)G3, (unsigned)B), dim3(64), 0, st, a, S,
+                         (const float*)(base + Lo.P2));
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

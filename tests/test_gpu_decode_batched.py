@@ -26,7 +26,8 @@ def test_batched_tiny_fp32_config():
     (512, 1000, 256, 80, 2, 5, "bf16"),   # d_ff not a multiple of the 32-neuron blocks, odd batch
     (1024, 4096, 512, 300, 4, 4, "f32"),
     (136, 300, 64, 29, 2, 3, "bf16"),     # ragged everywhere
-    (2304, 9216, 1152, 737, 2, 1, "bf16"),  # a batch of one
+    (2304, 9216, 1152, 737, 2, 1, "bf16"),  # a batch of one (the single-token V kernel)
+    (2304, 9216, 1152, 737, 2, 2, "bf16"),  # the smallest batch of the sliced V product
 ])
 def test_batched_shapes(dm, dff, r, k, L, B, dt):
     layers = [synth.ffn_layer(dm + dff + 1, l, dm, dff, r, dt) for l in range(L)]
