@@ -146,6 +146,30 @@ __global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int B = a.B, d = a.d_model, r = a.r;
   const int n0 = nfirst(blockIdx.x, a.d_ff, gridDim.x), n1 = nfirst(blockIdx.x + 1, a.d_ff, gridDim.x);
+  // scores: group gi (a half-wave) takes neurons n0 + 4 gi + u; lane l of the
+  // half takes the 16-byte chunks l, l + 32, ... of their K1 rows, in rounds
+  // of kRound chunks per neuron with all loads of a round issued before any
+  // is used.  The first round does not depend on the tokens: it is issued
+  // before their loads, so the two round trips overlap.
+  const int gi = tid >> 5, l32 = tid & 31;
+  const int CK = r / CN;
+  const size_t rowb = (size_t)r * sizeof(W);
+  const char* k1 = (const char*)a.k1t;
+  int nv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) nv[u] = min(n0 + 4 * gi + u, n1 - 1);  // slots past the range: a valid row, not stored
+  constexpr int kRound = 5;
+  u32x4 raw[kRound][4];
+  auto issue = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < kRound; ++k)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = min(c0 + 32 * k, CK - 1);
+        raw[k][u] = load16(k1 + (size_t)nv[u] * rowb + (size_t)c * 16);
+      }
+  };
+  issue(l32);
   // each token's RMS scale from the previous layer's per-workgroup sums of
   // squares (half-wave b, fixed order), and q[:r] of every token to LDS
   if (a.prenorm) {
@@ -173,33 +197,14 @@ __global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
 #pragma unroll
     for (int b = 0; b < BM; ++b)
       if (b < B) a.scale[b] = sc[b];
-  // scores: group gi (a half-wave) takes neurons n0 + 4 gi + u; lane l of the
-  // half takes the 16-byte chunks l, l + 32, ... of their K1 rows
-  const int gi = tid >> 5, l32 = tid & 31;
-  const int CK = r / CN;
-  const size_t rowb = (size_t)r * sizeof(W);
   float acc[4][BM];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int b = 0; b < BM; ++b) acc[u][b] = 0.f;
-  const char* k1 = (const char*)a.k1t;
-  int nv[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) nv[u] = min(n0 + 4 * gi + u, n1 - 1);  // slots past the range: a valid row, not stored
-  // the chunks of a thread in rounds of kRound per neuron, all loads of a
-  // round issued before any is used
   const f32x4* q4 = reinterpret_cast<const f32x4*>(qs);  // r is a multiple of 4
-  constexpr int kRound = 5;
   for (int c0 = l32; c0 < CK; c0 += 32 * kRound) {
-    u32x4 raw[kRound][4];
-#pragma unroll
-    for (int k = 0; k < kRound; ++k)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = min(c0 + 32 * k, CK - 1);
-        raw[k][u] = load16(k1 + (size_t)nv[u] * rowb + (size_t)c * 16);
-      }
+    if (c0 != l32) issue(c0);
 #pragma unroll
     for (int k = 0; k < kRound; ++k) {
       const int c = c0 + 32 * k;
@@ -268,21 +273,42 @@ __global__ __launch_bounds__(kBThreads) void bgate(const BatchArgs a) {
   const int B = a.B, d = a.d_model, r = a.r, rc = d - r;
   const int G = gridDim.x;
   const int n0 = nfirst(blockIdx.x, a.d_ff, G), n1 = nfirst(blockIdx.x + 1, a.d_ff, G);
+  // Everything that does not depend on theta is loaded first, in one round
+  // trip: the per-workgroup (mean, M2) of the scores (token b: half-wave b,
+  // lanes over workgroups), this group's scores, and q[r:] of every token.
+  const int gi = tid >> 5, l32 = tid & 31;
+  constexpr int KG = 8;  // workgroups per lane held in registers (one pass when G <= 256)
+  const bool one_pass = G <= 32 * KG;
+  float mn[KG], m2v[KG];
+  if (one_pass && gi < B) {
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const int g = l32 + 32 * k;
+      mn[k] = g < G ? a.P[((size_t)g * B + gi) * 2] : 0.f;
+      m2v[k] = g < G ? a.P[((size_t)g * B + gi) * 2 + 1] : 0.f;
+    }
+  }
+  float hv[4][BM];
+  int nv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    nv[u] = min(n0 + 4 * gi + u, n1 - 1);
+#pragma unroll
+    for (int b = 0; b < BM; ++b) hv[u][b] = (b < B) ? a.H[(size_t)b * a.d_ff + nv[u]] : 0.f;
+  }
+  for (int i = B * rc + tid; i < BM * rc; i += kBThreads) qs[i] = 0.f;  // empty token slots
+  load_tokens<BM, kBThreads>(a.yin, B, d, r, rc, qs, a.scale, nullptr);
   // theta of every token: the mean over all d_ff scores, then their sum of
-  // squared deviations, from the per-workgroup (mean, M2); token b is taken by
-  // the half-wave b (lanes over workgroups, fixed order), all loads first
+  // squared deviations, from the per-workgroup (mean, M2) (fixed order)
   {
-    const int b = tid >> 5, l32 = tid & 31;
-    constexpr int KG = 8;  // workgroups per lane held in registers (one pass when G <= 256)
+    const int b = gi;
     if (b < B) {
       float s1 = 0.f, s2 = 0.f, mu;
-      if (G <= 32 * KG) {
-        float mn[KG], m2v[KG], nn[KG];
+      if (one_pass) {
+        float nn[KG];
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
           const int g = l32 + 32 * k;
-          mn[k] = g < G ? a.P[((size_t)g * B + b) * 2] : 0.f;
-          m2v[k] = g < G ? a.P[((size_t)g * B + b) * 2 + 1] : 0.f;
           nn[k] = g < G ? (float)(nfirst(g + 1, a.d_ff, G) - nfirst(g, a.d_ff, G)) : 0.f;
         }
 #pragma unroll
@@ -326,25 +352,14 @@ __global__ __launch_bounds__(kBThreads) void bgate(const BatchArgs a) {
       if (l32 == 0) th[b] = mu + sqrtf(s2 / (float)a.d_ff) * a.z;
     }
   }
-  for (int i = B * rc + tid; i < BM * rc; i += kBThreads) qs[i] = 0.f;  // empty token slots
-  load_tokens<BM, kBThreads>(a.yin, B, d, r, rc, qs, a.scale, nullptr);
   __syncthreads();
   if (blockIdx.x == 0 && tid < B) a.theta[tid] = th[tid];
   // group gi: neurons n0 + 4 gi + u; the tokens selecting each, then one read
   // of the K2 row of a neuron selected by any of them
-  const int gi = tid >> 5, l32 = tid & 31;
   const int CK = rc / CN;
   const size_t rowb = (size_t)rc * sizeof(W);
   const char* k2 = (const char*)a.k2t;
-  float hv[4][BM];
   uint32_t sm[4];
-  int nv[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    nv[u] = min(n0 + 4 * gi + u, n1 - 1);
-#pragma unroll
-    for (int b = 0; b < BM; ++b) hv[u][b] = (b < B) ? a.H[(size_t)b * a.d_ff + nv[u]] : 0.f;
-  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     sm[u] = 0;
