@@ -39,6 +39,16 @@ def test_stat_topk_shapes(d, k):
     run_and_compare(x, k)
 
 
+@pytest.mark.parametrize("rows,d,k,cap", [(7001, 4096, 300, None), (6200, 8192, 650, 300), (6145, 9216, 737, 1474)])
+def test_stat_topk_many_rows_every_row(rows, d, k, cap):
+    """Thousands of rows whose length fills whole 16-byte lanes, every row
+    against the oracle: row counts that are not a multiple of the resident
+    workgroups, and a list capacity below the count (cap 300 at k 650)."""
+    x = synth.stat_rows(rows + d, rows, d)
+    _, got, want = run_and_compare(x, k, cap=cap)
+    assert np.abs(got.astype(np.int64) - want.astype(np.int64)).max() <= 2
+
+
 def test_stat_topk_config_rows_both_sets():
     """BASELINE's statistical top-k workload (65536 x 9216, k = 737), Gaussian and
     Student-t rows: all rows on the GPU, a sample of rows against the oracle;
