@@ -89,52 +89,45 @@ __device__ __forceinline__ void process_row(const float (&v)[E][4], int64_t row,
   for (int w = 0; w < NW; ++w) m2 += S.red[1][w];
   const float theta = mean + sqrtf(m2 / (float)d) * z;
 
-  // survivors of chunk e as a 4-bit mask per lane, their prefix within the
-  // wave, and the per-wave totals
-  int pre[E], msk[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
+  // survivors of chunk e as a 4-bit mask per lane.  Pass A publishes each
+  // (wave, chunk) total; pass B forms the masks and their in-wave prefix scans
+  // again (rather than holding them across the barrier), adds the totals of
+  // the earlier chunks and waves, and places every survivor at its ascending
+  // slot without a serial walk.
+  auto survivors = [&](int e) {
     int m = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) m |= ((EXACT || 4 * tid + 4 * NT * e + j < d) && v[e][j] > theta) ? (1 << j) : 0;
     // opaque: later tests read the bits rather than keeping the compares
     asm volatile("" : "+v"(m));
-    const int c = __builtin_popcount(m);
-    const int incl = wave_incl_scan_dpp(c);
-    msk[e] = m;
-    pre[e] = incl - c;
+    return m;
+  };
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int incl = wave_incl_scan_dpp(__builtin_popcount(survivors(e)));
     if (lane == kWave - 1) S.wtot[wv][e] = incl;
   }
   __syncthreads();
-  // totals of every chunk and of the waves before this one, one wave of the
-  // table at a time (a fully unrolled walk would hold NW x E values)
-  int before[E], all[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) before[e] = all[e] = 0;
-#pragma unroll(NW <= 4 ? NW : 1)
-  for (int w = 0; w < NW; ++w) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int t = S.wtot[w][e];
-      before[e] += (w < wv) ? t : 0;
-      all[e] += t;
-    }
-  }
-  int base = 0;
+  int base = 0;  // survivors of the chunks before e, all waves
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    pre[e] += base + before[e];
-    base += all[e];
-  }
-  if (idx != nullptr || vals != nullptr) {
-    // slot of survivor (e, j) of this lane: the chunk's prefix plus this
-    // lane's survivors before it in the chunk (no serial dependence)
-#pragma unroll
-    for (int e = 0; e < E; ++e)
+    int before = 0, all = 0;
+#pragma unroll(NW <= 4 ? NW : 1)
+    for (int w = 0; w < NW; ++w) {
+      const int t = S.wtot[w][e];
+      before += (w < wv) ? t : 0;
+      all += t;
+    }
+    if (idx != nullptr || vals != nullptr) {
+      const int m = survivors(e);
+      const int c = __builtin_popcount(m);
+      const int pre = base + before + wave_incl_scan_dpp(c) - c;
+      // slot of survivor (e, j): the chunk's prefix plus this lane's
+      // survivors before it in the chunk
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (msk[e] & (1 << j)) {
-          const int pos = pre[e] + __builtin_popcount(msk[e] & ((1 << j) - 1));
+        if (m & (1 << j)) {
+          const int pos = pre + __builtin_popcount(m & ((1 << j) - 1));
           const int i = 4 * tid + 4 * NT * e + j;
           if (pos < kStage) {
             S.s_idx[pos] = i;
@@ -144,6 +137,8 @@ __device__ __forceinline__ void process_row(const float (&v)[E][4], int64_t row,
             if (vals) vals[row * cap + pos] = v[e][j] - theta;
           }
         }
+    }
+    base += all;
   }
   if (tid == 0) {
     counts[row] = base;
