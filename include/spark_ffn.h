@@ -127,9 +127,11 @@ int spark_ffn_decode(const spark_ffn_shape *s, const spark_ffn_weights *layers, 
  * same trace layout with T = B), with the batch processed layer by layer: one
  * read of K1 per layer serves all B tokens, and the K2 and V rows of a neuron
  * are read once for all the tokens that select it (the union of the
- * per-token selected sets).  Three kernels per layer on `stream` (a fourth
- * when a trace is asked for); results equal spark_ffn_decode's up to the
- * order of fp32 sums.
+ * per-token selected sets).  Per layer on `stream`: the predictor kernel, the
+ * gate kernel, then the V product — one kernel for B = 1, a sliced product and
+ * a fixed-order reduction of the slices for B >= 2 — plus one kernel when a
+ * trace is asked for; results equal spark_ffn_decode's up to the order of
+ * fp32 sums.
  * Requires 0 <= B <= 8, d_model <= 8192, d_ff <= 65536,
  * P * max(r, d_model - r) * 4 <= 65536 with P = B rounded up to a power of
  * two (the token slots of the kernels), q and y 16-byte aligned, and the
@@ -199,7 +201,9 @@ int spark_attn_prefill(const void *q, const void *k1, const void *k2, const void
                        int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float *out, int32_t *counts, float *theta,
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace sizes (bytes) for the calls above with the same arguments. */
+/* Workspace sizes (bytes) for the calls above with the same arguments, on the
+ * current device: some depend on its compute-unit count, and every call checks
+ * ws_bytes against the size for the device current when it is made. */
 int spark_ffn_decode_workspace_size(const spark_ffn_shape *s, int n_layers, int64_t T, size_t *bytes);
 int spark_ffn_decode_batched_workspace_size(const spark_ffn_shape *s, int64_t B, size_t *bytes);
 int spark_ffn_prefill_workspace_size(const spark_ffn_shape *s, int64_t T, size_t *bytes);
