@@ -5,6 +5,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "internal.hpp"
 
 namespace spark {
 
@@ -101,7 +102,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
   // Two register sets of staged 16-byte chunks (stage s in set s & 1).
   // Chunk i of a stage belongs to step i % 4 of the stage that moves it.
   // Chunks past K are loaded from column 0 and zeroed when stored to LDS.
-  static_assert(CA % 4 == 0 && CB % 4 == 0, "chunks split over the four steps of a stage");
+  // (chunk i moves in step i % 4: any count works; multiples of 4 keep the
+  // four steps even)
   u32x4 ra[2][CA], rb[2][CB];
   auto gload_part = [&](int set, int k0, int part) {
 #pragma unroll
@@ -317,20 +319,39 @@ static __global__ __launch_bounds__(256) void transpose_bf16_x8(const bf16_t* __
   }
 }
 
-// Tile configuration of the prefill products: 128 x 128 per workgroup, four
-// waves of 64 x 64.  (Two waves of 128 x 64, at one wave per SIMD, measured
-// slower: too little to hide the LDS and global latencies.)
+// Tile configurations of the prefill products.  General: 128 x 128 per
+// workgroup, four waves of 64 x 64 (two workgroups per CU).  Large single
+// products: 256 x 192, eight waves of 64 x 96 (one workgroup per CU, 126 KB of
+// LDS; a wave reads five fragments per six MFMAs instead of four per four),
+// used when its tiles fill every CU at least once — at 4096 x 9216 that is
+// 768 tiles, three full rounds (104 against 117 us for K = 1152).  (Two waves
+// of 128 x 64, at one wave per SIMD, measured slower: too little to hide the
+// LDS and global latencies; 256 x 256 and 192 x 256 tiles leave a partly
+// filled last round at 4096 x 9216.)
 constexpr int kWM = 2, kWN = 2, kMI = 2, kNI = 2;
 constexpr int kBM = kWM * kMI * 32, kBN = kWN * kNI * 32;
+constexpr int kWM2 = 4, kWN2 = 2, kMI2 = 2, kNI2 = 3;
+constexpr int kBM2 = kWM2 * kMI2 * 32, kBN2 = kWN2 * kNI2 * 32;
 
 // Launch over batch `batch` (grid z) and `splits` K splits (grid y).
 template <int EPI>
 inline hipError_t launch_gemm(GemmArgs a, int splits, int batch, hipStream_t st) {
-  const int tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
-  const int grid = (tiles + 7) / 8 * 8;  // a multiple of the XCD count (see gemm_bf16_nt)
   int ks = (a.K + splits - 1) / splits;
   a.ksplit = (ks + GBK - 1) / GBK * GBK;
   if (a.bgroup < 1) a.bgroup = 1;
+  if constexpr (EPI != kEpiAttn) {
+    int cus = device_cu_count();
+    if (cus < 1) cus = 256;
+    const int64_t big = (int64_t)((a.M + kBM2 - 1) / kBM2) * ((a.N + kBN2 - 1) / kBN2);
+    if (splits == 1 && batch == 1 && a.causal == kCausalNone && big >= cus) {
+      const int grid = (int)((big + 7) / 8 * 8);  // a multiple of the XCD count (see gemm_bf16_nt)
+      hipLaunchKernelGGL((gemm_bf16_nt<EPI, kWM2, kWN2, kMI2, kNI2>), dim3(grid, 1, 1), dim3(kWM2 * kWN2 * 64), 0,
+                         st, a);
+      return hipGetLastError();
+    }
+  }
+  const int tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+  const int grid = (tiles + 7) / 8 * 8;  // a multiple of the XCD count (see gemm_bf16_nt)
   hipLaunchKernelGGL((gemm_bf16_nt<EPI, kWM, kWN, kMI, kNI>), dim3(grid, splits, batch), dim3(kWM * kWN * 64), 0,
                      st, a);
   return hipGetLastError();

@@ -54,6 +54,17 @@ def test_prefill_shapes(dm, dff, r, k, T):
     run_prefill(dm, dff, r, k, T, dm + T)
 
 
+def test_prefill_large_tiles_ragged():
+    """Enough tokens for the 256 x 192 product tiles (ceil(3000/256) x
+    ceil(4096/192) = 264 tiles, at least one per CU) with both edges ragged:
+    the last tile row holds 184 tokens and the last tile column 64 neurons.
+    A sample of tokens, every fourth of the last tile row included."""
+    T = 3000
+    rng = np.random.default_rng(5)
+    sample = np.unique(np.concatenate([rng.choice(2816, 60, replace=False), np.arange(2816, T, 4), [T - 1]]))
+    run_prefill(512, 4096, 256, 330, T, 11, sample)
+
+
 def test_prefill_deterministic():
     layer = [to_dev(a) for a in synth.ffn_layer(3, 0, 2304, 9216, 1152, "bf16")]
     Q = to_dev(synth.queries(3, 512, 2304, "bf16"))
