@@ -41,7 +41,7 @@ struct PrefillLayout {
   size_t H, C, Vt, P, counts, theta, total;
 };
 
-constexpr int kOutSplit = 2;  // K splits of the C V product (its tile grid alone is ~2.25 tiles per CU)
+constexpr int kOutSplit = 4;  // K splits of the C V product (4096 x 2304: 192 tiles of 256 x 192, 768 with the splits)
 
 static PrefillLayout prefill_layout(int64_t d_model, int64_t d_ff, int64_t T) {
   PrefillLayout L;

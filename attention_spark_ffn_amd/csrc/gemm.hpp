@@ -323,8 +323,9 @@ static __global__ __launch_bounds__(256) void transpose_bf16_x8(const bf16_t* __
 // workgroup, four waves of 64 x 64 (two workgroups per CU).  Large single
 // products: 256 x 192, eight waves of 64 x 96 (one workgroup per CU, 126 KB of
 // LDS; a wave reads five fragments per six MFMAs instead of four per four),
-// used when its tiles fill every CU at least once — at 4096 x 9216 that is
-// 768 tiles, three full rounds (104 against 117 us for K = 1152).  (Two waves
+// used when its tiles times the K splits fill every CU at least once — at
+// 4096 x 9216 that is 768 tiles, three full rounds (104 against 117 us for
+// K = 1152); at 4096 x 2304 with four K splits, 768 workgroups.  (Two waves
 // of 128 x 64, at one wave per SIMD, measured slower: too little to hide the
 // LDS and global latencies; 256 x 256 and 192 x 256 tiles leave a partly
 // filled last round at 4096 x 9216.)
@@ -343,10 +344,10 @@ inline hipError_t launch_gemm(GemmArgs a, int splits, int batch, hipStream_t st)
     int cus = device_cu_count();
     if (cus < 1) cus = 256;
     const int64_t big = (int64_t)((a.M + kBM2 - 1) / kBM2) * ((a.N + kBN2 - 1) / kBN2);
-    if (splits == 1 && batch == 1 && a.causal == kCausalNone && big >= cus) {
+    if (batch == 1 && a.causal == kCausalNone && big * splits >= cus) {
       const int grid = (int)((big + 7) / 8 * 8);  // a multiple of the XCD count (see gemm_bf16_nt)
-      hipLaunchKernelGGL((gemm_bf16_nt<EPI, kWM2, kWN2, kMI2, kNI2>), dim3(grid, 1, 1), dim3(kWM2 * kWN2 * 64), 0,
-                         st, a);
+      hipLaunchKernelGGL((gemm_bf16_nt<EPI, kWM2, kWN2, kMI2, kNI2>), dim3(grid, splits, 1), dim3(kWM2 * kWN2 * 64),
+                         0, st, a);
       return hipGetLastError();
     }
   }

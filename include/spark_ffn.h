@@ -152,7 +152,8 @@ int spark_ffn_decode_batched(const spark_ffn_shape *s, const spark_ffn_weights *
  *   (its q_in is ignored).
  * Requires bf16 weights and Q, d_ff a multiple of 256, r a multiple of 64,
  * d_model a multiple of 8, d_model <= 8192, d_ff <= 65536.  The workspace
- * holds the scores, the gated values and a transposed copy of V.
+ * holds the scores, the gated values, a transposed copy of V and the K-split
+ * partial sums of the output (added in a fixed order).
  */
 int spark_ffn_prefill(const spark_ffn_shape *s, const spark_ffn_weights *w, const void *Q, int64_t T, float *Y,
                       const spark_ffn_trace *trace, void *ws, size_t ws_bytes, hipStream_t stream);
