@@ -217,17 +217,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
         }
       }
     }
+    // the scores of all NI blocks of this row of blocks, loaded before any
+    // is used (one round trip per row of blocks, not one per block)
+    float hvs[EPI != kEpiStore ? NI : 1][16];
+    if (EPI != kEpiStore) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int n = n0 + wn * NI * 32 + j * 32 + (lane & 31);
-      float hv[16];
-      if (EPI != kEpiStore) {  // all 16 score loads of the block before any use
+      for (int j = 0; j < NI; ++j) {
+        const int n = min(n0 + wn * NI * 32 + j * 32 + (lane & 31), N - 1);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * MI * 32 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          hv[r] = H[(size_t)min(m, M - 1) * g.ldh + min(n, N - 1)];
+          hvs[j][r] = H[(size_t)min(m, M - 1) * g.ldh + n];
         }
       }
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int n = n0 + wn * NI * 32 + j * 32 + (lane & 31);
+      const float* hv = hvs[EPI != kEpiStore ? j : 0];
       // row of register r: mb + 8 (r / 4) + r % 4; one address per block,
       // constant row offsets per register; the gates are selects (the
       // arithmetic runs for every element, as a wave with any selected lane
