@@ -51,7 +51,8 @@ def test_attn_config(n):
     (8, 4, 257, 256, 128, 256),     # one past the boundary
     (4, 4, 1000, 128, 64, 100),     # no grouping, ragged
     (8, 2, 5000, 64, 32, 300),      # group of 4
-    (2, 1, 70000, 256, 128, 512),   # long context
+    (8, 4, 10000, 256, 128, 256),   # 128-token chunks (79 of them, the last 16 tokens long)
+    (2, 1, 70000, 256, 128, 512),   # long context, 256-token chunks (the last 112 tokens long)
     (1, 1, 33, 16, 8, 8),           # tiny
 ])
 def test_attn_shapes(Hq, Hkv, n, hd, r, ka):
