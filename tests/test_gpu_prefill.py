@@ -65,6 +65,17 @@ def test_prefill_large_tiles_ragged():
     run_prefill(512, 4096, 256, 330, T, 11, sample)
 
 
+def test_prefill_large_tiles_full_width_ragged():
+    """The full-width layer (2304 x 9216, r 1152, k 737) over 2900 tokens: the
+    scores and gate products on 256 x 192 tiles (12 x 48) and the C V product
+    on 256 x 192 tiles in four K splits (12 x 12 x 4), the last tile row 84
+    tokens deep.  A sample of tokens including the last tile row."""
+    T = 2900
+    rng = np.random.default_rng(6)
+    sample = np.unique(np.concatenate([rng.choice(2816, 24, replace=False), np.arange(2816, T, 6), [T - 1]]))
+    run_prefill(2304, 9216, 1152, 737, T, 12, sample)
+
+
 def test_prefill_deterministic():
     layer = [to_dev(a) for a in synth.ffn_layer(3, 0, 2304, 9216, 1152, "bf16")]
     Q = to_dev(synth.queries(3, 512, 2304, "bf16"))
