@@ -251,16 +251,17 @@ __global__ __launch_bounds__(256) void attn_chunk(const bf16_t* __restrict__ q, 
     for (int e = tid; e < cnt; e += 256) lidx[(size_t)h * n_ctx + j0 + e] = j0 + loc[e];
 }
 
-// One 1024-thread workgroup per query head.  The chunk statistics are read in
-// parallel; the weighted column sums run in four quarters of the chunks (chunk
-// c in quarter c % 4, eight loads in flight per thread) combined in a fixed
-// order.
+// One 1024-thread workgroup per query head.  The chunk statistics (m_c, l_c,
+// count) are read in one parallel pass; the weighted column sums run in four
+// quarters of the chunks (chunk c in quarter c % 4, up to sixteen loads in
+// flight per thread) combined in a fixed order.
 template <int kChunk>
 __global__ __launch_bounds__(1024) void attn_merge(int n_ctx, int hd, const float* __restrict__ part,
                                                    const int32_t* __restrict__ lidx, float* __restrict__ out,
                                                    int32_t* __restrict__ counts, int32_t* __restrict__ idx_out,
                                                    int64_t cap, float* __restrict__ theta_out) {
   __shared__ float wexp[kMaxChunks];  // m_c, then e^(m_c - m)
+  __shared__ float lsum[kMaxChunks];  // l_c
   __shared__ int ccnt[kMaxChunks];
   __shared__ float red[16];
   __shared__ int ired[16];
@@ -274,8 +275,10 @@ __global__ __launch_bounds__(1024) void attn_merge(int n_ctx, int hd, const floa
   int cn = 0;
   for (int c = tid; c < nch; c += 1024) {
     const float mc = ph[(size_t)c * stride];
+    const float lc = ph[(size_t)c * stride + 1];
     const int k = __float_as_int(ph[(size_t)c * stride + 2]);
     wexp[c] = mc;
+    lsum[c] = lc;
     ccnt[c] = k;
     mx = fmaxf(mx, mc);
     cn += k;
@@ -301,7 +304,7 @@ __global__ __launch_bounds__(1024) void attn_merge(int n_ctx, int hd, const floa
     const float mc = wexp[c];
     const float w = mc == -INFINITY ? 0.f : __expf(mc - m);
     wexp[c] = w;
-    dsum += w * ph[(size_t)c * stride + 1];
+    dsum += w * lsum[c];
   }
   dsum = wave_sum_dpp(dsum);
   if (lane == 0) red[wv] = dsum;
@@ -316,6 +319,13 @@ __global__ __launch_bounds__(1024) void attn_merge(int n_ctx, int hd, const floa
     float o = 0.f;
     if (col < hd) {
       int c = quarter;
+      for (; c + 60 < nch; c += 64) {
+        float x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) x[u] = ph[(size_t)(c + 4 * u) * stride + kPartHead + col];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) o += wexp[c + 4 * u] * x[u];
+      }
       for (; c + 28 < nch; c += 32) {
         float x[8];
 #pragma unroll
