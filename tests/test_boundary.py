@@ -173,3 +173,21 @@ def test_attention_prefill_rejects_bad_arguments():
     ws = ctypes.create_string_buffer(16)
     assert L.spark_attn_prefill(None, None, None, None, 64, 8, 4, 256, 128, 256, None, None, None, ws, 16,
                                 None) == sf.SPARK_EINVAL
+
+
+def test_empty_prefills():
+    """A prefill of no tokens is a no-op that enqueues nothing (T >= 0); an
+    attention prefill needs at least one position (1 <= T <= 16384)."""
+    L = sf.lib()
+    vp = ctypes.c_void_p(256)
+    s = _shape(d_model=512, d_ff=1024, r=256, k=80, wdtype=sf.SPARK_BF16)
+    w = sf.WeightsC(256, 256, 256)
+    n = ctypes.c_size_t(0)
+    assert L.spark_ffn_prefill_workspace_size(ctypes.byref(s), 0, ctypes.byref(n)) == sf.SPARK_OK
+    assert L.spark_ffn_prefill(ctypes.byref(s), ctypes.byref(w), vp, 0, vp, None, vp, 1 << 30, None) == sf.SPARK_OK
+    assert L.spark_ffn_prefill(ctypes.byref(s), ctypes.byref(w), vp, -1, vp, None, vp, 1 << 30, None) == sf.SPARK_EINVAL
+    P = L.spark_attn_prefill_workspace_size
+    assert P(0, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EINVAL
+    assert P(16385, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED
+    assert L.spark_attn_prefill(vp, vp, vp, vp, 0, 8, 4, 256, 128, 256, vp, None, None, vp, 1 << 30,
+                                None) == sf.SPARK_EINVAL
