@@ -12,7 +12,10 @@ Entry points (same names as the C ABI):
   spark_ffn_decode_batched(q, layers, k, r, eps, ...)  -> the same, B <= 8 tokens layer by layer
   spark_ffn_prefill(Q, layer, k, r, ...)            -> Y  (and a trace dict)
   spark_attn_decode(q, k1, k2, v, k_attn, cap=None) -> (out, counts, idx, theta)
-  spark_attn_prefill(q, k1, k2, v, k_attn)          -> (out, counts, theta)
+  spark_attn_prefill(q, k1, k2, v, k_attn, cap=0)   -> (out, counts, idx, theta)
+
+Workspaces are cached per (kind, device, stream), so calls on different
+streams never share one.
 """
 from __future__ import annotations
 
@@ -78,6 +81,8 @@ def lib() -> ctypes.CDLL:
                 L.spark_attn_decode.restype = _ci
                 L.spark_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
                                                 _vp, _i64, _vp, _vp, _sz, _vp]
+                L.spark_ffn_decode_tags.restype = _i64
+                L.spark_ffn_decode_tags.argtypes = [_ci, _i64]
                 L.spark_ffn_decode_workspace_size.restype = _ci
                 L.spark_ffn_decode_workspace_size.argtypes = [ctypes.POINTER(ShapeC), _ci, _i64,
                                                               ctypes.POINTER(_sz)]
@@ -87,9 +92,9 @@ def lib() -> ctypes.CDLL:
                 L.spark_attn_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_sz)]
                 L.spark_attn_prefill.restype = _ci
                 L.spark_attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
-                                                 _vp, _vp, _sz, _vp]
+                                                 _vp, _i64, _vp, _vp, _sz, _vp]
                 L.spark_attn_prefill_workspace_size.restype = _ci
-                L.spark_attn_prefill_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64,
+                L.spark_attn_prefill_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                                                 ctypes.POINTER(_sz)]
                 _lib = L
     return _lib
@@ -154,19 +159,73 @@ def stat_topk(x: torch.Tensor, k: int, cap: int | None = None):
     return vals, idx, counts, theta
 
 
-# ---------------------------------------------------------------------------- decode
+# ---------------------------------------------------------------------------- workspaces
 _ws_cache: dict = {}
+
+TAG_LIMIT = (1 << 32) - 1  # exchange tags are 32-bit; tag 0 is what a zeroed workspace holds
+
+
+def _ws_key(kind: str, device):
+    return (kind, device, torch.cuda.current_stream(device).cuda_stream)
 
 
 def _cached_workspace(kind: str, device, nbytes: int) -> torch.Tensor:
-    """Per-device workspace, zero-filled once when created and then carried
-    between calls (the decode kernel keeps a sequence counter in it)."""
-    key = (kind, device)
+    """Workspace for one (kind, device, stream), zero-filled when created."""
+    key = _ws_key(kind, device)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
+
+
+class DecodeWorkspace:
+    """A decode workspace with its host-side bookkeeping: the exchange tags the
+    calls on it have used since it was last zeroed (it is zeroed again, on its
+    stream, before they would pass 2^32 - 1), and the failed-call count the
+    host last saw (the kernel counts failed calls in the 8-byte word at byte
+    offset 16)."""
+
+    def __init__(self, buf: torch.Tensor):
+        self.buf = buf
+        self.tags_used = 0
+        self.failures_seen = 0
+
+    def reserve(self, tags: int) -> bool:
+        """Account for a call that uses `tags` tags; returns True when the
+        workspace must be zeroed first (the count then restarts)."""
+        reset = self.tags_used + tags > TAG_LIMIT
+        if reset:
+            self.tags_used = 0
+        self.tags_used += tags
+        return reset
+
+    def failures(self) -> int:
+        """Failed calls recorded in the workspace (reads it: synchronises)."""
+        return int(self.buf[16:24].view(torch.int64).item())
+
+    def new_failures(self) -> int:
+        """Failed calls recorded since this was last asked (synchronises)."""
+        n = self.failures()
+        d, self.failures_seen = n - self.failures_seen, n
+        return d
+
+
+def decode_tags(n_layers: int, T: int) -> int:
+    """Exchange tags one spark_ffn_decode call uses (the library's count)."""
+    return int(lib().spark_ffn_decode_tags(int(n_layers), int(T)))
+
+
+def _decode_workspace(device, nbytes: int) -> DecodeWorkspace:
+    key = _ws_key("decode", device)
+    dw = _ws_cache.get(key)
+    if dw is None or dw.buf.numel() < nbytes:
+        dw = DecodeWorkspace(torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device))
+        _ws_cache[key] = dw
+    return dw
+
+
+# ---------------------------------------------------------------------------- decode
 
 
 def _shape(d_model, d_ff, r, k, wd) -> ShapeC:
@@ -203,15 +262,20 @@ def _trace_buffers(T: int, L: int, d_ff: int, d_model: int, cap, dev):
 
 
 def spark_ffn_decode(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6, trace: bool = False,
-                     cap: int | None = None, ws: torch.Tensor | None = None):
+                     cap: int | None = None, ws: torch.Tensor | DecodeWorkspace | None = None, check: bool = True):
     """Run the stack of Spark FFN layers on T independent tokens.
 
     q [T][d_model] fp32; layers: list of (k1t [d_ff][r], k2t [d_ff][d_model-r],
     v [d_ff][d_model]) tensors, all bf16 or all fp32.  Returns y [T][d_model]
     fp32 (last layer, before normalisation).  With trace=True also returns a
     dict with counts [T][L], idx [T][L][cap], theta [T][L], q_in [T][L][d_model].
-    ws: optional zero-initialised uint8 workspace to use (and carry) instead of
-    the module's cached one.
+    ws: optional workspace to use (and carry) instead of the cached one of
+    this device and stream: a DecodeWorkspace, or a zero-filled uint8 tensor
+    (the caller then keeps its tag count below 2^32; see decode_tags).
+    check: synchronise after the call and raise if the kernel recorded a
+    failed exchange (a grid that could not make progress) since the
+    workspace's count was last read; with check=False the caller reads
+    DecodeWorkspace.new_failures() itself.
     """
     T, d_model, L, d_ff, shape, wts = _stack_args(q, layers, k, r)
     need = ctypes.c_size_t(0)
@@ -219,15 +283,24 @@ def spark_ffn_decode(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6,
            "spark_ffn_decode_workspace_size")
     dev = q.device
     if ws is None:
-        ws = _cached_workspace("decode", dev, need.value)
+        ws = _decode_workspace(dev, need.value)
+    elif isinstance(ws, torch.Tensor):
+        ws = DecodeWorkspace(ws)
+    if ws.reserve(decode_tags(L, T)):
+        ws.buf.zero_()
+        ws.failures_seen = 0
     y = torch.empty((T, d_model), dtype=torch.float32, device=dev)
     tr = None
     trc = None
     if trace:
         tr, trc = _trace_buffers(T, L, d_ff, d_model, cap, dev)
     st = lib().spark_ffn_decode(ctypes.byref(shape), wts, L, _p(q), T, _p(y), float(eps),
-                                ctypes.byref(trc) if trc is not None else None, _p(ws), ws.numel(), _stream(dev))
+                                ctypes.byref(trc) if trc is not None else None, _p(ws.buf), ws.buf.numel(),
+                                _stream(dev))
     _check(st, "spark_ffn_decode")
+    if check and ws.new_failures():
+        raise RuntimeError("spark_ffn_decode: a grid-wide exchange timed out (the device could not keep the "
+                           "whole grid running); the output holds NaN")
     return (y, tr) if trace else y
 
 
@@ -252,14 +325,16 @@ def spark_ffn_decode_batched(q: torch.Tensor, layers, k: int, r: int, eps: float
     return (y, tr) if trace else y
 
 
-def decode_workspace_failed(ws: torch.Tensor | None = None, device=None) -> bool:
-    """True if a decode kernel that used this workspace recorded a timeout
-    (reads the workspace header; synchronises)."""
+def decode_workspace_failed(ws: torch.Tensor | DecodeWorkspace | None = None, device=None) -> bool:
+    """True if a decode kernel that used this workspace (by default the cached
+    one of the device and its current stream) recorded a failed call (reads
+    the workspace header; synchronises)."""
     if ws is None:
-        ws = _ws_cache.get(("decode", device or torch.device("cuda", torch.cuda.current_device())))
+        ws = _ws_cache.get(_ws_key("decode", device or torch.device("cuda", torch.cuda.current_device())))
         if ws is None:
             return False
-    return int(ws[8:16].view(torch.int64).item()) != 0
+    buf = ws.buf if isinstance(ws, DecodeWorkspace) else ws
+    return int(buf[16:24].view(torch.int64).item()) != 0
 
 
 # ---------------------------------------------------------------------------- prefill
@@ -268,12 +343,17 @@ def spark_ffn_prefill(Q: torch.Tensor, layer, k: int, r: int, trace: bool = Fals
     (k1t, k2t, v) bf16.  Returns Y [T][d_model] fp32 (and with trace=True a dict
     with counts [T], idx [T][cap], theta [T])."""
     _need_cuda(Q, *layer)
+    if Q.dim() != 2:
+        raise ValueError("Q must be [T][d_model]")
     T, d_model = Q.shape
     k1t, k2t, v = layer
     d_ff = v.shape[0]
     wd = _wdtype(k1t)
-    if Q.dtype != k1t.dtype:
-        raise TypeError("Q must have the weights' dtype")
+    if Q.dtype != k1t.dtype or any(a.dtype != k1t.dtype for a in layer):
+        raise TypeError("Q and the weights must share one dtype")
+    if k1t.shape != (d_ff, r) or k2t.shape != (d_ff, d_model - r) or v.shape != (d_ff, d_model):
+        raise ValueError("weight shapes do not match Q / r: need k1t [d_ff][r], k2t [d_ff][d_model-r], "
+                         "v [d_ff][d_model]")
     shape = _shape(d_model, d_ff, r, k, wd)
     w = WeightsC(k1t.data_ptr(), k2t.data_ptr(), v.data_ptr())
     need = ctypes.c_size_t(0)
@@ -306,8 +386,12 @@ def spark_attn_decode(q: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor, v: to
     for t in (q, k1, k2, v):
         if t.dtype != torch.bfloat16:
             raise TypeError("attention inputs must be bf16")
+    if q.dim() != 2 or k1.dim() != 3:
+        raise ValueError("q must be [Hq][hd] and k1 [Hkv][n_ctx][r]")
     Hq, hd = q.shape
     Hkv, n, r = k1.shape
+    if k2.shape != (Hkv, n, hd - r) or v.shape != (Hkv, n, hd):
+        raise ValueError("cache shapes do not match: need k2 [Hkv][n_ctx][hd-r], v [Hkv][n_ctx][hd]")
     cap = min(n, 4096) if cap is None else int(cap)
     need = ctypes.c_size_t(0)
     _check(lib().spark_attn_workspace_size(Hq, Hkv, n, hd, r, int(k_attn), ctypes.byref(need)),
@@ -324,27 +408,36 @@ def spark_attn_decode(q: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor, v: to
     return out, counts, idx, theta
 
 
-def spark_attn_prefill(q: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor, v: torch.Tensor, k_attn: int):
+def spark_attn_prefill(q: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor, v: torch.Tensor, k_attn: int,
+                       cap: int = 0):
     """Causal Spark attention over a prompt.  q [T][Hq][hd] bf16; k1 [Hkv][T][r],
     k2 [Hkv][T][hd-r], v [Hkv][T][hd] bf16.  Returns out [T][Hq][hd] fp32,
-    counts [T][Hq] and theta [T][Hq] (NaN where t + 1 <= k_attn)."""
+    counts [T][Hq], idx [T][Hq][cap] (the attended positions of each row,
+    ascending, -1 padded; None when cap = 0) and theta [T][Hq] (NaN where
+    t + 1 <= k_attn)."""
     _need_cuda(q, k1, k2, v)
     for t in (q, k1, k2, v):
         if t.dtype != torch.bfloat16:
             raise TypeError("attention inputs must be bf16")
+    if q.dim() != 3 or k1.dim() != 3:
+        raise ValueError("q must be [T][Hq][hd] and k1 [Hkv][T][r]")
     T, Hq, hd = q.shape
     Hkv, n, r = k1.shape
     if n != T:
         raise ValueError("the cache must hold the T prompt positions")
+    if k2.shape != (Hkv, T, hd - r) or v.shape != (Hkv, T, hd):
+        raise ValueError("cache shapes do not match: need k2 [Hkv][T][hd-r], v [Hkv][T][hd]")
+    cap = int(cap)
     need = ctypes.c_size_t(0)
-    _check(lib().spark_attn_prefill_workspace_size(T, Hq, Hkv, hd, r, int(k_attn), ctypes.byref(need)),
+    _check(lib().spark_attn_prefill_workspace_size(T, Hq, Hkv, hd, r, int(k_attn), cap, ctypes.byref(need)),
            "spark_attn_prefill_workspace_size")
     dev = q.device
     ws = _cached_workspace("attn_prefill", dev, need.value)
     out = torch.empty((T, Hq, hd), dtype=torch.float32, device=dev)
     counts = torch.empty((T, Hq), dtype=torch.int32, device=dev)
     theta = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, Hq, cap), dtype=torch.int32, device=dev) if cap > 0 else None
     st = lib().spark_attn_prefill(_p(q), _p(k1), _p(k2), _p(v), T, Hq, Hkv, hd, r, int(k_attn), _p(out), _p(counts),
-                                  _p(theta), _p(ws), ws.numel(), _stream(dev))
+                                  _p(idx), cap, _p(theta), _p(ws), ws.numel(), _stream(dev))
     _check(st, "spark_attn_prefill")
-    return out, counts, theta
+    return out, counts, idx, theta

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <mutex>
 
 #include "internal.hpp"
@@ -35,7 +36,13 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SPARK_OK : SPARK_EHIP; }
 
 int check_ffn_shape(const spark_ffn_shape* s) {
   if (!s) return SPARK_EINVAL;
-  if (s->wdtype != SPARK_F32 && s->wdtype != SPARK_BF16) return SPARK_EUNSUPPORTED;
+  // The dtype field is read as the int it holds: a C caller or a foreign-function
+  // layer may store any int there, and C++ may not load an out-of-range value
+  // as the enum type itself.
+  int wd = 0;
+  static_assert(sizeof(wd) == sizeof(s->wdtype), "spark_dtype is int-sized");
+  std::memcpy(&wd, &s->wdtype, sizeof wd);
+  if (wd != SPARK_F32 && wd != SPARK_BF16) return SPARK_EUNSUPPORTED;
   if (s->d_model <= 0 || s->d_ff <= 0 || s->r <= 0 || s->r >= s->d_model) return SPARK_EINVAL;
   if (s->k <= 0 || s->k >= s->d_ff) return SPARK_EINVAL;
   const int64_t cn = s->wdtype == SPARK_BF16 ? 8 : 4;  // elements per 16-byte chunk
@@ -84,6 +91,12 @@ int stat_topk(const float* x, int64_t rows, int64_t d, int64_t ldx, int64_t k, f
   if (rows == 0) return SPARK_OK;
   const double z = spark_threshold_z(k, d);
   return hip_status(spark::launch_stat_topk(x, rows, d, ldx, z, vals, idx, cap, counts, theta, stream));
+}
+
+int64_t spark_ffn_decode_tags(int n_layers, int64_t T) {
+  if (n_layers < 1 || T < 0) return -1;
+  const int64_t launches = (n_layers + spark::kDecodeMaxLayersPerLaunch - 1) / spark::kDecodeMaxLayersPerLaunch;
+  return T * (3 * (int64_t)n_layers - launches);
 }
 
 int spark_ffn_decode_workspace_size(const spark_ffn_shape* s, int n_layers, int64_t T, size_t* bytes) {
@@ -207,27 +220,29 @@ int spark_attn_decode(const void* q, const void* k1, const void* k2, const void*
 }
 
 int spark_attn_prefill_workspace_size(int64_t T, int64_t Hq, int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn,
-                                      size_t* bytes) {
+                                      int64_t cap, size_t* bytes) {
   if (!bytes) return SPARK_EINVAL;
-  if (T <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || hd <= 0 || r <= 0 || r >= hd || k_attn <= 0)
+  if (T <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || hd <= 0 || r <= 0 || r >= hd || k_attn <= 0 || cap < 0)
     return SPARK_EINVAL;
   if (r % 8 != 0 || (hd - r) % 8 != 0) return SPARK_EINVAL;
   if (hd > 512 || T > 16384 || Hq > 1024) return SPARK_EUNSUPPORTED;
-  *bytes = spark::attn_prefill_workspace_bytes(T, Hq, Hkv, hd, r);
+  *bytes = spark::attn_prefill_workspace_bytes(T, Hq, Hkv, hd, r, cap > 0);
   return SPARK_OK;
 }
 
 int spark_attn_prefill(const void* q, const void* k1, const void* k2, const void* v, int64_t T, int64_t Hq,
-                       int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float* out, int32_t* counts, float* theta,
-                       void* ws, size_t ws_bytes, hipStream_t stream) {
+                       int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float* out, int32_t* counts, int32_t* idx,
+                       int64_t cap, float* theta, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (idx && cap < 0) return SPARK_EINVAL;
+  const int64_t lcap = idx ? cap : 0;
   size_t need = 0;
-  int st = spark_attn_prefill_workspace_size(T, Hq, Hkv, hd, r, k_attn, &need);
+  int st = spark_attn_prefill_workspace_size(T, Hq, Hkv, hd, r, k_attn, lcap, &need);
   if (st != SPARK_OK) return st;
   if (!q || !k1 || !k2 || !v || !out) return SPARK_EINVAL;
   if (!aligned(q, 16) || !aligned(k1, 16) || !aligned(k2, 16) || !aligned(v, 16)) return SPARK_EINVAL;
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return SPARK_EWORKSPACE;
-  return hip_status(spark::launch_attn_prefill(q, k1, k2, v, T, Hq, Hkv, hd, r, k_attn, out, counts, theta, ws,
-                                               stream));
+  return hip_status(spark::launch_attn_prefill(q, k1, k2, v, T, Hq, Hkv, hd, r, k_attn, out, counts,
+                                               lcap > 0 ? idx : nullptr, lcap, theta, ws, stream));
 }
 
 }  // extern "C"

@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256) void attn_prefill_rows(const float* __restrict
                                                          int k_attn,
                                                          const float* __restrict__ ztab, float* __restrict__ rth,
                                                          float* __restrict__ rmx, float* __restrict__ rl,
-                                                         int32_t* __restrict__ counts, float* __restrict__ theta) {
+                                                         int32_t* __restrict__ counts, float* __restrict__ theta,
+                                                         uint32_t* __restrict__ sel, int nw) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int h = blockIdx.x / T, t = blockIdx.x % T, n = t + 1;
@@ -119,6 +120,23 @@ __global__ __launch_bounds__(256) void attn_prefill_rows(const float* __restrict
     const float m2 = rows_sum(b, red);
     th = mean + sqrtf(m2 / (float)n) * ztab[n];
   }
+  if (sel) {
+    // selection bitmask of the row (see sel_to_list): position j = 4 (tid + 256 c) + e
+    // is bit j % 32 of word j / 32; the eight threads of a word OR their nibbles
+    uint32_t* srow = sel + ((size_t)t * Hq + h) * nw;
+#pragma unroll
+    for (int c4 = 0; c4 < PER / 4; ++c4) {
+      uint32_t nib = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nib |= (ok[4 * c4 + e] && v[4 * c4 + e] > th) ? 1u << e : 0u;
+      uint32_t wd = nib << (4 * (tid & 7));
+      wd |= __shfl_xor(wd, 1, kWave);
+      wd |= __shfl_xor(wd, 2, kWave);
+      wd |= __shfl_xor(wd, 4, kWave);
+      const int wi = (tid >> 3) + 32 * c4;
+      if ((tid & 7) == 0 && 32 * wi < n) srow[wi] = wd;
+    }
+  }
   float mx = -INFINITY;
   int c = 0;
 #pragma unroll
@@ -150,6 +168,41 @@ __global__ void zero_pad_bf16(bf16_t* __restrict__ p, int64_t rows, int ld, int 
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows * w) return;
   p[(i / w) * ld + c0 + i % w] = 0;
+}
+
+// Selected lists from the selection bitmasks: row (t, h) of sel holds bit
+// j % 32 of word j / 32 set when position j <= t is attended.  One wave per
+// row: words in rounds of 64 (one per lane), their popcounts scanned across
+// the wave, each lane then writes the positions of its word's set bits in
+// ascending order; the first min(count, cap) positions are stored and the
+// rest of the row's cap slots read -1.
+__global__ __launch_bounds__(256) void sel_to_list(const uint32_t* __restrict__ sel, int nw, int T, int Hq,
+                                                   int32_t* __restrict__ idx, int64_t cap) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)T * Hq) return;
+  const int t = (int)(row / Hq);
+  const uint32_t* srow = sel + row * nw;
+  int32_t* irow = idx + row * cap;
+  const int nwr = t / 32 + 1;  // words holding positions 0..t
+  int64_t base = 0;
+  for (int w0 = 0; w0 < nwr; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t bits = w < nwr ? srow[w] : 0u;
+    if (w == nwr - 1 && (t & 31) != 31) bits &= (1u << ((t & 31) + 1)) - 1u;  // positions past t
+    const int pc = __builtin_popcount(bits);
+    const int incl = wave_incl_scan_dpp(pc);
+    const int64_t off = base + incl - pc;
+    int e = 0;
+    while (bits) {
+      const int b = __builtin_ctz(bits);
+      bits &= bits - 1;
+      if (off + e < cap) irow[off + e] = 32 * w + b;
+      ++e;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  for (int64_t e = base + lane; e < cap; e += 64) irow[e] = -1;
 }
 
 // ---------------------------------------------------------------- fused path
@@ -200,6 +253,8 @@ struct FusedArgs {
   float* out;          // [T][Hq][hd]
   int32_t* counts;     // [T][Hq] or null
   float* theta;        // [T][Hq] or null
+  uint8_t* sel;        // [T][Hq][selb] selection bitmask bytes (see sel_to_list), or null
+  int selb;            // bytes per row of sel
   int T, Hq, G, LT, k_attn;
   int pair_heads;      // 1: the two row sets are heads 2u, 2u + 1 over 32 queries; 0: head u over 64 queries
   int nunits, nq;      // head pairs (or heads); query blocks of 32 (or 64) positions
@@ -597,15 +652,19 @@ __global__ __launch_bounds__(kFusedThreads2) void attn_prefill_fused(const Fused
         auto weights = [&](auto dc) {
           constexpr bool DIAG = decltype(dc)::value;
           bf16x8 pw;
+          uint32_t bits = 0;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const bool sel = (!DIAG || 32 * kt + 16 * half + 8 * hl + j <= tq) && sc[j] > th;
             const float e = sel ? __builtin_amdgcn_exp2f(fmaf(sc[j], kL2E, -mxs)) : 0.f;
             lsum += e;
             cnt += sel ? 1 : 0;
+            bits |= sel ? 1u << j : 0u;
             pw[j] = (__bf16)(e * softplus_gate(gc[j]));
           }
           *reinterpret_cast<bf16x8*>(&xch[wv][8 * lane]) = pw;
+          // keys 32 kt + 16 half + 8 hl + j: byte 4 kt + 2 half + hl of the row's bitmask
+          if (a.sel && tq < T) a.sel[((size_t)tq * Hq + h) * a.selb + 4 * kt + 2 * half + hl] = (uint8_t)bits;
         };
         if (kt < diag)
           weights(std::integral_constant<bool, false>{});
@@ -717,10 +776,13 @@ bool attn_prefill_fused_ok(int64_t hd, int64_t r) {
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct AttnPrefillLayout {
-  size_t S, W, Vt, rth, rmx, rl, z, total;
+  size_t S, W, Vt, rth, rmx, rl, z, sel, total;
 };
 
-static AttnPrefillLayout attn_prefill_layout(int64_t T, int64_t Hq, int64_t Hkv, int64_t hd, int64_t r) {
+// Words of one row of the selection bitmask.
+static int64_t sel_words(int64_t T) { return (T + 31) / 32; }
+
+static AttnPrefillLayout attn_prefill_layout(int64_t T, int64_t Hq, int64_t Hkv, int64_t hd, int64_t r, bool lists) {
   const int64_t LT = (T + 7) & ~(int64_t)7;
   const bool fused = attn_prefill_fused_ok(hd, r);
   AttnPrefillLayout L;
@@ -739,12 +801,14 @@ static AttnPrefillLayout attn_prefill_layout(int64_t T, int64_t Hq, int64_t Hkv,
   if (!fused) off += round_up((size_t)Hq * T * 4, 256);
   L.z = off;
   off += round_up((size_t)(T + 1) * 4, 256);
+  L.sel = off;  // selection bitmasks [T][Hq][sel_words(T)] (only when lists are asked for)
+  if (lists) off += round_up((size_t)T * Hq * sel_words(T) * 4, 256);
   L.total = off;
   return L;
 }
 
-size_t attn_prefill_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t hd, int64_t r) {
-  return attn_prefill_layout(T, Hq, Hkv, hd, r).total;
+size_t attn_prefill_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t hd, int64_t r, bool lists) {
+  return attn_prefill_layout(T, Hq, Hkv, hd, r, lists).total;
 }
 
 template <int R>
@@ -757,10 +821,29 @@ static hipError_t launch_fused_t(const FusedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+static hipError_t attn_prefill_main(const void* q, const void* k1, const void* k2, const void* v, int64_t T,
+                                    int64_t Hq, int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float* out,
+                                    int32_t* counts, float* theta, uint32_t* sel, const AttnPrefillLayout& L, void* ws,
+                                    hipStream_t st);
+
 hipError_t launch_attn_prefill(const void* q, const void* k1, const void* k2, const void* v, int64_t T, int64_t Hq,
                                int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float* out, int32_t* counts,
-                               float* theta, void* ws, hipStream_t st) {
-  const AttnPrefillLayout L = attn_prefill_layout(T, Hq, Hkv, hd, r);
+                               int32_t* idx, int64_t cap, float* theta, void* ws, hipStream_t st) {
+  const bool lists = idx != nullptr && cap > 0;
+  const AttnPrefillLayout L = attn_prefill_layout(T, Hq, Hkv, hd, r, lists);
+  uint32_t* sel = lists ? (uint32_t*)((char*)ws + L.sel) : nullptr;
+  hipError_t e = attn_prefill_main(q, k1, k2, v, T, Hq, Hkv, hd, r, k_attn, out, counts, theta, sel, L, ws, st);
+  if (e != hipSuccess || !lists) return e;
+  const int64_t rows = T * Hq;
+  hipLaunchKernelGGL(sel_to_list, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, (const uint32_t*)sel,
+                     (int)sel_words(T), (int)T, (int)Hq, idx, cap);
+  return hipGetLastError();
+}
+
+static hipError_t attn_prefill_main(const void* q, const void* k1, const void* k2, const void* v, int64_t T,
+                                    int64_t Hq, int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float* out,
+                                    int32_t* counts, float* theta, uint32_t* sel, const AttnPrefillLayout& L, void* ws,
+                                    hipStream_t st) {
   char* base = (char*)ws;
   float* S = (float*)(base + L.S);
   bf16_t* W = (bf16_t*)(base + L.W);
@@ -791,6 +874,8 @@ hipError_t launch_attn_prefill(const void* q, const void* k1, const void* k2, co
     a.out = out;
     a.counts = counts;
     a.theta = theta;
+    a.sel = (uint8_t*)sel;
+    a.selb = (int)(4 * sel_words(T));
     a.T = Ti;
     a.Hq = H;
     a.G = G;
@@ -821,19 +906,19 @@ hipError_t launch_attn_prefill(const void* q, const void* k1, const void* k2, co
     const dim3 g((unsigned)(H * T)), b(256);
     if (Ti <= 1024)
       hipLaunchKernelGGL(attn_prefill_rows<4>, g, b, 0, st, S, Ti, LT, H, (int)k_attn, ztab, rth, rmx, rl, counts,
-                         theta);
+                         theta, sel, (int)sel_words(T));
     else if (Ti <= 2048)
       hipLaunchKernelGGL(attn_prefill_rows<8>, g, b, 0, st, S, Ti, LT, H, (int)k_attn, ztab, rth, rmx, rl, counts,
-                         theta);
+                         theta, sel, (int)sel_words(T));
     else if (Ti <= 4096)
       hipLaunchKernelGGL(attn_prefill_rows<16>, g, b, 0, st, S, Ti, LT, H, (int)k_attn, ztab, rth, rmx, rl, counts,
-                         theta);
+                         theta, sel, (int)sel_words(T));
     else if (Ti <= 8192)
       hipLaunchKernelGGL(attn_prefill_rows<32>, g, b, 0, st, S, Ti, LT, H, (int)k_attn, ztab, rth, rmx, rl, counts,
-                         theta);
+                         theta, sel, (int)sel_words(T));
     else
       hipLaunchKernelGGL(attn_prefill_rows<64>, g, b, 0, st, S, Ti, LT, H, (int)k_attn, ztab, rth, rmx, rl, counts,
-                         theta);
+                         theta, sel, (int)sel_words(T));
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

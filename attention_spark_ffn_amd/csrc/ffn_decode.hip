@@ -26,7 +26,10 @@
 // tag of the exchange appears, so no cross-XCD fence is needed.  Exchanges A
 // and C are replicated once per XCD so each replica has 32 readers.
 // Every wait is bounded: on timeout the kernel records a failure in the
-// workspace header and all workgroups leave.
+// workspace header (the failed call's mark and a count of failed calls), the
+// workgroups write NaN over the output columns they own and leave, and
+// workgroup 0 still advances the tag in the header past every tag the call
+// owns, so no word of the failed call can satisfy a wait of a later one.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -60,7 +63,8 @@ struct DecodeParams {
   float* tr_theta;
   float* tr_q;
   int64_t tr_cap;
-  uint64_t* hdr;    // [0]: last tag used, [1]: failure flag
+  uint64_t* hdr;    // [0]: tag before the next call, [1]: mark (tag0 + 1) of the last failed call, [2]: failed
+                    // calls, [3]: bound of every wait when nonzero (test hook)
   uint64_t* stats;  // kRep x stats_stride: means of all workgroups, then their M2 (kRecRow apart)
   uint64_t* rec;    // kRep x rec_stride: selected-list record per workgroup
   uint64_t* ovf;    // G x kOvfWords: list entries past the record
@@ -74,7 +78,7 @@ struct DecodeParams {
 // timeout, or when another workgroup has recorded a failure.
 template <int K>
 __device__ __forceinline__ bool gather_tagged(const uint64_t* const (&ptrs)[K], uint32_t tag, float (&out)[K],
-                                              const uint64_t* hdr, uint32_t spin_limit) {
+                                              const uint64_t* hdr, uint64_t fmark, uint32_t spin_limit) {
   bool got[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) got[k] = ptrs[k] == nullptr;
@@ -97,7 +101,7 @@ __device__ __forceinline__ bool gather_tagged(const uint64_t* const (&ptrs)[K], 
     }
     if (all) return true;
     if (spin > spin_limit) return false;
-    if ((spin & 1023) == 1023 && get_word(hdr + 1) != 0) return false;
+    if ((spin & 1023) == 1023 && get_word(hdr + 1) == fmark) return false;
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -108,7 +112,7 @@ __device__ __forceinline__ bool gather_tagged(const uint64_t* const (&ptrs)[K], 
 // trip later instead of a whole one.
 template <int K>
 __device__ __forceinline__ bool gather_tagged2(const uint64_t* const (&ptrs)[K], uint32_t tag, float (&out)[K],
-                                               const uint64_t* hdr, uint32_t spin_limit) {
+                                               const uint64_t* hdr, uint64_t fmark, uint32_t spin_limit) {
   bool got[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) got[k] = ptrs[k] == nullptr;
@@ -140,7 +144,7 @@ __device__ __forceinline__ bool gather_tagged2(const uint64_t* const (&ptrs)[K],
     issue(a);
     if (check(b)) return true;
     if (spin > spin_limit) return false;
-    if ((spin & 1022) == 1022 && get_word(hdr + 1) != 0) return false;
+    if ((spin & 1022) == 1022 && get_word(hdr + 1) == fmark) return false;
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -154,8 +158,13 @@ __device__ __forceinline__ T* fresh(T* ptr) {
   return ptr;
 }
 
-__device__ __forceinline__ void raise_failure(uint64_t* hdr) {
-  __hip_atomic_store(hdr + 1, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Record that the call whose first tag is tag0 failed: its mark tag0 + 1 (never
+// 0, the value of a fresh header) goes to hdr[1], which the waits of the
+// same call poll; the first workgroup to set the mark also counts the failed
+// call in hdr[2], which the host can read.
+__device__ __forceinline__ void raise_failure(uint64_t* hdr, uint64_t fmark) {
+  const uint64_t old = __hip_atomic_exchange(hdr + 1, fmark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old != fmark) __hip_atomic_fetch_add(hdr + 2, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // LDS of one decode workgroup.
@@ -177,6 +186,9 @@ struct DecShared {
   uint64_t candmask;
   int ntot, fail;
   uint32_t tag0;
+  uint32_t spin_limit;  // polling rounds a wait may take
+  uint32_t poison;      // XORed into the tag exchange A waits for (nonzero: the test hook's forced failure)
+  uint64_t fmark;       // tag0 + 1: the failure mark of this call
 };
 
 // Shape of the work of one workgroup.
@@ -473,7 +485,7 @@ __device__ __forceinline__ bool v_record(const DecodeParams& p, const DecShared&
     } else {
       const uint64_t* op[1] = {p.ovf + (size_t)gg * kOvfWords + (e - kRecEntries)};
       float ov[1];
-      ok = ok && gather_tagged<1>(op, tagB, ov, p.hdr, p.spin_limit);
+      ok = ok && gather_tagged<1>(op, tagB, ov, p.hdr, S.fmark, S.spin_limit);
       cv = ok ? ov[0] : 0.f;
     }
 #pragma unroll
@@ -508,6 +520,12 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
   }
   const int nb_rec = own_first(tid < G ? tid : 0, g.d_ff, G);
   const bool trace_here = w == 0 && (p.tr_idx || p.tr_counts || p.tr_theta);
+  // a failed call: mark it, and NaN over the owned output columns of every token
+  auto fail_out = [&]() {
+    if (tid == 0) raise_failure(p.hdr, S.fmark);
+    if (tid < g.ncol)
+      for (int t2 = 0; t2 < g.T; ++t2) p.y_out[(size_t)t2 * d_model + g.c0 + tid] = __builtin_nanf("");
+  };
 
   float qs = 1.f;  // scale of the q held in LDS (its RMS normalisation, applied to the products)
   for (int t = 0; t < g.T; ++t) {
@@ -564,7 +582,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           pa[2 * k + 1] = gg < G ? src + kRecRow + gg : nullptr;
         }
         float vals[KA];
-        const bool ok = gather_tagged2<KA>(pa, tagA, vals, p.hdr, p.spin_limit);
+        const bool ok = gather_tagged2<KA>(pa, tagA ^ S.poison, vals, p.hdr, S.fmark, S.spin_limit);
         // two passes over the records: the mean, then the squared deviations
         // about it (Chan et al.'s combination, written as two plain sums)
         float s1 = 0.f;
@@ -581,7 +599,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         if (lane == 0) S.theta = mu + sqrtf(m2 / (float)g.d_ff) * p.z;
         if (__builtin_amdgcn_ballot_w64(!ok) != 0 && lane == 0) {
           S.fail = 1;
-          raise_failure(p.hdr);
+          raise_failure(p.hdr, S.fmark);
         }
       } else {
         // ---------------- waves 1..3, meanwhile: K2 dots of the top candidates.
@@ -614,7 +632,10 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         }
       }
       bar();  // A
-      if (S.fail) return;
+      if (S.fail) {
+        fail_out();
+        return;
+      }
       const float theta = S.theta;
 
       // ---------------- selection, gated values, publish the record
@@ -695,7 +716,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           if (check(ra)) break;
           issue(ra);
           if (check(rb)) break;
-          if (spin > p.spin_limit || ((spin & 1022) == 1022 && get_word(p.hdr + 1) != 0)) {
+          if (spin > S.spin_limit || ((spin & 1022) == 1022 && get_word(p.hdr + 1) == S.fmark)) {
             okB = false;
             break;
           }
@@ -710,7 +731,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
 #pragma unroll
           for (int k = 0; k < NR; ++k) pe[k] = kSpecE + k < n ? rp + (size_t)(2 + kSpecE + k) * kRecRow : nullptr;
           float ev[NR];
-          okB = gather_tagged<NR>(pe, tagB, ev, p.hdr, p.spin_limit);
+          okB = gather_tagged<NR>(pe, tagB, ev, p.hdr, S.fmark, S.spin_limit);
 #pragma unroll
           for (int k = 0; k < NR; ++k)
             if (kSpecE + k < n) S.t.stage[gg][kSpecE + k] = ev[k];
@@ -786,7 +807,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       }
       bar();  // V
       if (S.fail) {
-        if (tid == 0) raise_failure(p.hdr);
+        fail_out();
         return;
       }
       const float ymine =
@@ -817,7 +838,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
             ptrs[k] = c < d_model ? src + c : nullptr;
           }
           float vals[KC];
-          okC = gather_tagged2<KC>(ptrs, tagC, vals, p.hdr, p.spin_limit);
+          okC = gather_tagged2<KC>(ptrs, tagC, vals, p.hdr, S.fmark, S.spin_limit);
 #pragma unroll
           for (int k = 0; k < KC; ++k) {
             const int c = c00 + tid + kWorkers * k;
@@ -833,7 +854,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       }
       bar();  // C
       if (S.fail) {
-        if (tid == 0) raise_failure(p.hdr);
+        fail_out();
         return;
       }
       // the layer output stays in LDS as gathered; its RMS normalisation is the
@@ -841,7 +862,6 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       qs = 1.f / sqrtf((S.wred[0] + S.wred[1] + S.wred[2] + S.wred[3]) / (float)d_model + p.eps);
     }
   }
-  if (w == 0 && tid == 0) __hip_atomic_store(p.hdr, (uint64_t)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename W>
@@ -876,13 +896,30 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
   g.rep = xcc_id();
   if (threadIdx.x == 0) {
     S.tag0 = (uint32_t)get_word(p.hdr);
+    S.fmark = (uint64_t)S.tag0 + 1;
+    // hdr[3], when nonzero, is a host-set test hook that drives the failure
+    // path: it replaces the bound of every wait, and exchange A waits for a
+    // tag no word carries (bit 31 flipped: the statistics words hold this
+    // layer's or the previous layer's tag), so every workgroup times out
+    // there and every wave still exits
+    const uint64_t lim = get_word(p.hdr + 3);
+    S.spin_limit = lim ? (uint32_t)lim : p.spin_limit;
+    S.poison = lim ? 0x80000000u : 0u;
     S.fail = 0;
   }
   __syncthreads();
-  if (threadIdx.x < kWorkers)
+  if (threadIdx.x < kWorkers) {
     decode_worker<W>(p, kp->k2t, kp->v, g, S);
-  else
+    // on every way out, failed or not: the next call's tags start after the
+    // T (3 L - 1) tags this call owns (A, B and C per layer, no C after the
+    // last).  Every workgroup has read hdr[0] before it published anything,
+    // and workgroup 0 cannot get past the first exchange before that.
+    if (g.w == 0 && threadIdx.x == 0)
+      __hip_atomic_store(p.hdr, (uint64_t)(S.tag0 + (uint32_t)g.T * (uint32_t)(3 * g.L - 1)), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  } else {
     decode_streamer<W>(p, kp->k1t, g, S);
+  }
 }
 
 // ---------------------------------------------------------------- host side

@@ -106,20 +106,36 @@ int stat_topk(const float *x, int64_t rows, int64_t d, int64_t ldx, int64_t k, f
  *   last layer (before normalisation);  layers: host array of n_layers weight
  *   sets; trace may be NULL.
  * Weights fp32 or bf16; arithmetic fp32 with fp32 accumulation.
- * Requires d_model <= 8192, d_ff <= 65536, 1 <= n_layers, T >= 0, rms_eps >= 0;
- * weight rows 16-byte aligned (k1t, k2t, v base pointers 256-byte aligned and
- * r, d_model - r, d_model multiples of 8 elements).
+ * Requires d_model <= 8192, d_ff <= 65536, 1 <= n_layers, T >= 0, rms_eps >= 0,
+ * k1t, k2t and v base pointers 16-byte aligned, and r and d_model - r
+ * multiples of 8 elements (bf16) or 4 elements (fp32), so that every weight
+ * row is whole 16-byte chunks; SPARK_EINVAL otherwise.
  * The kernel is a cooperative (co-resident) grid; it returns SPARK_EHIP if the
  * device cannot host it.
- * Workspace: zero-filled before its first use, then kept between calls (it
- * carries the tags of the grid-wide exchanges from call to call); calls that
- * overlap on one workspace race.  A timed-out exchange (a kernel that could not
- * make progress) ends the call early and sets the 8-byte word at offset 8 of
- * the workspace to nonzero.
+ * Workspace: zero-filled before its first use, then kept between calls: it
+ * carries the 32-bit tags of the grid-wide exchanges from call to call, and a
+ * call uses spark_ffn_decode_tags(n_layers, T) of them.  Zero the workspace
+ * again before the tags used since it was last zeroed would exceed
+ * 2^32 - 1 (a tag must never repeat while a word carrying it can still be
+ * read).  Calls that overlap on one workspace race.
+ * Failure: every exchange wait is bounded.  When one times out (a grid that
+ * could not make progress), the call ends early, the columns of y it did not
+ * finish read NaN, and the 8-byte counter at byte offset 16 of the workspace
+ * is incremented (once per failed call); the tags still advance as after a
+ * complete call, so the next call on the workspace is unaffected.  The
+ * 8-byte word at byte offset 24 is a test hook that drives this failure
+ * path from the host: when nonzero, every wait is bounded by that many
+ * polling rounds and the first exchange cannot complete, so the call fails;
+ * leave it zero.
  */
 int spark_ffn_decode(const spark_ffn_shape *s, const spark_ffn_weights *layers, int n_layers, const float *q,
                      int64_t T, float *y, float rms_eps, const spark_ffn_trace *trace, void *ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* Exchange tags one spark_ffn_decode call with these arguments uses: T times
+ * (3 n_layers - the number of launches), a launch holding up to 32 layers.
+ * Returns -1 for n_layers < 1 or T < 0. */
+int64_t spark_ffn_decode_tags(int n_layers, int64_t T);
 
 /*
  * Batched Spark FFN decode: the computation of spark_ffn_decode for B
@@ -187,6 +203,11 @@ int spark_attn_decode(const void *q, const void *k1, const void *k2, const void 
  * selected set and softplus gates, as spark_attn_decode does for one query.
  *   q [T][Hq][hd] bf16 (position-major); k1 [Hkv][T][r], k2 [Hkv][T][hd-r],
  *   v [Hkv][T][hd] bf16; out [T][Hq][hd] fp32; counts [T][Hq] (may be NULL);
+ *   idx [T][Hq][cap] int32 (may be NULL): the attended positions of each
+ *   (t, h) in ascending order, the first min(count, cap) of them, the rest of
+ *   the row's slots -1 (cap >= 0; with cap > 0 the workspace must be sized
+ *   for that cap, since it then also holds a selection bitmask of
+ *   T * Hq * ceil(T/32) words);
  *   theta [T][Hq] (may be NULL; NaN where t + 1 <= k_attn).
  * All products run on the matrix cores.  With r = hd - r in {32, 64, 128}
  * two fused kernels walk the keys of each query twice (moments and maximum
@@ -199,19 +220,21 @@ int spark_attn_decode(const void *q, const void *k1, const void *k2, const void 
  * hd - r multiples of 8, 1 <= T <= 16384, k_attn >= 1.
  */
 int spark_attn_prefill(const void *q, const void *k1, const void *k2, const void *v, int64_t T, int64_t Hq,
-                       int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float *out, int32_t *counts, float *theta,
-                       void *ws, size_t ws_bytes, hipStream_t stream);
+                       int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, float *out, int32_t *counts, int32_t *idx,
+                       int64_t cap, float *theta, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace sizes (bytes) for the calls above with the same arguments, on the
  * current device: some depend on its compute-unit count, and every call checks
- * ws_bytes against the size for the device current when it is made. */
+ * ws_bytes against the size for the device current when it is made.  For
+ * spark_attn_prefill, cap is the list capacity the call will pass with a
+ * non-NULL idx (0 when it passes no list). */
 int spark_ffn_decode_workspace_size(const spark_ffn_shape *s, int n_layers, int64_t T, size_t *bytes);
 int spark_ffn_decode_batched_workspace_size(const spark_ffn_shape *s, int64_t B, size_t *bytes);
 int spark_ffn_prefill_workspace_size(const spark_ffn_shape *s, int64_t T, size_t *bytes);
 int spark_attn_workspace_size(int64_t Hq, int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn,
                               size_t *bytes);
 int spark_attn_prefill_workspace_size(int64_t T, int64_t Hq, int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn,
-                                      size_t *bytes);
+                                      int64_t cap, size_t *bytes);
 
 /* z = Q(1 - k/d), the standard-normal quantile the threshold uses (host fp64). */
 double spark_threshold_z(int64_t k, int64_t d);

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "spark_ffn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|double|const char \*)\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|double|const char \*)\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -159,20 +159,31 @@ def test_attention_prefill_rejects_bad_arguments():
     L = sf.lib()
     n = ctypes.c_size_t(0)
     P = L.spark_attn_prefill_workspace_size
-    assert P(64, 8, 3, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EINVAL  # Hq % Hkv
-    assert P(64, 8, 4, 256, 0, 256, ctypes.byref(n)) == sf.SPARK_EINVAL  # r
-    assert P(64, 8, 4, 256, 100, 256, ctypes.byref(n)) == sf.SPARK_EINVAL  # r % 8
-    assert P(0, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EINVAL  # T
-    assert P(1 << 15, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED  # T too long
-    assert P(64, 8, 4, 1024, 128, 256, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED  # hd
+    assert P(64, 8, 3, 256, 128, 256, 0, ctypes.byref(n)) == sf.SPARK_EINVAL  # Hq % Hkv
+    assert P(64, 8, 4, 256, 0, 256, 0, ctypes.byref(n)) == sf.SPARK_EINVAL  # r
+    assert P(64, 8, 4, 256, 100, 256, 0, ctypes.byref(n)) == sf.SPARK_EINVAL  # r % 8
+    assert P(0, 8, 4, 256, 128, 256, 0, ctypes.byref(n)) == sf.SPARK_EINVAL  # T
+    assert P(1 << 15, 8, 4, 256, 128, 256, 0, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED  # T too long
+    assert P(64, 8, 4, 1024, 128, 256, 0, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED  # hd
     # r = hd - r: the fused kernels need only V^T and the threshold table
-    assert P(64, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_OK
+    assert P(64, 8, 4, 256, 128, 256, 0, ctypes.byref(n)) == sf.SPARK_OK
     assert 4 * 256 * 64 * 2 <= n.value < 64 * 64 * 8 * 6
     # other head splits materialise fp32 scores and bf16 weights
-    assert P(64, 8, 4, 96, 32, 16, ctypes.byref(n)) == sf.SPARK_OK and n.value > 64 * 64 * 8 * 6
+    assert P(64, 8, 4, 96, 32, 16, 0, ctypes.byref(n)) == sf.SPARK_OK and n.value > 64 * 64 * 8 * 6
     ws = ctypes.create_string_buffer(16)
-    assert L.spark_attn_prefill(None, None, None, None, 64, 8, 4, 256, 128, 256, None, None, None, ws, 16,
+    assert L.spark_attn_prefill(None, None, None, None, 64, 8, 4, 256, 128, 256, None, None, None, 0, None, ws, 16,
                                 None) == sf.SPARK_EINVAL
+    vp = ctypes.c_void_p(256)
+    assert P(64, 8, 4, 256, 128, 256, -1, ctypes.byref(n)) == sf.SPARK_EINVAL  # negative list capacity
+    assert L.spark_attn_prefill(vp, vp, vp, vp, 64, 8, 4, 256, 128, 256, vp, None, vp, -1, None, vp, 1 << 30,
+                                None) == sf.SPARK_EINVAL
+    # lists need the bitmask region: a workspace sized without it is too small
+    assert P(64, 8, 4, 256, 128, 256, 0, ctypes.byref(n)) == sf.SPARK_OK
+    small = n.value
+    assert P(64, 8, 4, 256, 128, 256, 16, ctypes.byref(n)) == sf.SPARK_OK
+    assert n.value >= small + 64 * 8 * 2 * 4
+    assert L.spark_attn_prefill(vp, vp, vp, vp, 64, 8, 4, 256, 128, 256, vp, None, vp, 16, None, vp, small,
+                                None) == sf.SPARK_EWORKSPACE
 
 
 def test_empty_prefills():
@@ -187,7 +198,7 @@ def test_empty_prefills():
     assert L.spark_ffn_prefill(ctypes.byref(s), ctypes.byref(w), vp, 0, vp, None, vp, 1 << 30, None) == sf.SPARK_OK
     assert L.spark_ffn_prefill(ctypes.byref(s), ctypes.byref(w), vp, -1, vp, None, vp, 1 << 30, None) == sf.SPARK_EINVAL
     P = L.spark_attn_prefill_workspace_size
-    assert P(0, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EINVAL
-    assert P(16385, 8, 4, 256, 128, 256, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED
-    assert L.spark_attn_prefill(vp, vp, vp, vp, 0, 8, 4, 256, 128, 256, vp, None, None, vp, 1 << 30,
+    assert P(0, 8, 4, 256, 128, 256, 0, ctypes.byref(n)) == sf.SPARK_EINVAL
+    assert P(16385, 8, 4, 256, 128, 256, 0, ctypes.byref(n)) == sf.SPARK_EUNSUPPORTED
+    assert L.spark_attn_prefill(vp, vp, vp, vp, 0, 8, 4, 256, 128, 256, vp, None, None, 0, None, vp, 1 << 30,
                                 None) == sf.SPARK_EINVAL
