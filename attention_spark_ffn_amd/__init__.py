@@ -9,6 +9,7 @@ RuntimeError is raised.
 Entry points (same names as the C ABI):
   stat_topk(x, k, cap=None)                         -> (vals, idx, counts, theta)
   spark_ffn_decode(q, layers, k, r, eps, ...)       -> y  (and a trace dict)
+  spark_ffn_decode_noalloc(q, layers, k, r, eps, ...)  -> the same, no device allocation by the library
   spark_ffn_decode_batched(q, layers, k, r, eps, ...)  -> the same, B <= 8 tokens layer by layer
   spark_ffn_prefill(Q, layer, k, r, ...)            -> Y  (and a trace dict)
   spark_attn_decode(q, k1, k2, v, k_attn, cap=None) -> (out, counts, idx, theta)
@@ -81,6 +82,11 @@ def lib() -> ctypes.CDLL:
                 L.spark_attn_decode.restype = _ci
                 L.spark_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
                                                 _vp, _i64, _vp, _vp, _sz, _vp]
+                L.spark_ffn_decode_noalloc.restype = _ci
+                L.spark_ffn_decode_noalloc.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _ci, _vp,
+                                                       _i64, _vp, _f, ctypes.POINTER(TraceC), _vp]
+                L.spark_ffn_decode_noalloc_max_bytes.restype = _sz
+                L.spark_ffn_decode_noalloc_max_bytes.argtypes = []
                 L.spark_ffn_decode_tags.restype = _i64
                 L.spark_ffn_decode_tags.argtypes = [_ci, _i64]
                 L.spark_ffn_decode_workspace_size.restype = _ci
@@ -301,6 +307,22 @@ def spark_ffn_decode(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6,
     if check and ws.new_failures():
         raise RuntimeError("spark_ffn_decode: a grid-wide exchange timed out (the device could not keep the "
                            "whole grid running); the output holds NaN")
+    return (y, tr) if trace else y
+
+
+def spark_ffn_decode_noalloc(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6, trace: bool = False,
+                             cap: int | None = None):
+    """spark_ffn_decode through the entry point that allocates nothing on the
+    device: the library's own per-device scratch array replaces the workspace
+    (calls on one device must not overlap).  Same arguments and results as
+    spark_ffn_decode; this wrapper allocates only the outputs."""
+    T, d_model, L, d_ff, shape, wts = _stack_args(q, layers, k, r)
+    dev = q.device
+    y = torch.empty((T, d_model), dtype=torch.float32, device=dev)
+    tr, trc = _trace_buffers(T, L, d_ff, d_model, cap, dev) if trace else (None, None)
+    st = lib().spark_ffn_decode_noalloc(ctypes.byref(shape), wts, L, _p(q), T, _p(y), float(eps),
+                                        ctypes.byref(trc) if trc is not None else None, _stream(dev))
+    _check(st, "spark_ffn_decode_noalloc")
     return (y, tr) if trace else y
 
 

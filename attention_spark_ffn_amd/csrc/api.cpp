@@ -133,6 +133,32 @@ int spark_ffn_decode(const spark_ffn_shape* s, const spark_ffn_weights* layers, 
   return hip_status(spark::launch_decode(*s, layers, n_layers, q, T, y, rms_eps, z, trace, ws, stream));
 }
 
+int spark_ffn_decode_noalloc(const spark_ffn_shape* s, const spark_ffn_weights* layers, int n_layers,
+                             const float* q, int64_t T, float* y, float rms_eps, const spark_ffn_trace* trace,
+                             hipStream_t stream) {
+  int st = check_ffn_shape(s);
+  if (st != SPARK_OK) return st;
+  if (n_layers < 1 || !layers || T < 0 || !(rms_eps >= 0.f) || !std::isfinite(rms_eps)) return SPARK_EINVAL;
+  st = decode_limits(s);
+  if (st != SPARK_OK) return st;
+  if (T > 0 && (!q || !y)) return SPARK_EINVAL;
+  for (int l = 0; l < n_layers; ++l) {
+    st = check_weights(layers[l]);
+    if (st != SPARK_OK) return st;
+  }
+  if (trace && trace->idx && trace->cap < 0) return SPARK_EINVAL;
+  if ((int64_t)T * n_layers * 3 >= (int64_t)1 << 31) return SPARK_EUNSUPPORTED;
+  size_t need = 0;
+  spark_ffn_decode_workspace_size(s, n_layers, T, &need);
+  if (need > spark::kNoAllocScratchBytes) return SPARK_EUNSUPPORTED;  // beyond the built-in scratch
+  if (T == 0) return SPARK_OK;
+  const double z = spark_threshold_z(s->k, s->d_ff);
+  return hip_status(spark::launch_decode_noalloc(*s, layers, n_layers, q, T, y, rms_eps, z, trace,
+                                                 (uint64_t)spark_ffn_decode_tags(n_layers, T), stream));
+}
+
+size_t spark_ffn_decode_noalloc_max_bytes(void) { return spark::kNoAllocScratchBytes; }
+
 int spark_ffn_decode_batched_workspace_size(const spark_ffn_shape* s, int64_t B, size_t* bytes) {
   if (!bytes) return SPARK_EINVAL;
   int st = check_ffn_shape(s);

@@ -30,6 +30,8 @@
 // workgroups write NaN over the output columns they own and leave, and
 // workgroup 0 still advances the tag in the header past every tag the call
 // owns, so no word of the failed call can satisfy a wait of a later one.
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -1023,6 +1025,62 @@ hipError_t launch_decode(const spark_ffn_shape& s, const spark_ffn_weights* laye
   if (T == 0) return hipSuccess;
   if (s.wdtype == SPARK_BF16) return launch_decode_t<bf16_t>(s, layers, n_layers, q, T, y, eps, z, trace, ws, st);
   return launch_decode_t<float>(s, layers, n_layers, q, T, y, eps, z, trace, ws, st);
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// The workspace of spark_ffn_decode_noalloc: one array per device, kept for the
+// life of the process, shared by every call on that device (it carries the
+// exchange tags from call to call like a caller's workspace).  In host code
+// `scratch` names a host-side stand-in, never the device memory: the device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static __global__ void zero_words(uint64_t* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+namespace {
+struct NoAllocDevice {
+  void* ptr = nullptr;    // device address of `scratch` on this device
+  uint64_t tags = 0;      // exchange tags used since the scratch was last cleared
+  bool cleared = false;   // the first clear has been enqueued
+};
+std::mutex g_noalloc_mu;
+NoAllocDevice g_noalloc[kMaxDevices];
+}  // namespace
+
+hipError_t launch_decode_noalloc(const spark_ffn_shape& s, const spark_ffn_weights* layers, int n_layers,
+                                 const float* q, int64_t T, float* y, float eps, double z,
+                                 const spark_ffn_trace* trace, uint64_t tags, hipStream_t st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> g(g_noalloc_mu);
+    NoAllocDevice& d = g_noalloc[dev];
+    if (!d.ptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      d.ptr = p;
+    }
+    // clear before the first call on this device, and again before the 32-bit
+    // tags would wrap (a tag must never repeat while a word can carry it)
+    if (!d.cleared || d.tags + tags > 0xFFFFFFFFull) {
+      const size_t words = kNoAllocScratchBytes / 8;
+      hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, st, (uint64_t*)d.ptr, words);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      d.cleared = true;
+      d.tags = 0;
+    }
+    d.tags += tags;
+    ws = d.ptr;
+  }
+  return launch_decode(s, layers, n_layers, q, T, y, eps, z, trace, ws, st);
 }
 
 }  // namespace spark

@@ -26,6 +26,14 @@ int decode_grid(int64_t d_ff);  // workgroups of the persistent grid on the curr
 hipError_t launch_decode(const spark_ffn_shape& s, const spark_ffn_weights* layers, int n_layers, const float* q,
                          int64_t T, float* y, float eps, double z, const spark_ffn_trace* trace, void* ws,
                          hipStream_t st);
+// spark_ffn_decode_noalloc: the same kernel on a static per-device scratch of
+// kNoAllocScratchBytes (cleared on the first call on a device and before the
+// exchange tags would wrap; `tags` is the call's tag count).
+constexpr size_t kNoAllocScratchBytes = size_t(2) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t launch_decode_noalloc(const spark_ffn_shape& s, const spark_ffn_weights* layers, int n_layers,
+                                 const float* q, int64_t T, float* y, float eps, double z,
+                                 const spark_ffn_trace* trace, uint64_t tags, hipStream_t st);
 
 // ---------------------------------------------------------------- batched decode
 constexpr int kBatchMax = 8;          // tokens per batch

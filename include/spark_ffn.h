@@ -132,6 +132,32 @@ int spark_ffn_decode(const spark_ffn_shape *s, const spark_ffn_weights *layers, 
                      int64_t T, float *y, float rms_eps, const spark_ffn_trace *trace, void *ws, size_t ws_bytes,
                      hipStream_t stream);
 
+/*
+ * spark_ffn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, results and failure behaviour as spark_ffn_decode, without
+ * the workspace: the exchanges use a scratch array built into the library,
+ * one per device, of spark_ffn_decode_noalloc_max_bytes() bytes (2 MiB),
+ * which each device holds until the process ends.  This entry point makes no
+ * allocation (no hipMalloc, hipFree or allocating library call).
+ *   - The first call on a device looks up that device's copy of the array
+ *     (hipGetSymbolAddress, with the device current) and clears it with a
+ *     small kernel on `stream`; it is cleared the same way whenever the
+ *     exchange tags used since the last clear would pass 2^32 - 1.
+ *   - Every call on a device shares that device's array, which keeps the last
+ *     call's contents: calls that overlap on one device (other streams, other
+ *     host threads) race, so serialise them.
+ *   - Sizes whose spark_ffn_decode_workspace_size exceeds the array return
+ *     SPARK_EUNSUPPORTED before anything is enqueued (every shape of up to 32
+ *     layers fits; more layers need 8 * T * d_model bytes more).
+ */
+int spark_ffn_decode_noalloc(const spark_ffn_shape *s, const spark_ffn_weights *layers, int n_layers,
+                             const float *q, int64_t T, float *y, float rms_eps, const spark_ffn_trace *trace,
+                             hipStream_t stream);
+
+/* Bytes of the per-device scratch array spark_ffn_decode_noalloc uses. */
+size_t spark_ffn_decode_noalloc_max_bytes(void);
+
 /* Exchange tags one spark_ffn_decode call with these arguments uses: T times
  * (3 n_layers - the number of launches), a launch holding up to 32 layers.
  * Returns -1 for n_layers < 1 or T < 0. */

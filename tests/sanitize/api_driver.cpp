@@ -39,6 +39,11 @@ hipError_t launch_decode(const spark_ffn_shape&, const spark_ffn_weights*, int, 
   ++launches;
   return std::isfinite(z) ? hipSuccess : hipErrorInvalidValue;
 }
+hipError_t launch_decode_noalloc(const spark_ffn_shape&, const spark_ffn_weights*, int, const float*, int64_t,
+                                 float*, float, double z, const spark_ffn_trace*, uint64_t tags, hipStream_t) {
+  ++launches;
+  return std::isfinite(z) && tags > 0 ? hipSuccess : hipErrorInvalidValue;
+}
 size_t decode_batched_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t B) {
   return (size_t)(d_model + d_ff) * B * 8;
 }
@@ -129,6 +134,23 @@ int main() {
   EXPECT(spark_ffn_decode_workspace_size(&s2, 26, 1, &need) == SPARK_EUNSUPPORTED);
   EXPECT(spark_ffn_decode_tags(26, 1) == 77 && spark_ffn_decode_tags(40, 2) == 2 * (120 - 2));
   EXPECT(spark_ffn_decode_tags(0, 1) == -1);
+
+  // decode without a workspace: the same checks, sizes within the built-in scratch
+  n0 = launches;
+  EXPECT(spark_ffn_decode_noalloc(&s, layers.data(), 26, x, 1, (float*)P, 1e-6f, nullptr, nullptr) == SPARK_OK);
+  EXPECT(launches == n0 + 1);
+  EXPECT(spark_ffn_decode_noalloc(&s, bad.data(), 26, x, 1, (float*)P, 1e-6f, nullptr, nullptr) == SPARK_EINVAL);
+  EXPECT(spark_ffn_decode_noalloc(&s, layers.data(), 0, x, 1, (float*)P, 1e-6f, nullptr, nullptr) == SPARK_EINVAL);
+  EXPECT(spark_ffn_decode_noalloc_max_bytes() == spark::kNoAllocScratchBytes);
+  // more than one launch of layers needs 8 T d_model bytes more: too many tokens exceed the scratch
+  EXPECT(spark_ffn_decode_noalloc(&s, layers.data(), 40, x, 1, (float*)P, 1e-6f, nullptr, nullptr) == SPARK_OK);
+  {
+    const int64_t T = (int64_t)(spark::kNoAllocScratchBytes / (8 * s.d_model)) + 1;
+    EXPECT(spark_ffn_decode_workspace_size(&s, 40, T, &need) == SPARK_OK && need > spark::kNoAllocScratchBytes);
+    EXPECT(spark_ffn_decode_noalloc(&s, layers.data(), 40, x, T, (float*)P, 1e-6f, nullptr, nullptr) ==
+           SPARK_EUNSUPPORTED);
+  }
+  EXPECT(spark_ffn_decode_noalloc(&s, layers.data(), 26, x, 0, (float*)P, 1e-6f, nullptr, nullptr) == SPARK_OK);
 
   // batched decode
   EXPECT(spark_ffn_decode_batched_workspace_size(&s, 8, &need) == SPARK_OK);

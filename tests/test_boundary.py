@@ -18,12 +18,13 @@ HEADER = os.path.join(ROOT, "include", "spark_ffn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|int64_t|double|const char \*)\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|size_t|double|const char \*)\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["stat_topk", "spark_ffn_decode", "spark_ffn_decode_batched", "spark_ffn_prefill", "spark_attn_decode",
+              "spark_ffn_decode_noalloc", "spark_ffn_decode_noalloc_max_bytes", "spark_ffn_decode_tags",
               "spark_ffn_decode_workspace_size", "spark_ffn_decode_batched_workspace_size",
               "spark_ffn_prefill_workspace_size", "spark_attn_workspace_size",
               "spark_attn_prefill", "spark_attn_prefill_workspace_size", "spark_status_string", "spark_threshold_z"]:
