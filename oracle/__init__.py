@@ -67,6 +67,14 @@ class _Lib:
                                                  vp]
         lib.oracle_spark_attn_prefill.restype = ci
         lib.oracle_spark_attn_prefill.argtypes = [ci, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, vp]
+        lib.oracle_huber_relu.restype = d
+        lib.oracle_huber_relu.argtypes = [d, d]
+        lib.oracle_huber_relu_grad.restype = d
+        lib.oracle_huber_relu_grad.argtypes = [d, d]
+        lib.oracle_stat_topk_huber_forward.restype = ci
+        lib.oracle_stat_topk_huber_forward.argtypes = [vp, i64, i64, i64, d, vp, vp]
+        lib.oracle_stat_topk_huber_backward.restype = ci
+        lib.oracle_stat_topk_huber_backward.argtypes = [vp, vp, i64, i64, i64, d, vp]
         self.c = lib
 
 
@@ -273,3 +281,42 @@ def spark_attn_prefill(q: np.ndarray, k1: np.ndarray, k2: np.ndarray, v: np.ndar
     if rc != 0:
         raise ValueError("oracle_spark_attn_prefill: bad arguments")
     return dict(out=out, counts=counts, theta=theta)
+
+
+def huber_relu(u: float, delta: float) -> float:
+    return _load().oracle_huber_relu(float(u), float(delta))
+
+
+def huber_relu_grad(u: float, delta: float) -> float:
+    return _load().oracle_huber_relu_grad(float(u), float(delta))
+
+
+def stat_topk_huber(x: np.ndarray, k: int, delta: float) -> dict:
+    """Huber-smoothed statistical top-k of each fp32 row of x [rows][d]:
+    y [rows][d] fp64 (dense) and theta [rows]."""
+    x = _c(np.asarray(x, dtype=np.float32))
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, d = x.shape
+    y = np.zeros((rows, d), np.float64)
+    theta = np.zeros(rows, np.float64)
+    rc = _load().oracle_stat_topk_huber_forward(_ptr(x), rows, d, int(k), float(delta), _ptr(y), _ptr(theta))
+    if rc != 0:
+        raise ValueError("oracle_stat_topk_huber_forward: bad arguments")
+    return dict(y=y, theta=theta)
+
+
+def stat_topk_huber_backward(x: np.ndarray, dy: np.ndarray, k: int, delta: float) -> np.ndarray:
+    """dL/dx [rows][d] fp64 of the Huber-smoothed statistical top-k, given
+    dy = dL/dy (fp32 [rows][d]) at the fp32 input x."""
+    x = _c(np.asarray(x, dtype=np.float32))
+    dy = _c(np.asarray(dy, dtype=np.float32))
+    if x.ndim == 1:
+        x, dy = x[None, :], dy[None, :]
+    assert dy.shape == x.shape
+    rows, d = x.shape
+    dx = np.zeros((rows, d), np.float64)
+    rc = _load().oracle_stat_topk_huber_backward(_ptr(x), _ptr(dy), rows, d, int(k), float(delta), _ptr(dx))
+    if rc != 0:
+        raise ValueError("oracle_stat_topk_huber_backward: bad arguments")
+    return dx

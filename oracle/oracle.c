@@ -209,6 +209,108 @@ int oracle_stat_topk(const float *x, int64_t rows, int64_t d, int64_t ldx, int64
 }
 
 /*
+ * Training side of the statistical top-k (notes, "Statistical Top-k" item,
+ * differentiability bullet: with Huber smoothing the operator becomes
+ * continuously differentiable).  The pages name the smoothing but do not
+ * print it; the reading taken here replaces the soft-threshold max{u, 0},
+ * u = x - theta, by its Huber smoothing of width delta > 0,
+ *     h(u) = 0 (u <= 0),  u^2 / (2 delta) (0 < u < delta),  u - delta / 2 (u >= delta),
+ * the integral from 0 to u of min(max(t / delta, 0), 1): a quadratic joint in
+ * place of the kink, continuously differentiable, within delta / 2 of
+ * max{u, 0} and equal to it as delta -> 0.  theta is the same
+ * mean + std * Q(1 - k/d) as in the forward operator, and its dependence on
+ * every x_j is part of the gradient.
+ */
+double oracle_huber_relu(double u, double delta)
+{
+    if (u <= 0.0) return 0.0;
+    if (u < delta) return u * u / (2.0 * delta);
+    return u - 0.5 * delta;
+}
+
+/* h'(u) = min(max(u / delta, 0), 1). */
+double oracle_huber_relu_grad(double u, double delta)
+{
+    if (u <= 0.0) return 0.0;
+    if (u < delta) return u / delta;
+    return 1.0;
+}
+
+/* Mean and population std of one fp32 row, two passes in ascending order. */
+static void row_moments(const float *x, int64_t d, double *mean, double *sd)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < d; ++i)
+        s += (double)x[i];
+    const double mu = s / (double)d;
+    double ss = 0.0;
+    for (int64_t i = 0; i < d; ++i)
+        ss += ((double)x[i] - mu) * ((double)x[i] - mu);
+    *mean = mu;
+    *sd = sqrt(ss / (double)d);
+}
+
+/*
+ * Forward: y[r][i] = h(x[r][i] - theta_r) for every entry (a dense [rows][d]
+ * result, zero below the threshold).  theta [rows] may be NULL.  Returns 0,
+ * or -1 on bad arguments.
+ */
+int oracle_stat_topk_huber_forward(const float *x, int64_t rows, int64_t d, int64_t k, double delta, double *y,
+                                   double *theta)
+{
+    if (!x || !y || rows < 0 || d <= 0 || k <= 0 || k >= d || !(delta > 0.0))
+        return -1;
+    const double z = oracle_threshold_z(k, d);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double mu, sd;
+        row_moments(x + r * d, d, &mu, &sd);
+        const double th = mu + sd * z;
+        for (int64_t i = 0; i < d; ++i)
+            y[r * d + i] = oracle_huber_relu((double)x[r * d + i] - th, delta);
+        if (theta) theta[r] = th;
+    }
+    return 0;
+}
+
+/*
+ * Backward: given dy = dL/dy, dx = dL/dx by the chain rule through
+ * y_i = h(x_i - theta(x)):
+ *     a_i = dy_i h'(x_i - theta),   A = sum_i a_i,
+ *     d theta / d x_j = 1/d + z (x_j - mean) / (d std)   (d mean/dx_j = 1/d,
+ *                                   d std/dx_j = (x_j - mean) / (d std)),
+ *     dx_j = a_j - A d theta / d x_j.
+ * A row with zero spread has x_i - theta = 0 everywhere, so a = 0, A = 0 and
+ * dx = 0 (its std term, 0/0, is never formed).  Returns 0, or -1 on bad
+ * arguments.
+ */
+int oracle_stat_topk_huber_backward(const float *x, const float *dy, int64_t rows, int64_t d, int64_t k,
+                                    double delta, double *dx)
+{
+    if (!x || !dy || !dx || rows < 0 || d <= 0 || k <= 0 || k >= d || !(delta > 0.0))
+        return -1;
+    const double z = oracle_threshold_z(k, d);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double mu, sd;
+        row_moments(x + r * d, d, &mu, &sd);
+        const double th = mu + sd * z;
+        double A = 0.0;
+        for (int64_t i = 0; i < d; ++i) {
+            const double a = (double)dy[r * d + i] * oracle_huber_relu_grad((double)x[r * d + i] - th, delta);
+            dx[r * d + i] = a;
+            A += a;
+        }
+        for (int64_t j = 0; j < d; ++j) {
+            double dth = 1.0 / (double)d;
+            if (sd > 0.0) dth += z * ((double)x[r * d + j] - mu) / ((double)d * sd);
+            dx[r * d + j] -= A * dth;
+        }
+    }
+    return 0;
+}
+
+/*
  * One Spark FFN evaluation for one token, q given in fp64 (length d_model).
  * Weights in the stored layouts: k1t [d_ff][r] (K1 transposed: row i is the
  * predictor key of neuron i), k2t [d_ff][d_model-r] (K2 transposed), v

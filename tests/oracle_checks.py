@@ -344,7 +344,113 @@ def check_decode_chain():
         assert rel(res["y"][t], y) < 1e-12
 
 
+# ---------------------------------------------------------------- P15 training side (Huber smoothing)
+def check_huber_function():
+    """h(u) against numerical integration of its derivative clamp(t / delta, 0, 1)
+    (scipy quad), h' against central differences of h, continuity at the joints,
+    and the distance to max{u, 0} (at most delta / 2, reached for u >= delta)."""
+    from scipy.integrate import quad
+
+    for delta in (1e-3, 0.25, 2.0):
+        for u in np.concatenate([np.linspace(-2 * delta, 3 * delta, 41), [delta, 0.0, 5.0, -5.0]]):
+            val, _ = quad(lambda t: min(max(t / delta, 0.0), 1.0), 0.0, max(u, 0.0), points=[delta], limit=200)
+            assert abs(oracle.huber_relu(u, delta) - val) <= 1e-12 * max(1.0, abs(val)), (u, delta)
+            e = 1e-7 * delta
+            fd = (oracle.huber_relu(u + e, delta) - oracle.huber_relu(u - e, delta)) / (2 * e)
+            assert abs(oracle.huber_relu_grad(u, delta) - fd) <= 1e-5, (u, delta, fd)
+            assert 0.0 <= max(u, 0.0) - oracle.huber_relu(u, delta) <= delta / 2 + 1e-15
+        e = 1e-9 * delta
+        for j in (0.0, delta):  # value and slope continuous at the joints
+            l, r = oracle.huber_relu(j - e, delta), oracle.huber_relu(j + e, delta)
+            assert abs(l - r) <= 4 * e
+            assert abs(oracle.huber_relu_grad(j - e, delta) - oracle.huber_relu_grad(j + e, delta)) < 1e-8
+        assert oracle.huber_relu(10 * delta, delta) == 10 * delta - delta / 2
+
+
+def _quantised_rows(seed, rows, d, scale=1.0):
+    """Rows of multiples of 1/256 (exact in fp32, as are x +- 2^-12)."""
+    g = np.random.default_rng(seed)
+    return (np.round(g.standard_normal((rows, d)) * scale * 256) / 256).astype(np.float32)
+
+
+def check_huber_limit():
+    """delta -> 0: the smoothed forward is the soft-threshold max{x - theta, 0} of the
+    statistical top-k (the separately pinned unsmoothed operator)."""
+    x = synth.stat_rows(5, 16, 300)
+    base = oracle.stat_topk(x, 25)
+    for delta in (1e-6, 1e-9):
+        res = oracle.stat_topk_huber(x, 25, delta)
+        assert np.allclose(res["theta"], base["theta"], rtol=0, atol=1e-13)
+        for r in range(x.shape[0]):
+            dense = np.zeros(x.shape[1])
+            n = base["counts"][r]
+            dense[base["idx"][r, :n]] = base["vals"][r, :n]
+            assert np.abs(res["y"][r] - dense).max() <= delta / 2 + 1e-13, r
+
+
+def check_huber_gradient_fd():
+    """The backward against central differences of L(x) = sum_i dy_i y_i(x), the
+    forward evaluated by the oracle itself, on inputs that keep every x_i - theta
+    away from the joints 0 and delta by more than the step."""
+    eps, delta = 2.0 ** -12, 0.25
+    checked = 0
+    for seed in range(40):
+        for d, k in ((8, 2), (33, 5), (64, 9)):
+            x = _quantised_rows(seed + 100 * d, 1, d)[0]
+            th = oracle.stat_topk_huber(x, k, delta)["theta"][0]
+            u = x.astype(np.float64) - th
+            if np.min(np.abs(u)) < 4e-3 or np.min(np.abs(u - delta)) < 4e-3:
+                continue
+            dy = np.random.default_rng(seed).standard_normal(d).astype(np.float32)
+            grad = oracle.stat_topk_huber_backward(x, dy, k, delta)[0]
+
+            def loss(xx):
+                return float(np.dot(dy.astype(np.float64), oracle.stat_topk_huber(xx, k, delta)["y"][0]))
+
+            fd = np.zeros(d)
+            for j in range(d):
+                xp, xm = x.copy(), x.copy()
+                xp[j] += np.float32(eps)
+                xm[j] -= np.float32(eps)
+                fd[j] = (loss(xp) - loss(xm)) / (2 * eps)
+            assert np.abs(grad - fd).max() <= 1e-5 * max(1.0, np.abs(fd).max()), (seed, d, np.abs(grad - fd).max())
+            checked += 1
+    assert checked >= 40, checked
+
+
+def check_huber_autograd():
+    """The backward against torch autograd (fp64) of the same forward."""
+    for seed, (rows, d, k, delta) in enumerate(((4, 50, 6, 0.3), (3, 1000, 80, 0.05), (2, 9216, 737, 0.01))):
+        x = synth.stat_rows(seed + 40, rows, d)
+        dy = np.random.default_rng(seed).standard_normal((rows, d)).astype(np.float32)
+        got = oracle.stat_topk_huber_backward(x, dy, k, delta)
+        xt = torch.from_numpy(x.astype(np.float64)).requires_grad_(True)
+        th = xt.mean(1, keepdim=True) + xt.std(1, correction=0, keepdim=True) * float(ndtri(1 - k / d))
+        u = xt - th
+        h = torch.where(u <= 0, torch.zeros_like(u), torch.where(u < delta, u * u / (2 * delta), u - delta / 2))
+        (h * torch.from_numpy(dy.astype(np.float64))).sum().backward()
+        ref = xt.grad.numpy()
+        assert rel(got, ref) < 1e-10, (seed, rel(got, ref))
+
+
+def check_huber_invariances():
+    """A common shift of a row moves theta with it and leaves y unchanged, so the
+    gradient sums to zero along each row; a constant row gives y = 0 and dx = 0."""
+    x = _quantised_rows(7, 5, 200)
+    dy = np.random.default_rng(3).standard_normal(x.shape).astype(np.float32)
+    a = oracle.stat_topk_huber(x, 20, 0.1)
+    b = oracle.stat_topk_huber(x + np.float32(3.0), 20, 0.1)
+    assert np.abs(a["y"] - b["y"]).max() < 1e-12 and np.allclose(b["theta"] - a["theta"], 3.0, atol=1e-12)
+    g = oracle.stat_topk_huber_backward(x, dy, 20, 0.1)
+    assert np.abs(g.sum(1)).max() < 1e-12 * max(1.0, np.abs(g).max() * x.shape[1])
+    assert np.abs(g).max() > 0
+    c = np.full((2, 64), 1.5, np.float32)
+    assert np.all(oracle.stat_topk_huber(c, 6, 0.1)["y"] == 0)
+    assert np.all(oracle.stat_topk_huber_backward(c, np.ones_like(c), 6, 0.1) == 0)
+
+
 ALL_CHECKS = [check_quantile, check_threshold_closed_form, check_special_rows, check_quantile_grid,
               check_invariants, check_scale_invariance, check_theorem31, check_student_t, check_ffn_dense_masked,
               check_ffn_bf16_widening, check_topk_is_largest, check_activations, check_attention,
-              check_attention_prefill, check_continuity, check_decode_chain]
+              check_attention_prefill, check_continuity, check_decode_chain, check_huber_function,
+              check_huber_limit, check_huber_gradient_fd, check_huber_autograd, check_huber_invariances]

@@ -29,6 +29,12 @@ int oracle_decode_stack(int64_t d_model, int64_t d_ff, int64_t r, int64_t k, int
 int oracle_spark_attn_decode(int dtype, const void *q, const void *k1, const void *k2, const void *v, int64_t Hq,
                              int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn, double *out,
                              int32_t *counts, double *theta, double *scores);
+double oracle_huber_relu(double u, double delta);
+double oracle_huber_relu_grad(double u, double delta);
+int oracle_stat_topk_huber_forward(const float *x, int64_t rows, int64_t d, int64_t k, double delta, double *y,
+                                   double *theta);
+int oracle_stat_topk_huber_backward(const float *x, const float *dy, int64_t rows, int64_t d, int64_t k,
+                                    double delta, double *dx);
 int oracle_spark_attn_prefill(int dtype, const void *q, const void *k1, const void *k2, const void *v, int64_t T,
                               int64_t Hq, int64_t Hkv, int64_t hd, int64_t r, int64_t k_attn, double *out,
                               int32_t *counts, double *theta);
@@ -146,6 +152,27 @@ int main(void)
         EXPECT(oracle_spark_attn_prefill(1, qp, k1, k2, v, T, Hq, Hkv, hd, r, 8, op, cp, tp) == 0);
         for (int64_t i = 0; i < T * Hq; ++i) EXPECT(cp[i] > 0 && cp[i] <= i / Hq + 1 && isfinite(op[i * hd]));
         free(q), free(k1), free(k2), free(v), free(out), free(sc), free(qp), free(op), free(tp), free(cp);
+    }
+    /* training side: Huber-smoothed statistical top-k, forward and gradient */
+    {
+        const int64_t rows = 5, d = 300, k = 25;
+        float *x = f32s(rows * d, 1.0), *dy = f32s(rows * d, 1.0);
+        double *y = malloc(sizeof(double) * rows * d), *dx = malloc(sizeof(double) * rows * d), th[5];
+        EXPECT(oracle_stat_topk_huber_forward(x, rows, d, k, 0.1, y, th) == 0);
+        EXPECT(oracle_stat_topk_huber_backward(x, dy, rows, d, k, 0.1, dx) == 0);
+        for (int64_t r = 0; r < rows; ++r) {
+            double s = 0.0, m = 0.0;
+            for (int64_t i = 0; i < d; ++i) {
+                EXPECT(y[r * d + i] >= 0.0 && isfinite(dx[r * d + i]));
+                s += dx[r * d + i];
+                m = fmax(m, fabs(dx[r * d + i]));
+            }
+            EXPECT(fabs(s) <= 1e-9 * (1.0 + m * d));
+        }
+        EXPECT(oracle_stat_topk_huber_forward(x, rows, d, k, 0.0, y, th) == -1);
+        EXPECT(oracle_stat_topk_huber_backward(x, dy, rows, d, d, 0.1, dx) == -1);
+        EXPECT(oracle_huber_relu(-1.0, 0.5) == 0.0 && oracle_huber_relu_grad(2.0, 0.5) == 1.0);
+        free(x), free(dy), free(y), free(dx);
     }
     printf("oracle driver: %d failures\n", failures);
     return failures == 0 ? 0 : 1;

@@ -34,12 +34,20 @@ MUTANTS = [
     ("bf16_widen_shift", "uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16;",
      "uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 15;"),
     ("mean_off_by_one", "double mean = s / (double)d;", "double mean = s / (double)(d + 1);"),
+    ("huber_quadratic_scale", "if (u < delta) return u * u / (2.0 * delta);", "if (u < delta) return u * u / delta;"),
+    ("huber_grad_slope", "if (u < delta) return u / delta;", "if (u < delta) return 1.0;"),
+    ("huber_backward_no_std_term", "if (sd > 0.0) dth += z", "if (sd < 0.0) dth += z"),
+    ("huber_backward_no_mean_term", "double dth = 1.0 / (double)d;", "double dth = 0.0;"),
+    ("huber_backward_sign", "dx[r * d + j] -= A * dth;", "dx[r * d + j] += A * dth;"),
+    ("huber_sample_std", "*sd = sqrt(ss / (double)d);", "*sd = sqrt(ss / (double)(d - 1));"),
 ]
 
 # faster, smaller versions of the slow checks are enough to catch the mutants
 FAST = [oc.check_quantile, oc.check_threshold_closed_form, oc.check_special_rows, oc.check_quantile_grid,
         oc.check_invariants, oc.check_ffn_dense_masked, oc.check_ffn_bf16_widening, oc.check_activations,
-        oc.check_attention, oc.check_attention_prefill, oc.check_continuity, oc.check_decode_chain]
+        oc.check_attention, oc.check_attention_prefill, oc.check_continuity, oc.check_decode_chain,
+        oc.check_huber_function, oc.check_huber_limit, oc.check_huber_gradient_fd, oc.check_huber_autograd,
+        oc.check_huber_invariances]
 
 
 def _caught(path):
