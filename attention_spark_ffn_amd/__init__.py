@@ -8,6 +8,9 @@ RuntimeError is raised.
 
 Entry points (same names as the C ABI):
   stat_topk(x, k, cap=None)                         -> (vals, idx, counts, theta)
+  stat_topk_huber(x, k, delta)                      -> (y, theta)   Huber-smoothed, dense
+  stat_topk_huber_backward(x, dy, k, delta)         -> dx
+  StatTopkHuber.apply(x, k, delta)                  -> y, as a torch.autograd.Function
   spark_ffn_decode(q, layers, k, r, eps, ...)       -> y  (and a trace dict)
   spark_ffn_decode_noalloc(q, layers, k, r, eps, ...)  -> the same, no device allocation by the library
   spark_ffn_decode_batched(q, layers, k, r, eps, ...)  -> the same, B <= 8 tokens layer by layer
@@ -65,6 +68,10 @@ def lib() -> ctypes.CDLL:
                 L.spark_status_string.argtypes = [_ci]
                 L.spark_threshold_z.restype = _d
                 L.spark_threshold_z.argtypes = [_i64, _i64]
+                L.stat_topk_huber_forward.restype = _ci
+                L.stat_topk_huber_forward.argtypes = [_vp, _i64, _i64, _i64, _f, _vp, _vp, _vp]
+                L.stat_topk_huber_backward.restype = _ci
+                L.stat_topk_huber_backward.argtypes = [_vp, _vp, _i64, _i64, _i64, _f, _vp, _vp]
                 L.stat_topk.restype = _ci
                 L.stat_topk.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp]
                 L.spark_ffn_decode.restype = _ci
@@ -79,6 +86,11 @@ def lib() -> ctypes.CDLL:
                 L.spark_ffn_prefill.restype = _ci
                 L.spark_ffn_prefill.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _vp, _i64, _vp,
                                                 ctypes.POINTER(TraceC), _vp, _sz, _vp]
+                L.spark_ffn_prefill_scores.restype = _ci
+                L.spark_ffn_prefill_scores.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _vp, _i64,
+                                                       _vp, _vp]
+                L.spark_hbm_read_probe.restype = _ci
+                L.spark_hbm_read_probe.argtypes = [_vp, _sz, _vp, _vp]
                 L.spark_attn_decode.restype = _ci
                 L.spark_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
                                                 _vp, _i64, _vp, _vp, _sz, _vp]
@@ -163,6 +175,55 @@ def stat_topk(x: torch.Tensor, k: int, cap: int | None = None):
                          _p(theta), _stream(dev))
     _check(st, "stat_topk")
     return vals, idx, counts, theta
+
+
+# ---------------------------------------------------------------------------- training side
+def _rows_f32(*ts):
+    for t in ts:
+        if t.dim() != 2 or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("expected contiguous 2-D fp32 HIP tensors")
+
+
+def stat_topk_huber(x: torch.Tensor, k: int, delta: float):
+    """Huber-smoothed statistical top-k of each row of fp32 x [rows][d]: the
+    dense y [rows][d] = h(x - theta) and theta [rows]."""
+    _rows_f32(x)
+    rows, d = x.shape
+    y = torch.empty_like(x)
+    theta = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(lib().stat_topk_huber_forward(_p(x), rows, d, int(k), float(delta), _p(y), _p(theta), _stream(x.device)),
+           "stat_topk_huber_forward")
+    return y, theta
+
+
+def stat_topk_huber_backward(x: torch.Tensor, dy: torch.Tensor, k: int, delta: float) -> torch.Tensor:
+    """dL/dx of the Huber-smoothed statistical top-k at input x, given dy = dL/dy."""
+    _rows_f32(x, dy)
+    if dy.shape != x.shape:
+        raise ValueError("dy must have the shape of x")
+    rows, d = x.shape
+    dx = torch.empty_like(x)
+    _check(lib().stat_topk_huber_backward(_p(x), _p(dy), rows, d, int(k), float(delta), _p(dx), _stream(x.device)),
+           "stat_topk_huber_backward")
+    return dx
+
+
+class StatTopkHuber(torch.autograd.Function):
+    """y = StatTopkHuber.apply(x, k, delta): the smoothed operator as an
+    autograd function (forward and backward both run in the HIP kernels)."""
+
+    @staticmethod
+    def forward(ctx, x, k, delta):
+        x = x.contiguous()
+        y, _ = stat_topk_huber(x, k, delta)
+        ctx.save_for_backward(x)
+        ctx.k, ctx.delta = int(k), float(delta)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        (x,) = ctx.saved_tensors
+        return stat_topk_huber_backward(x, dy.contiguous(), ctx.k, ctx.delta), None, None
 
 
 # ---------------------------------------------------------------------------- workspaces
@@ -396,6 +457,28 @@ def spark_ffn_prefill(Q: torch.Tensor, layer, k: int, r: int, trace: bool = Fals
                                  ctypes.byref(trc) if trc is not None else None, _p(ws), ws.numel(), _stream(dev))
     _check(st, "spark_ffn_prefill")
     return (Y, tr) if trace else Y
+
+
+def spark_ffn_prefill_scores(Q: torch.Tensor, layer, r: int) -> torch.Tensor:
+    """The predictor step of the prefill alone: H [T][d_ff] fp32 = Q[:, :r] K1."""
+    _need_cuda(Q, *layer)
+    T, d_model = Q.shape
+    k1t = layer[0]
+    d_ff = k1t.shape[0]
+    if k1t.shape != (d_ff, r) or Q.dtype != torch.bfloat16 or k1t.dtype != torch.bfloat16:
+        raise ValueError("need bf16 Q [T][d_model] and k1t [d_ff][r]")
+    shape = _shape(d_model, d_ff, r, 1, SPARK_BF16)
+    w = WeightsC(k1t.data_ptr(), layer[1].data_ptr(), layer[2].data_ptr())
+    H = torch.empty((T, d_ff), dtype=torch.float32, device=Q.device)
+    _check(lib().spark_ffn_prefill_scores(ctypes.byref(shape), ctypes.byref(w), _p(Q), T, _p(H), _stream(Q.device)),
+           "spark_ffn_prefill_scores")
+    return H
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Stream every byte of buf (a measurement helper; see the header)."""
+    _check(lib().spark_hbm_read_probe(_p(buf), buf.numel() * buf.element_size(), _p(sink), _stream(buf.device)),
+           "spark_hbm_read_probe")
 
 
 # ---------------------------------------------------------------------------- attention

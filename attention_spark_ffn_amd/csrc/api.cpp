@@ -93,6 +93,30 @@ int stat_topk(const float* x, int64_t rows, int64_t d, int64_t ldx, int64_t k, f
   return hip_status(spark::launch_stat_topk(x, rows, d, ldx, z, vals, idx, cap, counts, theta, stream));
 }
 
+static int check_huber(const float* x, const void* other, const float* out, int64_t rows, int64_t d, int64_t k,
+                       float delta) {
+  if (rows < 0 || d <= 0 || k <= 0 || k >= d || !(delta > 0.f) || !std::isfinite(delta)) return SPARK_EINVAL;
+  if (d > 65536) return SPARK_EUNSUPPORTED;
+  if (rows > 0 && (!x || !other || !out)) return SPARK_EINVAL;
+  return SPARK_OK;
+}
+
+int stat_topk_huber_forward(const float* x, int64_t rows, int64_t d, int64_t k, float delta, float* y, float* theta,
+                            hipStream_t stream) {
+  const int st = check_huber(x, y, y, rows, d, k, delta);
+  if (st != SPARK_OK || rows == 0) return st;
+  return hip_status(spark::launch_stat_topk_huber(false, x, nullptr, rows, d, spark_threshold_z(k, d), delta, y, theta,
+                                                  stream));
+}
+
+int stat_topk_huber_backward(const float* x, const float* dy, int64_t rows, int64_t d, int64_t k, float delta,
+                             float* dx, hipStream_t stream) {
+  const int st = check_huber(x, dy, dx, rows, d, k, delta);
+  if (st != SPARK_OK || rows == 0) return st;
+  return hip_status(spark::launch_stat_topk_huber(true, x, dy, rows, d, spark_threshold_z(k, d), delta, dx, nullptr,
+                                                  stream));
+}
+
 int64_t spark_ffn_decode_tags(int n_layers, int64_t T) {
   if (n_layers < 1 || T < 0) return -1;
   const int64_t launches = (n_layers + spark::kDecodeMaxLayersPerLaunch - 1) / spark::kDecodeMaxLayersPerLaunch;
@@ -217,6 +241,25 @@ int spark_ffn_prefill(const spark_ffn_shape* s, const spark_ffn_weights* w, cons
   if (T == 0) return SPARK_OK;
   const double z = spark_threshold_z(s->k, s->d_ff);
   return hip_status(spark::launch_prefill(*s, *w, Q, T, Y, z, trace, ws, stream));
+}
+
+int spark_ffn_prefill_scores(const spark_ffn_shape* s, const spark_ffn_weights* w, const void* Q, int64_t T, float* H,
+                             hipStream_t stream) {
+  size_t need = 0;
+  const int st = spark_ffn_prefill_workspace_size(s, T, &need);  // the same shape limits as the whole prefill
+  if (st != SPARK_OK) return st;
+  if (!w) return SPARK_EINVAL;
+  const int sw = check_weights(*w);
+  if (sw != SPARK_OK) return sw;
+  if (T > 0 && (!Q || !H || !aligned(Q, 16))) return SPARK_EINVAL;
+  if (T == 0) return SPARK_OK;
+  return hip_status(spark::launch_prefill_scores(*s, *w, Q, T, H, stream));
+}
+
+int spark_hbm_read_probe(const void* p, size_t bytes, float* sink, hipStream_t stream) {
+  if (!p || !sink || bytes % 16 != 0 || !aligned(p, 16)) return SPARK_EINVAL;
+  if (bytes == 0) return SPARK_OK;
+  return hip_status(spark::launch_hbm_read_probe(p, bytes, sink, stream));
 }
 
 int spark_attn_workspace_size(int64_t Hq, int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn,

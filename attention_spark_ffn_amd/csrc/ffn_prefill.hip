@@ -66,6 +66,41 @@ size_t prefill_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t T) {
   return prefill_layout(d_model, d_ff, T).total;
 }
 
+hipError_t launch_prefill_scores(const spark_ffn_shape& s, const spark_ffn_weights& w, const void* Q, int64_t T,
+                                 float* H, hipStream_t st) {
+  const int M = (int)T, F = (int)s.d_ff, r = (int)s.r, dm = (int)s.d_model;
+  return launch_gemm<kEpiStore>(gemm_args((const bf16_t*)Q, dm, (const bf16_t*)w.k1t, r, H, F, M, F, r), 1, 1, st);
+}
+
+// Streaming read of `bytes` bytes (a multiple of 16, 16-byte aligned): every
+// thread sums the 16-byte chunks it reads, four loads in flight; the sum is
+// stored only if it equals a value no finite data gives, so the loads stay
+// and nothing is written.
+__global__ __launch_bounds__(256) void hbm_read_probe(const u32x4* __restrict__ p, size_t n, float* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float acc = 0.f;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += __uint_as_float(v[u].x ^ v[u].y ^ v[u].z ^ v[u].w);
+  }
+  for (; i < n; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc += __uint_as_float(v.x ^ v.y ^ v.z ^ v.w);
+  }
+  if (__float_as_uint(acc) == 0x7fbadbadu) sink[0] = acc;
+}
+
+hipError_t launch_hbm_read_probe(const void* p, size_t bytes, float* sink, hipStream_t st) {
+  int cus = device_cu_count();
+  if (cus < 1) cus = 256;
+  hipLaunchKernelGGL(hbm_read_probe, dim3((unsigned)(8 * cus)), dim3(256), 0, st, (const u32x4*)p, bytes / 16, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill(const spark_ffn_shape& s, const spark_ffn_weights& w, const void* Q, int64_t T, float* Y,
                           double z, const spark_ffn_trace* trace, void* ws, hipStream_t st) {
   const PrefillLayout L = prefill_layout(s.d_model, s.d_ff, T);

@@ -13,6 +13,11 @@ namespace spark {
 hipError_t launch_stat_topk(const float* x, int64_t rows, int64_t d, int64_t ldx, double z, float* vals, int32_t* idx,
                             int64_t cap, int32_t* counts, float* theta, hipStream_t st);
 
+// ---------------------------------------------------------------- training side (Huber-smoothed stat top-k)
+// backward = false: out = y (theta may be null); backward = true: out = dx from dy.
+hipError_t launch_stat_topk_huber(bool backward, const float* x, const float* dy, int64_t rows, int64_t d, double z,
+                                  float delta, float* out, float* theta, hipStream_t st);
+
 // ---------------------------------------------------------------- decode
 // Layers handled by one launch of the persistent decode kernel.
 constexpr int kDecodeMaxLayersPerLaunch = 32;
@@ -47,6 +52,9 @@ hipError_t launch_decode_batched(const spark_ffn_shape& s, const spark_ffn_weigh
 size_t prefill_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t T);
 hipError_t launch_prefill(const spark_ffn_shape& s, const spark_ffn_weights& w, const void* Q, int64_t T, float* Y,
                           double z, const spark_ffn_trace* trace, void* ws, hipStream_t st);
+hipError_t launch_prefill_scores(const spark_ffn_shape& s, const spark_ffn_weights& w, const void* Q, int64_t T,
+                                 float* H, hipStream_t st);
+hipError_t launch_hbm_read_probe(const void* p, size_t bytes, float* sink, hipStream_t st);
 
 // ---------------------------------------------------------------- attention
 size_t attn_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn);

@@ -16,6 +16,7 @@
 // stores.  One HBM read of the row, writes only the survivors.
 #include "common.hpp"
 #include "internal.hpp"
+#include "rows.hpp"
 
 namespace spark {
 
@@ -32,26 +33,6 @@ struct StatShared {
   int s_idx[kStage];
   float s_val[kStage];
 };
-
-// Lane t's elements 4t + 4*NT*e + j (e < E, j < 4) of one row.  Entries past
-// the row end are 0.  EXACT: d == 4*NT*E, no bounds tests.
-template <int NT, int E, bool VEC, bool EXACT>
-__device__ __forceinline__ void load_row(const float* xr, int d, int tid, float (&v)[E][4]) {
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i0 = 4 * tid + 4 * NT * e;
-    if (EXACT || (VEC && i0 + 3 < d)) {
-      const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xr + i0));
-      v[e][0] = t.x;
-      v[e][1] = t.y;
-      v[e][2] = t.z;
-      v[e][3] = t.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[e][j] = i0 + j < d ? xr[i0 + j] : 0.f;
-    }
-  }
-}
 
 // Statistics, threshold and list of one row held in registers.
 template <int NT, int E, bool EXACT>

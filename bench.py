@@ -78,8 +78,23 @@ def cpu_baseline(layers_np, budget_s: float = 15.0):
     t0 = time.perf_counter()
     oracle.decode_stack(qs, layers_np, R, K, 1e-6)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n} tokens through the same 26-layer stack (fp64 C oracle, OpenMP), {dt:.1f} s"}
+    out = {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"{n} tokens through the same 26-layer stack (fp64 C oracle, OpenMP), {dt:.1f} s"}
+    # the same oracle computing one layer densely (every neuron's K2 dot and V
+    # row, unselected neurons weighted by zero) against the sparse layer on the
+    # same tokens: the CPU sparse-vs-dense ratio
+    nq = 32
+    ql = np.random.default_rng(777).standard_normal((nq, D_MODEL)).astype(np.float32)
+    t0 = time.perf_counter()
+    oracle.spark_ffn(ql, *layers_np[0], R, K)
+    t_sparse = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.spark_ffn_dense(ql, *layers_np[0], R, K)
+    t_dense = time.perf_counter() - t0
+    out["dense_masked"] = {"sparse_layer_tokens_per_s": nq / t_sparse, "dense_layer_tokens_per_s": nq / t_dense,
+                           "sparse_over_dense_speedup": t_dense / t_sparse,
+                           "sample": f"{nq} tokens through layer 0, sparse and dense-masked oracle"}
+    return out
 
 
 def _time_ms(torch, fn, reps=20, warm=3):
@@ -100,6 +115,18 @@ def _time_ms(torch, fn, reps=20, warm=3):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def read_ceiling(torch, sf, dev, gib: int = 4, reps: int = 10) -> float:
+    """HBM read ceiling on this device: GB/s of the library's streaming-read
+    probe over a buffer far larger than the caches (median of reps)."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, device=dev)
+    ms = _time_ms(torch, lambda: sf.hbm_read_probe(buf, sink), reps=reps)
+    del buf
+    torch.cuda.empty_cache()
+    return (gib << 30) / ms / 1e6
 
 
 def _oracle_rate(fn, n_units: int, unit: str, sample: str) -> dict:
@@ -167,7 +194,30 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
         xs = synth.stat_rows(seed, 2000, d)
         res["stat_topk"]["cpu_baseline"] = _oracle_rate(lambda: oracle.stat_topk(xs, k, cap), 2000, "rows/s",
                                                         "2000 rows of 9216 (same recipe, host-generated)")
-    del x, vals, idx
+    del vals, idx
+    torch.cuda.empty_cache()
+    # training side on the same rows: Huber-smoothed forward (read x, write y)
+    # and its gradient (read x and dy, write dx)
+    delta = 0.01
+    y = torch.empty_like(x)
+    dyt = torch.randn((rows, d), generator=g, device=dev)
+    ms_f = _time_ms(torch, lambda: sf.stat_topk_huber(x, k, delta), reps=10)
+    ms_b = _time_ms(torch, lambda: sf.stat_topk_huber_backward(x, dyt, k, delta), reps=10)
+    bf_, bb_ = rows * d * 8 + rows * 4, rows * d * 12
+    res["stat_topk_train"] = {
+        "workload": "Huber-smoothed statistical top-k, 65536 x 9216 fp32 rows, k 737, delta 0.01",
+        "forward_ms": ms_f, "backward_ms": ms_b,
+        "roofline_forward": {"bound": "hbm", "achieved": bf_ / ms_f / 1e6, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": bf_ / ms_f / 1e6 / HBM_PEAK_GBS},
+        "roofline_backward": {"bound": "hbm", "achieved": bb_ / ms_b / 1e6, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": bb_ / ms_b / 1e6 / HBM_PEAK_GBS}}
+    if with_cpu:
+        xs = synth.stat_rows(seed, 500, d)
+        gs = np.random.default_rng(seed).standard_normal(xs.shape).astype(np.float32)
+        res["stat_topk_train"]["cpu_baseline"] = _oracle_rate(
+            lambda: (oracle.stat_topk_huber(xs, k, delta), oracle.stat_topk_huber_backward(xs, gs, k, delta)), 500,
+            "rows/s", "forward and gradient of 500 rows of 9216 (same recipe, host-generated)")
+    del x, y, dyt
     torch.cuda.empty_cache()
     # prefill: 4096 tokens through one 2304 x 9216 layer, bf16
     T = 4096
@@ -176,20 +226,32 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
     layer = tuple(bf(a) for a in lw)
     Q = bf(synth.queries(seed, T, D_MODEL, "bf16"))
     ms = _time_ms(torch, lambda: sf.spark_ffn_prefill(Q, layer, K, R), reps=10)
+    _, ptr = sf.spark_ffn_prefill(Q, layer, K, R, trace=True, cap=1)
+    nsel = float(ptr["counts"].double().sum().item())
     flops = 2.0 * T * R * D_FF
+    # the method's own work: the dense predictor product, and per token the
+    # selected neurons' K2 dots and V rows
+    method = flops + 2.0 * nsel * ((D_MODEL - R) + D_MODEL)
+    # the predictor product alone (its own entry point), HIP events
+    pred_ms = _time_ms(torch, lambda: sf.spark_ffn_prefill_scores(Q, layer, R), reps=50)
     Qr = Q[:, :R].contiguous()
     K1 = layer[0].t().contiguous()  # [r][d_ff]
     ref_ms = _time_ms(torch, lambda: torch.mm(Qr, K1), reps=10)
     del Qr, K1
-    # the three products run dense on the matrix cores (unselected neurons
+    # the products as run: dense on the matrix cores (unselected neurons
     # contribute exact zeros): scores, gated K2 values, and C V
     dense = 2.0 * T * D_FF * (R + (D_MODEL - R) + D_MODEL)
     res["prefill"] = {"workload": "4096 tokens, one 2304 x 9216 layer (r 1152, k 737), bf16", "ms": ms,
-                      "tokens_per_s": T / ms * 1e3, "us_per_token": ms * 1e3 / T, "predictor_gflop": flops / 1e9,
-                      "dense_products_gflop": dense / 1e9,
-                      "roofline": {"bound": "mfma", "achieved": dense / ms / 1e9, "peak": MFMA_BF16_PEAK_TFLOPS,
-                                   "unit": "TFLOP/s", "frac": dense / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
-                                   "note": "all three products (scores, gated K2, C V) over the whole call"},
+                      "tokens_per_s": T / ms * 1e3, "us_per_token": ms * 1e3 / T, "mean_selected": nsel / T,
+                      "method_gflop": method / 1e9, "dense_products_gflop": dense / 1e9,
+                      "roofline": {"bound": "mfma", "achieved": method / ms / 1e9, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": method / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+                                   "note": "the method's FLOPs (2 T r d_ff + 2 sum_t |S_t| (d_model - r + d_model)) "
+                                           "over the whole call"},
+                      "predictor_gemm": {"us": pred_ms * 1e3, "gflop": flops / 1e9,
+                                         "roofline": {"bound": "mfma", "achieved": flops / pred_ms / 1e9,
+                                                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                                      "frac": flops / pred_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}},
                       "hipblaslt_predictor_gemm_ms": ref_ms,
                       "hipblaslt_predictor_tflops": flops / ref_ms / 1e9}
     if with_cpu:
@@ -318,6 +380,7 @@ def main():
     avg_launch_s = per_launch_ms.mean() / 1e3
     achieved_gbs = bytes_per_token.mean() / avg_launch_s / 1e9
     traffic = load_traffic()
+    probe_gbs = read_ceiling(torch, sf, dev)
 
     out = {
         "metric": METRIC,
@@ -341,8 +404,10 @@ def main():
                      "kernel": "spark::decode_kernel<bf16>",
                      "algorithmic_bytes_per_launch": float(bytes_per_token.mean()),
                      "avg_launch_us": avg_launch_s * 1e6,
+                     "median_us": float(np.median(per_launch_ms) * 1e3),
                      "p10_us": float(np.percentile(per_launch_ms, 10) * 1e3),
                      "p90_us": float(np.percentile(per_launch_ms, 90) * 1e3),
+                     "probe_read_gbs": probe_gbs, "frac_of_probe": achieved_gbs / probe_gbs,
                      "mean_selected_per_layer": float(counts.mean())},
         "cpu_baseline": None,
         "kernel_failed": bool(failed),

@@ -95,6 +95,26 @@ int stat_topk(const float *x, int64_t rows, int64_t d, int64_t ldx, int64_t k, f
               int64_t cap, int32_t *counts, float *theta, hipStream_t stream);
 
 /*
+ * Training side of the statistical top-k ("Statistical Top-k" item: with
+ * Huber smoothing the operator is continuously differentiable).  The smoothing
+ * taken: the soft-threshold max{u, 0}, u = x - theta, becomes
+ *     h(u) = 0 (u <= 0),  u^2 / (2 delta) (0 < u < delta),  u - delta/2 (u >= delta),
+ * with theta = mean + std * Q(1 - k/d) (population std) as above.
+ *   forward:  y [rows][d] = h(x - theta) for every entry (dense; zero at and
+ *             below theta); theta [rows] may be NULL.
+ *   backward: dx [rows][d] = dL/dx given dy = dL/dy [rows][d], through theta's
+ *             dependence on the row:  a_i = dy_i h'(x_i - theta),
+ *             A = sum_i a_i,  dx_j = a_j - (A/d) (1 + Q(1 - k/d) (x_j - mean)/std);
+ *             a row with zero spread gets dx = 0.  x is the forward's input.
+ * All arrays fp32 and contiguous (row stride d); any alignment.  Requires
+ * 0 < k < d <= 65536, delta > 0 finite, rows >= 0.  No workspace.
+ */
+int stat_topk_huber_forward(const float *x, int64_t rows, int64_t d, int64_t k, float delta, float *y, float *theta,
+                            hipStream_t stream);
+int stat_topk_huber_backward(const float *x, const float *dy, int64_t rows, int64_t d, int64_t k, float delta,
+                             float *dx, hipStream_t stream);
+
+/*
  * Spark FFN decode ("Spark FFN" item): for each of T independent tokens, run
  * the stack of n_layers Spark FFN layers
  *     y_l = V (GELU(StatTopk(K1^T q_l[:r])) (.) (K2^T q_l[r:]))
@@ -199,6 +219,24 @@ int spark_ffn_decode_batched(const spark_ffn_shape *s, const spark_ffn_weights *
  */
 int spark_ffn_prefill(const spark_ffn_shape *s, const spark_ffn_weights *w, const void *Q, int64_t T, float *Y,
                       const spark_ffn_trace *trace, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The predictor step of spark_ffn_prefill alone: H [T][d_ff] fp32 =
+ * Q[:, :r] K1 (H[t][i] = q_t[:r] . k1t[i]), the dense bf16 product on the
+ * matrix cores.  Same shape and weight requirements as spark_ffn_prefill; no
+ * workspace.  (H is the input spark_ffn_prefill's statistical top-k reads.)
+ */
+int spark_ffn_prefill_scores(const spark_ffn_shape *s, const spark_ffn_weights *w, const void *Q, int64_t T, float *H,
+                             hipStream_t stream);
+
+/*
+ * Measurement helper, not part of the method: streams `bytes` bytes (a
+ * multiple of 16, 16-byte aligned base) from device memory p with 16-byte
+ * nontemporal loads across the whole device and discards them (sink, one
+ * float, is written only for a bit pattern no finite data produces).  Its
+ * rate is the HBM read ceiling the decode kernel's bandwidth is compared to.
+ */
+int spark_hbm_read_probe(const void *p, size_t bytes, float *sink, hipStream_t stream);
 
 /*
  * Spark attention decode ("Spark Attention" item): attention in the form of

@@ -67,6 +67,8 @@ class _Lib:
                                                  vp]
         lib.oracle_spark_attn_prefill.restype = ci
         lib.oracle_spark_attn_prefill.argtypes = [ci, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, vp]
+        lib.oracle_spark_ffn_dense.restype = ci
+        lib.oracle_spark_ffn_dense.argtypes = [i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, i64, vp]
         lib.oracle_huber_relu.restype = d
         lib.oracle_huber_relu.argtypes = [d, d]
         lib.oracle_huber_relu_grad.restype = d
@@ -320,3 +322,21 @@ def stat_topk_huber_backward(x: np.ndarray, dy: np.ndarray, k: int, delta: float
     if rc != 0:
         raise ValueError("oracle_stat_topk_huber_backward: bad arguments")
     return dx
+
+
+def spark_ffn_dense(q: np.ndarray, k1t: np.ndarray, k2t: np.ndarray, v: np.ndarray, r: int, k: int) -> np.ndarray:
+    """The layer computed densely (every neuron's K2 dot and V row, unselected
+    neurons weighted by zero): y [T][d_model] fp64, equal to spark_ffn's y."""
+    q = _c(q)
+    if q.ndim == 1:
+        q = q[None, :]
+    k1t, k2t, v = _c(k1t), _c(k2t), _c(v)
+    T, d_model = q.shape
+    d_ff = v.shape[0]
+    wd = _dtype_code(k1t)
+    y = np.zeros((T, d_model), np.float64)
+    rc = _load().oracle_spark_ffn_dense(d_model, d_ff, int(r), int(k), wd, _ptr(k1t), _ptr(k2t), _ptr(v),
+                                        _dtype_code(q), _ptr(q), T, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_spark_ffn_dense: bad arguments")
+    return y

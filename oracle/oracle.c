@@ -401,6 +401,58 @@ int oracle_spark_ffn(int64_t d_model, int64_t d_ff, int64_t r, int64_t k, int wd
 }
 
 /*
+ * The same layer computed without exploiting its sparsity: the K2 dot and
+ * the V row of EVERY neuron are used, the unselected neurons weighted by
+ * GELU(max{h_i - theta, 0}) = GELU(0) = 0 (the "dense" cost the notes compare
+ * the Spark FFN against).  Summed in ascending neuron order, the exact zeros
+ * leave every sum unchanged, so y equals oracle_spark_ffn's bit for bit.
+ * q [T][d_model] of dtype qdtype; y [T][d_model].
+ */
+int oracle_spark_ffn_dense(int64_t d_model, int64_t d_ff, int64_t r, int64_t k, int wdtype, const void *k1t,
+                           const void *k2t, const void *v, int qdtype, const void *q, int64_t T, double *y)
+{
+    if (!k1t || !k2t || !v || !q || !y || T < 0 || r <= 0 || r >= d_model || k <= 0 || k >= d_ff)
+        return -1;
+    const double z = oracle_threshold_z(k, d_ff);
+    const int64_t rc = d_model - r;
+    double *qd = (double *)malloc(sizeof(double) * (size_t)d_model);
+    double *h = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *c = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t j = 0; j < d_model; ++j)
+            qd[j] = ld(q, qdtype, t * d_model + j);
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < d_ff; ++i) {
+            double s = 0.0;
+            for (int64_t j = 0; j < r; ++j)
+                s += ld(k1t, wdtype, i * r + j) * qd[j];
+            h[i] = s;
+        }
+        double th;
+        stat_topk_row(h, d_ff, z, NULL, NULL, &th, NULL, NULL, 0);
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < d_ff; ++i) {
+            double g = 0.0;
+            for (int64_t j = 0; j < rc; ++j)
+                g += ld(k2t, wdtype, i * rc + j) * qd[r + j];
+            const double m = h[i] > th ? h[i] - th : 0.0;
+            c[i] = oracle_gelu_tanh(m) * g;
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t col = 0; col < d_model; ++col) {
+            double s = 0.0;
+            for (int64_t i = 0; i < d_ff; ++i)
+                s += c[i] * ld(v, wdtype, i * d_model + col);
+            y[t * d_model + col] = s;
+        }
+    }
+    free(qd);
+    free(h);
+    free(c);
+    return 0;
+}
+
+/*
  * A stack of n_layers independent Spark FFN layers applied in sequence to
  * each of T tokens: layer l+1 reads q_{l+1} = y_l / sqrt(mean(y_l^2) + eps)
  * (RMS normalisation with unit gain and no residual).  The returned y is the

@@ -344,6 +344,23 @@ def check_decode_chain():
         assert rel(res["y"][t], y) < 1e-12
 
 
+# ---------------------------------------------------------------- P9b the dense form the bench times
+def check_ffn_dense_form():
+    """The oracle's dense-masked layer (every neuron used, the unselected ones
+    weighted by zero) equals the sparse layer bit for bit (adding exact zeros in
+    the same ascending order changes no fp64 sum), and the numpy dense form."""
+    for (dm, dff, r, k, wd) in ((16, 64, 8, 6, "f32"), (256, 1024, 128, 82, "f32"), (64, 200, 24, 15, "bf16")):
+        lw = synth.ffn_layer(3, 0, dm, dff, r, wd)
+        q = synth.queries(3, 3, dm)
+        dense = oracle.spark_ffn_dense(q, *lw, r, k)
+        sparse = oracle.spark_ffn(q, *lw, r, k)["y"]
+        assert np.array_equal(dense, sparse), (dm, dff)
+        w = [synth.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a for a in lw]
+        for t in range(q.shape[0]):
+            ref, _, _, _ = dense_masked_ffn(q[t], *w, r, k)
+            assert rel(dense[t], ref) < 1e-12
+
+
 # ---------------------------------------------------------------- P15 training side (Huber smoothing)
 def check_huber_function():
     """h(u) against numerical integration of its derivative clamp(t / delta, 0, 1)
@@ -452,5 +469,6 @@ def check_huber_invariances():
 ALL_CHECKS = [check_quantile, check_threshold_closed_form, check_special_rows, check_quantile_grid,
               check_invariants, check_scale_invariance, check_theorem31, check_student_t, check_ffn_dense_masked,
               check_ffn_bf16_widening, check_topk_is_largest, check_activations, check_attention,
-              check_attention_prefill, check_continuity, check_decode_chain, check_huber_function,
+              check_attention_prefill, check_continuity, check_decode_chain, check_ffn_dense_form,
+              check_huber_function,
               check_huber_limit, check_huber_gradient_fd, check_huber_autograd, check_huber_invariances]

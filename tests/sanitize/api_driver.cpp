@@ -30,6 +30,11 @@ hipError_t launch_stat_topk(const float*, int64_t, int64_t, int64_t, double z, f
   ++launches;
   return std::isfinite(z) ? hipSuccess : hipErrorInvalidValue;
 }
+hipError_t launch_stat_topk_huber(bool, const float*, const float*, int64_t, int64_t, double z, float delta, float*,
+                                  float*, hipStream_t) {
+  ++launches;
+  return std::isfinite(z) && delta > 0.f ? hipSuccess : hipErrorInvalidValue;
+}
 size_t decode_workspace_bytes(int64_t d_model, int64_t, int n_layers, int64_t T, int grid) {
   return 4096 + (size_t)grid * 64 + (size_t)d_model * 64 + (n_layers > kDecodeMaxLayersPerLaunch ? 8 * T * d_model : 0);
 }
@@ -57,6 +62,15 @@ hipError_t launch_prefill(const spark_ffn_shape&, const spark_ffn_weights&, cons
                           const spark_ffn_trace*, void*, hipStream_t) {
   ++launches;
   return hipSuccess;
+}
+hipError_t launch_prefill_scores(const spark_ffn_shape&, const spark_ffn_weights&, const void*, int64_t, float*,
+                                 hipStream_t) {
+  ++launches;
+  return hipSuccess;
+}
+hipError_t launch_hbm_read_probe(const void*, size_t bytes, float*, hipStream_t) {
+  ++launches;
+  return bytes % 16 == 0 ? hipSuccess : hipErrorInvalidValue;
 }
 size_t attn_workspace_bytes(int64_t Hq, int64_t, int64_t n_ctx, int64_t hd, int64_t, int64_t) {
   return (size_t)Hq * (n_ctx + hd) * 8;
@@ -109,6 +123,18 @@ int main() {
   EXPECT(stat_topk(x, 4, 10, 10, 10, nullptr, nullptr, 0, counts, nullptr, nullptr) == SPARK_EINVAL);
   EXPECT(stat_topk(x, 4, 70000, 70000, 3, nullptr, nullptr, 0, counts, nullptr, nullptr) == SPARK_EUNSUPPORTED);
   EXPECT(stat_topk(nullptr, 0, 10, 10, 3, nullptr, nullptr, 0, nullptr, nullptr, nullptr) == SPARK_OK);
+
+  // training side
+  n0 = launches;
+  EXPECT(stat_topk_huber_forward(x, 16, 9216, 737, 0.01f, (float*)P, nullptr, nullptr) == SPARK_OK);
+  EXPECT(stat_topk_huber_backward(x, x, 16, 9216, 737, 0.01f, (float*)P, nullptr) == SPARK_OK);
+  EXPECT(launches == n0 + 2);
+  EXPECT(stat_topk_huber_forward(x, 16, 9216, 737, 0.f, (float*)P, nullptr, nullptr) == SPARK_EINVAL);
+  EXPECT(stat_topk_huber_forward(x, 16, 9216, 737, INFINITY, (float*)P, nullptr, nullptr) == SPARK_EINVAL);
+  EXPECT(stat_topk_huber_forward(x, 16, 9216, 9216, 0.1f, (float*)P, nullptr, nullptr) == SPARK_EINVAL);
+  EXPECT(stat_topk_huber_backward(x, nullptr, 16, 9216, 737, 0.1f, (float*)P, nullptr) == SPARK_EINVAL);
+  EXPECT(stat_topk_huber_backward(x, x, 16, 70000, 737, 0.1f, (float*)P, nullptr) == SPARK_EUNSUPPORTED);
+  EXPECT(stat_topk_huber_backward(nullptr, nullptr, 0, 10, 3, 0.1f, nullptr, nullptr) == SPARK_OK);
 
   // decode
   spark_ffn_shape s{2304, 9216, 1152, 737, SPARK_BF16};
@@ -163,6 +189,11 @@ int main() {
   EXPECT(spark_ffn_prefill(&s, layers.data(), P, 4096, (float*)P, nullptr, ws, need, nullptr) == SPARK_OK);
   EXPECT(spark_ffn_prefill(&s, layers.data(), P + 2, 4096, (float*)P, nullptr, ws, need, nullptr) == SPARK_EINVAL);
   EXPECT(spark_ffn_prefill(&s, layers.data(), P, -1, (float*)P, nullptr, ws, need, nullptr) == SPARK_EINVAL);
+
+  EXPECT(spark_ffn_prefill_scores(&s, layers.data(), P, 4096, (float*)P, nullptr) == SPARK_OK);
+  EXPECT(spark_ffn_prefill_scores(&s, layers.data(), P + 4, 4096, (float*)P, nullptr) == SPARK_EINVAL);
+  EXPECT(spark_hbm_read_probe(P, 1 << 20, (float*)P, nullptr) == SPARK_OK);
+  EXPECT(spark_hbm_read_probe(P, 1000, (float*)P, nullptr) == SPARK_EINVAL);
 
   // attention decode and prefill
   EXPECT(spark_attn_workspace_size(8, 4, 32768, 256, 128, 256, &need) == SPARK_OK);
