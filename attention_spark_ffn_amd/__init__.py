@@ -86,6 +86,12 @@ def lib() -> ctypes.CDLL:
                 L.spark_ffn_prefill.restype = _ci
                 L.spark_ffn_prefill.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _vp, _i64, _vp,
                                                 ctypes.POINTER(TraceC), _vp, _sz, _vp]
+                L.spark_ffn_prefill_gathered.restype = _ci
+                L.spark_ffn_prefill_gathered.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _vp,
+                                                         _i64, _vp, ctypes.POINTER(TraceC), _vp, _sz, _vp]
+                L.spark_ffn_prefill_gathered_workspace_size.restype = _ci
+                L.spark_ffn_prefill_gathered_workspace_size.argtypes = [ctypes.POINTER(ShapeC), _i64,
+                                                                        ctypes.POINTER(_sz)]
                 L.spark_ffn_prefill_scores.restype = _ci
                 L.spark_ffn_prefill_scores.argtypes = [ctypes.POINTER(ShapeC), ctypes.POINTER(WeightsC), _vp, _i64,
                                                        _vp, _vp]
@@ -421,10 +427,12 @@ def decode_workspace_failed(ws: torch.Tensor | DecodeWorkspace | None = None, de
 
 
 # ---------------------------------------------------------------------------- prefill
-def spark_ffn_prefill(Q: torch.Tensor, layer, k: int, r: int, trace: bool = False, cap: int | None = None):
+def spark_ffn_prefill(Q: torch.Tensor, layer, k: int, r: int, trace: bool = False, cap: int | None = None,
+                      gathered: bool = False):
     """One Spark FFN layer on T tokens at once.  Q [T][d_model] bf16; layer =
     (k1t, k2t, v) bf16.  Returns Y [T][d_model] fp32 (and with trace=True a dict
-    with counts [T], idx [T][cap], theta [T])."""
+    with counts [T], idx [T][cap], theta [T]).  gathered=True runs
+    spark_ffn_prefill_gathered (only the selected K2 and V rows are read)."""
     _need_cuda(Q, *layer)
     if Q.dim() != 2:
         raise ValueError("Q must be [T][d_model]")
@@ -440,10 +448,10 @@ def spark_ffn_prefill(Q: torch.Tensor, layer, k: int, r: int, trace: bool = Fals
     shape = _shape(d_model, d_ff, r, k, wd)
     w = WeightsC(k1t.data_ptr(), k2t.data_ptr(), v.data_ptr())
     need = ctypes.c_size_t(0)
-    _check(lib().spark_ffn_prefill_workspace_size(ctypes.byref(shape), T, ctypes.byref(need)),
-           "spark_ffn_prefill_workspace_size")
+    size_fn = lib().spark_ffn_prefill_gathered_workspace_size if gathered else lib().spark_ffn_prefill_workspace_size
+    _check(size_fn(ctypes.byref(shape), T, ctypes.byref(need)), "prefill workspace size")
     dev = Q.device
-    ws = _cached_workspace("prefill", dev, need.value)
+    ws = _cached_workspace("prefill_gathered" if gathered else "prefill", dev, need.value)
     Y = torch.empty((T, d_model), dtype=torch.float32, device=dev)
     tr = None
     trc = None
@@ -453,9 +461,10 @@ def spark_ffn_prefill(Q: torch.Tensor, layer, k: int, r: int, trace: bool = Fals
                   idx=torch.full((T, 1, cap), -1, dtype=torch.int32, device=dev),
                   theta=torch.zeros((T, 1), dtype=torch.float32, device=dev))
         trc = TraceC(tr["counts"].data_ptr(), tr["idx"].data_ptr(), tr["theta"].data_ptr(), None, cap)
-    st = lib().spark_ffn_prefill(ctypes.byref(shape), ctypes.byref(w), _p(Q), T, _p(Y),
-                                 ctypes.byref(trc) if trc is not None else None, _p(ws), ws.numel(), _stream(dev))
-    _check(st, "spark_ffn_prefill")
+    fn = lib().spark_ffn_prefill_gathered if gathered else lib().spark_ffn_prefill
+    st = fn(ctypes.byref(shape), ctypes.byref(w), _p(Q), T, _p(Y), ctypes.byref(trc) if trc is not None else None,
+            _p(ws), ws.numel(), _stream(dev))
+    _check(st, "spark_ffn_prefill_gathered" if gathered else "spark_ffn_prefill")
     return (Y, tr) if trace else Y
 
 

@@ -243,6 +243,30 @@ int spark_ffn_prefill(const spark_ffn_shape* s, const spark_ffn_weights* w, cons
   return hip_status(spark::launch_prefill(*s, *w, Q, T, Y, z, trace, ws, stream));
 }
 
+int spark_ffn_prefill_gathered_workspace_size(const spark_ffn_shape* s, int64_t T, size_t* bytes) {
+  size_t dense = 0;
+  const int st = spark_ffn_prefill_workspace_size(s, T, &dense);  // the same shape limits
+  if (st != SPARK_OK) return st;
+  *bytes = spark::prefill_gathered_workspace_bytes(s->d_model, s->d_ff, T);
+  return SPARK_OK;
+}
+
+int spark_ffn_prefill_gathered(const spark_ffn_shape* s, const spark_ffn_weights* w, const void* Q, int64_t T,
+                               float* Y, const spark_ffn_trace* trace, void* ws, size_t ws_bytes, hipStream_t stream) {
+  size_t need = 0;
+  int st = spark_ffn_prefill_gathered_workspace_size(s, T, &need);
+  if (st != SPARK_OK) return st;
+  if (!w) return SPARK_EINVAL;
+  st = check_weights(*w);
+  if (st != SPARK_OK) return st;
+  if (T > 0 && (!Q || !Y || !aligned(Q, 16) || !aligned(Y, 16))) return SPARK_EINVAL;
+  if (trace && trace->idx && trace->cap < 0) return SPARK_EINVAL;
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return SPARK_EWORKSPACE;
+  if (T == 0) return SPARK_OK;
+  const double z = spark_threshold_z(s->k, s->d_ff);
+  return hip_status(spark::launch_prefill_gathered(*s, *w, Q, T, Y, z, trace, ws, stream));
+}
+
 int spark_ffn_prefill_scores(const spark_ffn_shape* s, const spark_ffn_weights* w, const void* Q, int64_t T, float* H,
                              hipStream_t stream) {
   size_t need = 0;

@@ -15,7 +15,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int GBK = 64;       // K per LDS stage
 constexpr int GLD = GBK + 8;  // LDS row length in bf16 (16-byte pad against bank conflicts)
 
-enum { kEpiStore = 0, kEpiGate = 1, kEpiAttn = 2 };
+enum { kEpiStore = 0, kEpiGate = 1, kEpiAttn = 2, kEpiStats = 3 };
 enum { kCausalNone = 0, kCausalTiles = 1, kCausalK = 2 };
 
 // Arguments of one (batched) product D = A * B^T.  Batch z = blockIdx.z uses
@@ -34,7 +34,29 @@ struct GemmArgs {
   const float* r2;
   int64_t sR;
   int causal;
+  f32x4* stats;  // kEpiStats: per (row, wave column tile) {shift, sum, sum of squares}, [M][ceil(N / wave width)]
 };
+
+// Column sums over the 32 lanes of each half-wave of NV per-lane values, all
+// at once (NV = 32): at each step a lane hands half the values it holds to
+// its partner (lane xor m, m = 16, 8, 4, 2, 1) and adds the other half to what
+// it receives; after the five steps lane l holds the full sum of value
+// l mod 32 over its half.
+__device__ __forceinline__ float half_colsum32(float (&v)[32], int lane) {
+#pragma unroll
+  for (int st = 0; st < 5; ++st) {
+    const int m = 16 >> st, h = 16 >> st;
+    const uint32_t upm = (lane & m) ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const uint32_t a = __float_as_uint(v[i]), b = __float_as_uint(v[i + h]);
+      const float give = __uint_as_float((a & upm) | (b & ~upm));
+      const float keep = __uint_as_float((b & upm) | (a & ~upm));
+      v[i] = keep + __shfl_xor(give, m, kWave);
+    }
+  }
+  return v[0];
+}
 
 // D = A[M][K] (bf16, row stride lda) * B^T where B is stored [N][K] (bf16,
 // row stride ldb), with K a multiple of 8 and 16-byte aligned rows, over the
@@ -59,6 +81,12 @@ struct GemmArgs {
 //              n <= m and H > r0[m] (theta, -inf when every token is
 //              attended; r1 the largest selected score, r2 the sum of
 //              e^(s - r1) over the selected), else 0.
+//   kEpiStats: as kEpiStore (no K split), and for every row the sums of
+//              (x - s) and (x - s)^2 over each wave's NI*32 columns, with the
+//              shift s the row's value in the wave's first column (so the
+//              moments keep their precision whatever the row's mean), to
+//              stats[m][tn * WN + wn] = {s, sum, sum of squares}: the per-row
+//              moments of the product in column tiles without reading it back.
 // causal: kCausalTiles skips tiles wholly above the diagonal (n0 > m0 + BM - 1);
 // kCausalK stops K at the end of the tile's rows (A's columns past the
 // diagonal tile are never read).
@@ -246,7 +274,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
       for (int r = 0; r < 16; ++r) {
         const int dm = 8 * (r >> 2) + (r & 3), m = mb + dm;
         const bool in = m < M && n < N;
-        if (EPI == kEpiStore) {
+        if (EPI == kEpiStore || EPI == kEpiStats) {
           if (in) frow[(size_t)dm * ldc] = acc[i][j][r];
         } else if (EPI == kEpiGate) {
           const float gv = gelu_tanh(hv[r] - p0[r]) * acc[i][j][r];
@@ -257,6 +285,48 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_nt(const GemmArgs g) {
               __builtin_amdgcn_exp2f(1.4426950408889634f * (hv[r] - p1[r])) * p2[r] * softplus_fast(acc[i][j][r]);
           const float c = (n <= m && hv[r] > p0[r]) ? gv : 0.f;
           if (in) brow[(size_t)dm * ldc] = f32_to_bf16(c);
+        }
+      }
+    }
+    if constexpr (EPI == kEpiStats) {
+      // register r of lane half hl is row 8 (r / 4) + 4 hl + r % 4 of the block
+      const int nw0 = n0 + wn * NI * 32;
+      const int cnt = min(max(N - nw0, 0), NI * 32);
+      if (cnt > 0) {
+        const int hl = lane >> 5;
+        float v[32], sh[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc[i][0][r]), 0));
+          const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc[i][0][r]), 32));
+          sh[r] = hl ? s1 : s0;
+          float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const float dv = nw0 + j * 32 + (lane & 31) < N ? acc[i][j][r] - sh[r] : 0.f;
+            t1 += dv;
+            t2 += dv * dv;
+          }
+          v[r] = t1;
+          v[16 + r] = t2;
+        }
+        const float tot = half_colsum32(v, lane);
+        // lane l of a half holds value l % 32: the sum of row l % 16 (l % 32 < 16)
+        // or its sum of squares
+        const int c = lane & 31, r = c & 15;
+        const int m = m0 + wm * MI * 32 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (m < M) {
+          const int nparts = (N + NI * 32 - 1) / (NI * 32);
+          float* dst = reinterpret_cast<float*>(g.stats + (size_t)m * nparts + tn * WN + wn);
+          float shr = sh[0];
+#pragma unroll
+          for (int k = 1; k < 16; ++k) shr = r == k ? sh[k] : shr;
+          if (c < 16) {
+            dst[0] = shr;
+            dst[1] = tot;
+          } else {
+            dst[2] = tot;
+          }
         }
       }
     }
@@ -341,6 +411,22 @@ constexpr int kBM = kWM * kMI * 32, kBN = kWN * kNI * 32;
 constexpr int kWM2 = 4, kWN2 = 2, kMI2 = 2, kNI2 = 3;
 constexpr int kBM2 = kWM2 * kMI2 * 32, kBN2 = kWN2 * kNI2 * 32;
 
+// Whether launch_gemm takes the large 256 x 192 tiles for this product.
+template <int EPI>
+inline bool gemm_big_tiles(const GemmArgs& a, int splits, int batch) {
+  if constexpr (EPI == kEpiAttn) return false;
+  int cus = device_cu_count();
+  if (cus < 1) cus = 256;
+  const int64_t big = (int64_t)((a.M + kBM2 - 1) / kBM2) * ((a.N + kBN2 - 1) / kBN2);
+  return batch == 1 && a.causal == kCausalNone && big * splits >= cus;
+}
+
+// Columns each wave of the chosen tile covers (the column tiles of kEpiStats).
+template <int EPI>
+inline int gemm_wave_cols(const GemmArgs& a, int splits, int batch) {
+  return gemm_big_tiles<EPI>(a, splits, batch) ? kNI2 * 32 : kNI * 32;
+}
+
 // Launch over batch `batch` (grid z) and `splits` K splits (grid y).
 template <int EPI>
 inline hipError_t launch_gemm(GemmArgs a, int splits, int batch, hipStream_t st) {
@@ -348,10 +434,8 @@ inline hipError_t launch_gemm(GemmArgs a, int splits, int batch, hipStream_t st)
   a.ksplit = (ks + GBK - 1) / GBK * GBK;
   if (a.bgroup < 1) a.bgroup = 1;
   if constexpr (EPI != kEpiAttn) {
-    int cus = device_cu_count();
-    if (cus < 1) cus = 256;
-    const int64_t big = (int64_t)((a.M + kBM2 - 1) / kBM2) * ((a.N + kBN2 - 1) / kBN2);
-    if (batch == 1 && a.causal == kCausalNone && big * splits >= cus) {
+    if (gemm_big_tiles<EPI>(a, splits, batch)) {
+      const int64_t big = (int64_t)((a.M + kBM2 - 1) / kBM2) * ((a.N + kBN2 - 1) / kBN2);
       const int grid = (int)((big + 7) / 8 * 8);  // a multiple of the XCD count (see gemm_bf16_nt)
       hipLaunchKernelGGL((gemm_bf16_nt<EPI, kWM2, kWN2, kMI2, kNI2>), dim3(grid, splits, 1), dim3(kWM2 * kWN2 * 64),
                          0, st, a);

@@ -10,8 +10,10 @@
 namespace spark {
 
 // ---------------------------------------------------------------- stat_topk
+// theta_in: per-row thresholds to select with (the statistics are then not formed).
 hipError_t launch_stat_topk(const float* x, int64_t rows, int64_t d, int64_t ldx, double z, float* vals, int32_t* idx,
-                            int64_t cap, int32_t* counts, float* theta, hipStream_t st);
+                            int64_t cap, int32_t* counts, float* theta, hipStream_t st,
+                            const float* theta_in = nullptr);
 
 // ---------------------------------------------------------------- training side (Huber-smoothed stat top-k)
 // backward = false: out = y (theta may be null); backward = true: out = dx from dy.
@@ -52,6 +54,9 @@ hipError_t launch_decode_batched(const spark_ffn_shape& s, const spark_ffn_weigh
 size_t prefill_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t T);
 hipError_t launch_prefill(const spark_ffn_shape& s, const spark_ffn_weights& w, const void* Q, int64_t T, float* Y,
                           double z, const spark_ffn_trace* trace, void* ws, hipStream_t st);
+size_t prefill_gathered_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t T);
+hipError_t launch_prefill_gathered(const spark_ffn_shape& s, const spark_ffn_weights& w, const void* Q, int64_t T,
+                                   float* Y, double z, const spark_ffn_trace* trace, void* ws, hipStream_t st);
 hipError_t launch_prefill_scores(const spark_ffn_shape& s, const spark_ffn_weights& w, const void* Q, int64_t T,
                                  float* H, hipStream_t st);
 hipError_t launch_hbm_read_probe(const void* p, size_t bytes, float* sink, hipStream_t st);

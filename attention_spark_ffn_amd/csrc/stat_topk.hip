@@ -34,26 +34,17 @@ struct StatShared {
   float s_val[kStage];
 };
 
-// Statistics, threshold and list of one row held in registers.
+// theta = mean + std * z of one row held in registers: two exact passes (the
+// mean, then the squared deviations about it; entries past the row end are 0
+// and left out of the second), each reduced with DPP wave sums and then the
+// waves in a fixed order.
 template <int NT, int E, bool EXACT>
-__device__ __forceinline__ void process_row(const float (&v)[E][4], int64_t row, int d, int tid, float z,
-                                            float* __restrict__ vals, int32_t* __restrict__ idx, int64_t cap,
-                                            int32_t* __restrict__ counts, float* __restrict__ theta_out,
-                                            StatShared<NT / kWave, E>& S) {
-  constexpr int NW = NT / kWave;
-  const int lane = tid & (kWave - 1), wv = tid / kWave;
-  // pass 1: mean (entries past the row end are 0)
+__device__ __forceinline__ float row_theta(const float (&v)[E][4], int d, int tid, float z, float* red0,
+                                           float* red1) {
   float s = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) s += (v[e][0] + v[e][1]) + (v[e][2] + v[e][3]);
-  s = wave_sum_dpp(s);
-  if (lane == 0) S.red[0][wv] = s;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) tot += S.red[0][w];
-  const float mean = tot / (float)d;
-  // pass 2: sum of squared deviations about the mean
+  const float mean = block_sum<NT / kWave>(s, red0) / (float)d;
   float q = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e)
@@ -62,13 +53,20 @@ __device__ __forceinline__ void process_row(const float (&v)[E][4], int64_t row,
       const float dv = v[e][j] - mean;
       q += (EXACT || 4 * tid + 4 * NT * e + j < d) ? dv * dv : 0.f;
     }
-  q = wave_sum_dpp(q);
-  if (lane == 0) S.red[1][wv] = q;
-  __syncthreads();
-  float m2 = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) m2 += S.red[1][w];
-  const float theta = mean + sqrtf(m2 / (float)d) * z;
+  const float m2 = block_sum<NT / kWave>(q, red1);
+  return mean + sqrtf(m2 / (float)d) * z;
+}
+
+// Statistics, threshold and list of one row held in registers.  theta_in:
+// the rows' thresholds when given (the statistics are then not formed).
+template <int NT, int E, bool EXACT>
+__device__ __forceinline__ void process_row(const float (&v)[E][4], int64_t row, int d, int tid, float z,
+                                            float* __restrict__ vals, int32_t* __restrict__ idx, int64_t cap,
+                                            int32_t* __restrict__ counts, float* __restrict__ theta_out,
+                                            const float* __restrict__ theta_in, StatShared<NT / kWave, E>& S) {
+  constexpr int NW = NT / kWave;
+  const int lane = tid & (kWave - 1), wv = tid / kWave;
+  const float theta = theta_in ? theta_in[row] : row_theta<NT, E, EXACT>(v, d, tid, z, S.red[0], S.red[1]);
 
   // survivors of chunk e as a 4-bit mask per lane.  Pass A publishes each
   // (wave, chunk) total; pass B forms the masks and their in-wave prefix scans
@@ -133,6 +131,10 @@ __device__ __forceinline__ void process_row(const float (&v)[E][4], int64_t row,
       if (idx) __builtin_nontemporal_store(S.s_idx[i], idx + row * cap + i);
       if (vals) __builtin_nontemporal_store(S.s_val[i], vals + row * cap + i);
     }
+  } else if (theta_in) {
+    // no statistics barriers precede the next row's counts: wait here until
+    // every wave has read this row's
+    __syncthreads();
   }
 }
 
@@ -141,7 +143,7 @@ template <int NT, int E, bool VEC, bool EXACT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 && E <= 9 ? 4 : 1)))
 void stat_topk_kernel(const float* __restrict__ x, int64_t rows, int d_arg, int64_t ldx, float z,
                       float* __restrict__ vals, int32_t* __restrict__ idx, int64_t cap, int32_t* __restrict__ counts,
-                      float* __restrict__ theta_out) {
+                      float* __restrict__ theta_out, const float* __restrict__ theta_in) {
   __shared__ StatShared<NT / kWave, E> S;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     // Opaque copies of the thread index and the row length: the element
@@ -151,45 +153,46 @@ void stat_topk_kernel(const float* __restrict__ x, int64_t rows, int d_arg, int6
     asm volatile("" : "+v"(tid), "+s"(d));
     float v[E][4];
     load_row<NT, E, VEC, EXACT>(x + row * ldx, d, tid, v);
-    process_row<NT, E, EXACT>(v, row, d, tid, z, vals, idx, cap, counts, theta_out, S);
+    process_row<NT, E, EXACT>(v, row, d, tid, z, vals, idx, cap, counts, theta_out, theta_in, S);
   }
 }
 
 template <int NT, int E>
 static hipError_t launch_e(bool vec, const float* x, int64_t rows, int d, int64_t ldx, float z, float* vals,
-                           int32_t* idx, int64_t cap, int32_t* counts, float* theta, hipStream_t st) {
+                           int32_t* idx, int64_t cap, int32_t* counts, float* theta, const float* theta_in,
+                           hipStream_t st) {
   const int64_t grid = rows < (1 << 30) ? rows : (1 << 30);
   const dim3 g((unsigned)grid), b(NT);
   if (vec && d == 4 * NT * E)
     hipLaunchKernelGGL((stat_topk_kernel<NT, E, true, true>), g, b, 0, st, x, rows, d, ldx, z, vals, idx, cap, counts,
-                       theta);
+                       theta, theta_in);
   else if (vec)
     hipLaunchKernelGGL((stat_topk_kernel<NT, E, true, false>), g, b, 0, st, x, rows, d, ldx, z, vals, idx, cap,
-                       counts, theta);
+                       counts, theta, theta_in);
   else
     hipLaunchKernelGGL((stat_topk_kernel<NT, E, false, false>), g, b, 0, st, x, rows, d, ldx, z, vals, idx, cap,
-                       counts, theta);
+                       counts, theta, theta_in);
   return hipGetLastError();
 }
 
 hipError_t launch_stat_topk(const float* x, int64_t rows, int64_t d, int64_t ldx, double z, float* vals, int32_t* idx,
-                            int64_t cap, int32_t* counts, float* theta, hipStream_t st) {
+                            int64_t cap, int32_t* counts, float* theta, hipStream_t st, const float* theta_in) {
   if (rows == 0) return hipSuccess;
   const bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 4 == 0);
   const float zf = (float)z;
   const int di = (int)d;
   // rows up to 16384 elements: 256 threads (several rows resident per CU);
   // longer rows: 1024 threads.
-  if (d <= 1024) return launch_e<256, 1>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, st);
-  if (d <= 2048) return launch_e<256, 2>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, st);
-  if (d <= 4096) return launch_e<256, 4>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, st);
-  if (d <= 6144) return launch_e<256, 6>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, st);
-  if (d <= 8192) return launch_e<256, 8>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, st);
-  if (d <= 9216) return launch_e<256, 9>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, st);
-  if (d <= 12288) return launch_e<256, 12>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, st);
-  if (d <= 16384) return launch_e<256, 16>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, st);
-  if (d <= 32768) return launch_e<1024, 8>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, st);
-  return launch_e<1024, 16>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, st);
+  if (d <= 1024) return launch_e<256, 1>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, theta_in, st);
+  if (d <= 2048) return launch_e<256, 2>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, theta_in, st);
+  if (d <= 4096) return launch_e<256, 4>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, theta_in, st);
+  if (d <= 6144) return launch_e<256, 6>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, theta_in, st);
+  if (d <= 8192) return launch_e<256, 8>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, theta_in, st);
+  if (d <= 9216) return launch_e<256, 9>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, theta_in, st);
+  if (d <= 12288) return launch_e<256, 12>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, theta_in, st);
+  if (d <= 16384) return launch_e<256, 16>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, theta_in, st);
+  if (d <= 32768) return launch_e<1024, 8>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, theta_in, st);
+  return launch_e<1024, 16>(vec, x, rows, di, ldx, zf, vals, idx, cap, counts, theta, theta_in, st);
 }
 
 }  // namespace spark

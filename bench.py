@@ -232,6 +232,8 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
     # the method's own work: the dense predictor product, and per token the
     # selected neurons' K2 dots and V rows
     method = flops + 2.0 * nsel * ((D_MODEL - R) + D_MODEL)
+    # the gathered form (only the selected K2 and V rows read, per token)
+    gath_ms = _time_ms(torch, lambda: sf.spark_ffn_prefill(Q, layer, K, R, gathered=True), reps=5)
     # the predictor product alone (its own entry point), HIP events
     pred_ms = _time_ms(torch, lambda: sf.spark_ffn_prefill_scores(Q, layer, R), reps=50)
     Qr = Q[:, :R].contiguous()
@@ -252,6 +254,9 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
                                          "roofline": {"bound": "mfma", "achieved": flops / pred_ms / 1e9,
                                                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                                       "frac": flops / pred_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}},
+                      "gathered": {"ms": gath_ms, "achieved_tflops": method / gath_ms / 1e9,
+                                   "gathered_row_bytes": nsel * ((D_MODEL - R) * 2 + D_MODEL * 2),
+                                   "note": "spark_ffn_prefill_gathered: per token only the selected K2 and V rows"},
                       "hipblaslt_predictor_gemm_ms": ref_ms,
                       "hipblaslt_predictor_tflops": flops / ref_ms / 1e9}
     if with_cpu:

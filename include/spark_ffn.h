@@ -221,6 +221,25 @@ int spark_ffn_prefill(const spark_ffn_shape *s, const spark_ffn_weights *w, cons
                       const spark_ffn_trace *trace, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * spark_ffn_prefill with the K2 and V steps exactly as the "Spark FFN" item
+ * states them: after the same dense predictor product and statistical top-k,
+ * each token reads only its selected neurons' K2 rows (k2t) and V rows, the
+ * gated values in fp32 and the V rows summed in ascending neuron order.
+ * The same arguments, requirements and results as spark_ffn_prefill (up to
+ * the rounding of the gated values, which that call feeds to the matrix
+ * cores as bf16); Y must also be 16-byte aligned.  With i.i.d. selections the
+ * dense products on the matrix cores are faster (each token's rows are
+ * gathered from memory separately); this is the gathered form for
+ * comparison and for selections that are sparser or clustered.  The
+ * workspace (spark_ffn_prefill_gathered_workspace_size) holds the scores and
+ * every token's full list: about 12 T d_ff bytes.
+ */
+int spark_ffn_prefill_gathered(const spark_ffn_shape *s, const spark_ffn_weights *w, const void *Q, int64_t T,
+                               float *Y, const spark_ffn_trace *trace, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
+int spark_ffn_prefill_gathered_workspace_size(const spark_ffn_shape *s, int64_t T, size_t *bytes);
+
+/*
  * The predictor step of spark_ffn_prefill alone: H [T][d_ff] fp32 =
  * Q[:, :r] K1 (H[t][i] = q_t[:r] . k1t[i]), the dense bf16 product on the
  * matrix cores.  Same shape and weight requirements as spark_ffn_prefill; no

@@ -26,7 +26,7 @@ static int launches = 0;
 
 namespace spark {
 hipError_t launch_stat_topk(const float*, int64_t, int64_t, int64_t, double z, float*, int32_t*, int64_t, int32_t*,
-                            float*, hipStream_t) {
+                            float*, hipStream_t, const float*) {
   ++launches;
   return std::isfinite(z) ? hipSuccess : hipErrorInvalidValue;
 }
@@ -60,6 +60,12 @@ hipError_t launch_decode_batched(const spark_ffn_shape&, const spark_ffn_weights
 size_t prefill_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t T) { return (size_t)(d_model + d_ff) * T * 8; }
 hipError_t launch_prefill(const spark_ffn_shape&, const spark_ffn_weights&, const void*, int64_t, float*, double,
                           const spark_ffn_trace*, void*, hipStream_t) {
+  ++launches;
+  return hipSuccess;
+}
+size_t prefill_gathered_workspace_bytes(int64_t, int64_t d_ff, int64_t T) { return (size_t)d_ff * T * 12 + 4096; }
+hipError_t launch_prefill_gathered(const spark_ffn_shape&, const spark_ffn_weights&, const void*, int64_t, float*,
+                                   double, const spark_ffn_trace*, void*, hipStream_t) {
   ++launches;
   return hipSuccess;
 }
@@ -190,6 +196,12 @@ int main() {
   EXPECT(spark_ffn_prefill(&s, layers.data(), P + 2, 4096, (float*)P, nullptr, ws, need, nullptr) == SPARK_EINVAL);
   EXPECT(spark_ffn_prefill(&s, layers.data(), P, -1, (float*)P, nullptr, ws, need, nullptr) == SPARK_EINVAL);
 
+  EXPECT(spark_ffn_prefill_gathered_workspace_size(&s, 4096, &need) == SPARK_OK && need > 0);
+  EXPECT(spark_ffn_prefill_gathered(&s, layers.data(), P, 4096, (float*)P, nullptr, ws, need, nullptr) == SPARK_OK);
+  EXPECT(spark_ffn_prefill_gathered(&s, layers.data(), P, 4096, (float*)(P + 4), nullptr, ws, need, nullptr) ==
+         SPARK_EINVAL);
+  EXPECT(spark_ffn_prefill_gathered(&s, layers.data(), P, 4096, (float*)P, nullptr, ws, need / 2, nullptr) ==
+         SPARK_EWORKSPACE);
   EXPECT(spark_ffn_prefill_scores(&s, layers.data(), P, 4096, (float*)P, nullptr) == SPARK_OK);
   EXPECT(spark_ffn_prefill_scores(&s, layers.data(), P + 4, 4096, (float*)P, nullptr) == SPARK_EINVAL);
   EXPECT(spark_hbm_read_probe(P, 1 << 20, (float*)P, nullptr) == SPARK_OK);

@@ -16,10 +16,10 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
 
 
-def run_prefill(dm, dff, r, k, T, seed, sample=None, tol=2e-2):
+def run_prefill(dm, dff, r, k, T, seed, sample=None, tol=2e-2, gathered=False):
     layer = synth.ffn_layer(seed, 0, dm, dff, r, "bf16")
     Q = synth.queries(seed, T, dm, "bf16")
-    Y, tr = sf.spark_ffn_prefill(to_dev(Q), tuple(to_dev(a) for a in layer), k, r, trace=True)
+    Y, tr = sf.spark_ffn_prefill(to_dev(Q), tuple(to_dev(a) for a in layer), k, r, trace=True, gathered=gathered)
     torch.cuda.synchronize()
     Y = Y.cpu().numpy()
     tr = {key: v.cpu().numpy() for key, v in tr.items()}
@@ -84,6 +84,21 @@ def test_prefill_deterministic():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("T", [4096, 300])
+def test_prefill_traced_and_untraced_agree(T):
+    """The timed call (no trace) and the traced call select with the same
+    thresholds, so their outputs are identical; the trace's counts are those of
+    its lists."""
+    layer = [to_dev(a) for a in synth.ffn_layer(4, 0, 2304, 9216, 1152, "bf16")]
+    Q = to_dev(synth.queries(4, T, 2304, "bf16"))
+    a = sf.spark_ffn_prefill(Q, layer, 737, 1152)
+    b, tr = sf.spark_ffn_prefill(Q, layer, 737, 1152, trace=True)
+    c, tr2 = sf.spark_ffn_prefill(Q, layer, 737, 1152, trace=True, cap=1)
+    assert torch.equal(a, b) and torch.equal(a, c)
+    assert torch.equal(tr["counts"], tr2["counts"]) and torch.equal(tr["theta"], tr2["theta"])
+    assert torch.equal((tr["idx"][:, 0] >= 0).sum(1).int(), tr["counts"][:, 0])
+
+
 def test_prefill_matches_decode_per_token():
     # the same layer through the prefill path and the decode path (bf16 q)
     dm, dff, r, k = 512, 1024, 256, 80
@@ -98,3 +113,38 @@ def test_prefill_matches_decode_per_token():
     # errors of the ~80 terms add at random, far inside 2^-8 of the norm.
     for t in range(16):
         assert rel_err(Y[t], Yd[t]) <= 2.0 ** -8
+
+
+# ---------------------------------------------------------------- the gathered form
+def test_prefill_gathered_config():
+    """spark_ffn_prefill_gathered on the prefill workload (4096 tokens, 2304 x
+    9216, r 1152, k 737): 96 sampled tokens against the oracle."""
+    T = 4096
+    sample = np.sort(np.random.default_rng(1).choice(T, 96, replace=False))
+    run_prefill(2304, 9216, 1152, 737, T, 0, sample, gathered=True)
+
+
+@pytest.mark.parametrize("dm,dff,r,k,T", [
+    (256, 1024, 128, 82, 300),
+    (136, 256, 64, 20, 1),
+    (512, 4096, 256, 330, 700),
+])
+def test_prefill_gathered_shapes(dm, dff, r, k, T):
+    run_prefill(dm, dff, r, k, T, dm + T + 1, gathered=True)
+
+
+def test_prefill_gathered_matches_dense_and_is_deterministic():
+    """The gathered and the dense forms select with the same thresholds (the
+    same scores and statistics), so their lists are identical; their outputs
+    differ only by the dense form's bf16 rounding of the gated values."""
+    layer = [to_dev(a) for a in synth.ffn_layer(9, 0, 2304, 9216, 1152, "bf16")]
+    Q = to_dev(synth.queries(9, 1000, 2304, "bf16"))
+    yd, trd = sf.spark_ffn_prefill(Q, layer, 737, 1152, trace=True)
+    yg, trg = sf.spark_ffn_prefill(Q, layer, 737, 1152, trace=True, gathered=True)
+    yg2 = sf.spark_ffn_prefill(Q, layer, 737, 1152, gathered=True)
+    torch.cuda.synchronize()
+    assert torch.equal(trd["idx"], trg["idx"]) and torch.equal(trd["counts"], trg["counts"])
+    assert torch.equal(yg, yg2)
+    yd, yg = yd.cpu().numpy(), yg.cpu().numpy()
+    for t in range(0, 1000, 7):
+        assert rel_err(yd[t], yg[t]) <= 2.0 ** -8, t
