@@ -252,12 +252,13 @@ def _cached_workspace(kind: str, device, nbytes: int) -> torch.Tensor:
     return ws
 
 
-class DecodeWorkspace:
-    """A decode workspace with its host-side bookkeeping: the exchange tags the
-    calls on it have used since it was last zeroed (it is zeroed again, on its
-    stream, before they would pass 2^32 - 1), and the failed-call count the
-    host last saw (the kernel counts failed calls in the 8-byte word at byte
-    offset 16)."""
+class TaggedWorkspace:
+    """A workspace whose kernels exchange tagged words between workgroups
+    (the decode kernel), with its host-side bookkeeping: the exchange
+    tags the calls on it have used since it was last zeroed (it is zeroed
+    again, on its stream, before they would pass 2^32 - 1), and the
+    failed-call count the host last saw (the kernels count failed calls in the
+    8-byte word at byte offset 16)."""
 
     def __init__(self, buf: torch.Tensor):
         self.buf = buf
@@ -289,13 +290,20 @@ def decode_tags(n_layers: int, T: int) -> int:
     return int(lib().spark_ffn_decode_tags(int(n_layers), int(T)))
 
 
-def _decode_workspace(device, nbytes: int) -> DecodeWorkspace:
-    key = _ws_key("decode", device)
+DecodeWorkspace = TaggedWorkspace
+
+
+def _tagged_workspace(kind: str, device, nbytes: int) -> TaggedWorkspace:
+    key = _ws_key(kind, device)
     dw = _ws_cache.get(key)
     if dw is None or dw.buf.numel() < nbytes:
-        dw = DecodeWorkspace(torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device))
+        dw = TaggedWorkspace(torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device))
         _ws_cache[key] = dw
     return dw
+
+
+def _decode_workspace(device, nbytes: int) -> TaggedWorkspace:
+    return _tagged_workspace("decode", device, nbytes)
 
 
 # ---------------------------------------------------------------------------- decode

@@ -274,7 +274,7 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
         # the operator alone through the C ABI: outputs preallocated, no list
         need = ctypes.c_size_t(0)
         L.spark_attn_workspace_size(8, 4, n, 256, 128, 256, ctypes.byref(need))
-        ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+        ws = torch.zeros(need.value, dtype=torch.uint8, device=dev)  # zero-filled before its first use
         o2 = torch.empty((8, 256), device=dev)
         c2 = torch.empty(8, dtype=torch.int32, device=dev)
         call = lambda: L.spark_attn_decode(*[sf._p(a) for a in args], 8, 4, n, 256, 128, 256, sf._p(o2), sf._p(c2),

@@ -273,6 +273,9 @@ int spark_hbm_read_probe(const void *p, size_t bytes, float *sink, hipStream_t s
  *   NULL; NaN when all tokens are attended).
  * Requires Hq % Hkv == 0, hd <= 512, 0 < r < hd, r and hd - r multiples of 8,
  * 1 <= n_ctx <= 1048576, k_attn >= 1.
+ * Three launches on `stream` (scores and chunk statistics; per chunk the
+ * selection, gates and a split-softmax partial; the merge).  The workspace
+ * needs no initialisation.
  */
 int spark_attn_decode(const void *q, const void *k1, const void *k2, const void *v, int64_t Hq, int64_t Hkv,
                       int64_t n_ctx, int64_t hd, int64_t r, int64_t k_attn, float *out, int32_t *counts,

@@ -66,3 +66,19 @@ def test_attn_deterministic():
     b = sf.spark_attn_decode(*args, 256)
     for u, w in zip(a, b):
         assert torch.equal(u, w)
+
+
+@pytest.mark.parametrize("Hq,Hkv,n,hd,r,ka", [
+    (16, 1, 3000, 128, 64, 200),     # 16 query heads per KV head (two register groups of 8)
+    (2, 1, 150000, 64, 32, 256),     # 586 chunks of 256 tokens
+])
+def test_attn_wide_groups_and_long_context(Hq, Hkv, n, hd, r, ka):
+    run_attn(Hq, Hkv, n, hd, r, ka, n + Hq, scale=0.5)
+
+
+def test_attn_repeated_calls():
+    """Many calls in a row on changing inputs and one cached workspace: each
+    matches the oracle's result for its own inputs."""
+    for i in range(6):
+        n = 4096 if i % 2 == 0 else 1500
+        run_attn(8, 4, n, 256, 128, 256, 100 + i)
