@@ -1,4 +1,4 @@
-// Spark FFN decode: a persistent, cooperative kernel that runs the whole stack of
+// Spark FFN decode: a persistent kernel that runs the whole stack of
 // layers for each token without returning to the host.
 //
 // Method (Spark Transformer reading notes, section "方法详解 / 关键设计", item
@@ -972,7 +972,9 @@ static hipError_t launch_decode_t(const spark_ffn_shape& s, const spark_ffn_weig
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<W>, kDecodeThreads, 0);
   if (e != hipSuccess) return e;
-  if ((int64_t)per_cu * device_cu_count() < grid) return hipErrorCooperativeLaunchTooLarge;
+  // the workgroups exchange data while they run, so the device must hold the
+  // whole grid at once (one workgroup per compute unit)
+  if ((int64_t)per_cu * device_cu_count() < grid) return hipErrorLaunchOutOfResources;
   const DecodeLayout Lo = decode_layout(s.d_model, T, grid, n_layers);
   char* base = (char*)ws;
   float* qbuf[2] = {(float*)(base + Lo.qbuf), (float*)(base + Lo.qbuf + round_up((size_t)T * s.d_model * 4, 256))};
@@ -1013,7 +1015,12 @@ static hipError_t launch_decode_t(const spark_ffn_shape& s, const spark_ffn_weig
     p.ycol_stride = Lo.ycol_stride;
     p.spin_limit = 1u << 22;
     void* args[] = {&p};
-    e = hipLaunchCooperativeKernel((const void*)decode_kernel<W>, dim3(grid), dim3(kDecodeThreads), args, 0, st);
+    // An ordinary launch: on a device that holds the grid every workgroup
+    // starts at once (the cooperative launch API guarantees the same thing but
+    // costs ~16-20 us more per call here).  Were other work to keep some
+    // workgroups from starting, the bounded waits would end the call as a
+    // recorded failure, never a hang.
+    e = hipLaunchKernel((const void*)decode_kernel<W>, dim3(grid), dim3(kDecodeThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -130,8 +130,11 @@ int stat_topk_huber_backward(const float *x, const float *dy, int64_t rows, int6
  * k1t, k2t and v base pointers 16-byte aligned, and r and d_model - r
  * multiples of 8 elements (bf16) or 4 elements (fp32), so that every weight
  * row is whole 16-byte chunks; SPARK_EINVAL otherwise.
- * The kernel is a cooperative (co-resident) grid; it returns SPARK_EHIP if the
- * device cannot host it.
+ * The kernel is one persistent grid of one workgroup per compute unit whose
+ * workgroups exchange data while they run, so the device must hold the whole
+ * grid at once: SPARK_EHIP if it cannot.  Other work running on the device
+ * at the same time can delay workgroups; a call whose waits then time out
+ * fails as described below (it does not hang).
  * Workspace: zero-filled before its first use, then kept between calls: it
  * carries the 32-bit tags of the grid-wide exchanges from call to call, and a
  * call uses spark_ffn_decode_tags(n_layers, T) of them.  Zero the workspace
