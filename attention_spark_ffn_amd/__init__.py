@@ -402,23 +402,37 @@ def spark_ffn_decode_noalloc(q: torch.Tensor, layers, k: int, r: int, eps: float
 
 
 def spark_ffn_decode_batched(q: torch.Tensor, layers, k: int, r: int, eps: float = 1e-6, trace: bool = False,
-                             cap: int | None = None):
+                             cap: int | None = None, ws: torch.Tensor | TaggedWorkspace | None = None,
+                             check: bool = True):
     """The computation of spark_ffn_decode for a batch of B <= 8 tokens, run
     layer by layer for the whole batch (one K1 read per layer, K2 and V rows
     read once for all the tokens that select them).  Same arguments, results
-    and trace as spark_ffn_decode with T = B."""
+    and trace as spark_ffn_decode with T = B.  ws: optional workspace to use
+    (and carry) instead of the cached one of this device and stream (a
+    TaggedWorkspace or a zero-filled uint8 tensor).  check: synchronise and
+    raise if a grid-wide exchange timed out."""
     B, d_model, L, d_ff, shape, wts = _stack_args(q, layers, k, r)
     need = ctypes.c_size_t(0)
     _check(lib().spark_ffn_decode_batched_workspace_size(ctypes.byref(shape), B, ctypes.byref(need)),
            "spark_ffn_decode_batched_workspace_size")
     dev = q.device
-    ws = _cached_workspace("decode_batched", dev, need.value)
+    if ws is None:
+        ws = _tagged_workspace("decode_batched", dev, need.value)
+    elif isinstance(ws, torch.Tensor):
+        ws = TaggedWorkspace(ws)
+    # a batched call uses the exchange tags of one single-token call
+    if ws.reserve(decode_tags(L, 1)):
+        ws.buf.zero_()
+        ws.failures_seen = 0
     y = torch.empty((B, d_model), dtype=torch.float32, device=dev)
     tr, trc = _trace_buffers(B, L, d_ff, d_model, cap, dev) if trace else (None, None)
     st = lib().spark_ffn_decode_batched(ctypes.byref(shape), wts, L, _p(q), B, _p(y), float(eps),
-                                        ctypes.byref(trc) if trc is not None else None, _p(ws), ws.numel(),
+                                        ctypes.byref(trc) if trc is not None else None, _p(ws.buf), ws.buf.numel(),
                                         _stream(dev))
     _check(st, "spark_ffn_decode_batched")
+    if check and ws.new_failures():
+        raise RuntimeError("spark_ffn_decode_batched: a grid-wide exchange timed out (the device could not keep "
+                           "the whole grid running); the output holds NaN")
     return (y, tr) if trace else y
 
 

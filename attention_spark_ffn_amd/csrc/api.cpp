@@ -3,6 +3,7 @@
 // the first device call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -55,6 +56,10 @@ int check_weights(const spark_ffn_weights& w) {
   if (!aligned(w.k1t, 16) || !aligned(w.k2t, 16) || !aligned(w.v, 16)) return SPARK_EINVAL;
   return SPARK_OK;
 }
+
+// Bytes at the start of a batched-decode workspace kept for the header of the
+// single-token persistent kernel (exchange tags, failure mark and count).
+constexpr size_t kBatchedHeader = 256;
 
 int decode_limits(const spark_ffn_shape* s) {
   if (s->d_model > spark::kDecodeMaxDModel || s->d_ff > 65536) return SPARK_EUNSUPPORTED;
@@ -192,7 +197,14 @@ int spark_ffn_decode_batched_workspace_size(const spark_ffn_shape* s, int64_t B,
   const int64_t wide = s->r > s->d_model - s->r ? s->r : s->d_model - s->r;
   const int64_t slots = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8;  // token slots of the kernels
   if (slots * wide * 4 > spark::kBatchMaxLds) return SPARK_EUNSUPPORTED;
-  *bytes = spark::decode_batched_workspace_bytes(s->d_model, s->d_ff, B > 0 ? B : 1);
+  // room for either form a call may take: the header of the single-token
+  // persistent kernel, then the layer-by-layer kernels' buffers; or that
+  // kernel's own layout (B = 1)
+  size_t need = kBatchedHeader + spark::decode_batched_workspace_bytes(s->d_model, s->d_ff, B > 0 ? B : 1);
+  if (decode_limits(s) == SPARK_OK)
+    need = std::max(need, spark::decode_workspace_bytes(s->d_model, s->d_ff, spark::kDecodeMaxLayersPerLaunch + 1, 1,
+                                                        spark::decode_grid(s->d_ff)));
+  *bytes = need;
   return SPARK_OK;
 }
 
@@ -210,9 +222,15 @@ int spark_ffn_decode_batched(const spark_ffn_shape* s, const spark_ffn_weights* 
   if (B > 0 && (!q || !y || !aligned(q, 16) || !aligned(y, 16))) return SPARK_EINVAL;
   if (trace && trace->idx && trace->cap < 0) return SPARK_EINVAL;
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return SPARK_EWORKSPACE;
+  if ((int64_t)n_layers * 3 >= (int64_t)1 << 31) return SPARK_EUNSUPPORTED;
   if (B == 0) return SPARK_OK;
   const double z = spark_threshold_z(s->k, s->d_ff);
-  return hip_status(spark::launch_decode_batched(*s, layers, n_layers, q, B, y, rms_eps, z, trace, ws, stream));
+  // one token: the single-token persistent kernel; more: the layer-by-layer
+  // kernels (after the header the persistent kernel keeps)
+  if (B == 1 && decode_limits(s) == SPARK_OK)
+    return hip_status(spark::launch_decode(*s, layers, n_layers, q, 1, y, rms_eps, z, trace, ws, stream));
+  return hip_status(spark::launch_decode_batched(*s, layers, n_layers, q, B, y, rms_eps, z, trace,
+                                                 (char*)ws + kBatchedHeader, stream));
 }
 
 int spark_ffn_prefill_workspace_size(const spark_ffn_shape* s, int64_t T, size_t* bytes) {

@@ -143,17 +143,23 @@ def _oracle_rate(fn, n_units: int, unit: str, sample: str) -> dict:
 def batched_decode(torch, sf, layers, qs):
     """The same 26-layer stack decoded B tokens at a time (one K1 read per
     layer for the batch; K2 and V rows read once per union of the selected
-    sets), for B in 1, 4, 8.  Algorithmic bytes per call: per layer K1, the
+    sets), for B in 1, 2, 4, 8.  Algorithmic bytes per call: per layer K1, the
     union's K2 and V rows, the fp32 input and output vectors of the batch."""
     res = {}
-    for B in (1, 4, 8):
+    for B in (1, 2, 4, 8):
         q = qs[:B].contiguous()
-        ms = _time_ms(torch, lambda: sf.spark_ffn_decode_batched(q, layers, K, R), reps=20)
+        ms = _time_ms(torch, lambda: sf.spark_ffn_decode_batched(q, layers, K, R, check=False), reps=20)
+        # 20 calls back to back in one timed region (the launch of one call
+        # overlaps the end of the previous one)
+        ms20 = _time_ms(torch, lambda: [sf.spark_ffn_decode_batched(q, layers, K, R, check=False)
+                                        for _ in range(20)], reps=3, warm=1) / 20
         _, tr = sf.spark_ffn_decode_batched(q, layers, K, R, trace=True)
         idx, cnt = tr["idx"].cpu().numpy(), tr["counts"].cpu().numpy()
         union = [len(set().union(*[set(idx[b, l, :cnt[b, l]].tolist()) for b in range(B)])) for l in range(LAYERS)]
         moved = sum(R * D_FF * 2 + u * ((D_MODEL - R) * 2 + D_MODEL * 2) + 2 * B * D_MODEL * 4 for u in union)
-        res[str(B)] = {"ms_per_call": ms, "tokens_per_s": B / ms * 1e3, "mean_union_per_layer": float(np.mean(union)),
+        res[str(B)] = {"ms_per_call": ms, "tokens_per_s": B / ms * 1e3,
+                       "ms_per_call_back_to_back": ms20, "tokens_per_s_back_to_back": B / ms20 * 1e3,
+                       "mean_union_per_layer": float(np.mean(union)),
                        "algorithmic_bytes_per_call": float(moved),
                        "roofline": {"bound": "hbm", "achieved": moved / ms / 1e6, "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": moved / ms / 1e6 / HBM_PEAK_GBS}}

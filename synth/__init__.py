@@ -68,11 +68,17 @@ def ffn_layer_planted(seed: int, layer: int, d_model: int, d_ff: int, r: int, q:
     """ffn_layer with planted blocks of predictor keys: for each (t, lo, hi, s)
     in `blocks`, K1 rows lo..hi-1 become s times the unit direction of
     q[t, :r] plus N(0, (0.02 s)^2 / r) noise, so their scores for token t are
-    about s * |q[t, :r]| (far above or below the rest for |s| ~ 0.1)."""
+    about s * |q[t, :r]| (far above or below the rest for |s| ~ 0.1).  t may
+    also be a tuple of tokens: the direction is then the normalised sum of
+    their unit directions (about 1/sqrt(len(t)) of the score for each)."""
     k1t, k2t, v = ffn_layer(seed, layer, d_model, d_ff, r, "f32")
     g = rng(seed, layer, K1_ID, 1)
     for t, lo, hi, s in blocks:
-        u = q[t, :r].astype(np.float64)
+        ts = t if isinstance(t, tuple) else (t,)
+        u = np.zeros(r)
+        for tt in ts:
+            qt = q[tt, :r].astype(np.float64)
+            u += qt / np.linalg.norm(qt)
         u = (u / np.linalg.norm(u)).astype(np.float32)
         k1t[lo:hi] = np.float32(s) * u + _normal(g, (hi - lo, r), 0.02 * abs(s) / np.sqrt(r))
     if dtype == "bf16":
