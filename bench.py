@@ -46,7 +46,7 @@ def algorithmic_bytes(counts: np.ndarray) -> float:
 
 def source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("ffn_decode.hip", "common.hpp"):
+    for f in ("ffn_decode.hip", "exchange.hpp", "common.hpp"):
         with open(os.path.join(ROOT, "attention_spark_ffn_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
