@@ -26,6 +26,8 @@
 //          the union of the selected sets, read each union neuron's V row
 //          segment once and accumulate it into the B outputs, then sum over
 //          threads in a fixed order.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -136,8 +138,106 @@ __device__ __forceinline__ void load_tokens(const float* __restrict__ yin, int B
   }
 }
 
+// ---------------------------------------------------------------- products on the matrix cores
+// D[n][b] = row_n . q_b for a workgroup's rows (at most 48: three tiles of
+// 16) and its token slots (BM <= 8), on v_mfma_f32_16x16x32_bf16 (rows = the
+// tile's rows, columns = token slots and parts).  Each fp32 token vector
+// enters the bf16 products as three parts, q = hi + mid + lo (hi = bf16(q),
+// mid = bf16(q - hi), lo = bf16(q - hi - mid); the two differences are exact,
+// and |q - hi - mid - lo| <= 2^-27 |q|): with the bf16 weights exact and the
+// products accumulated in fp32 the result keeps the accuracy of fp32
+// products.  Two products per K step: columns 0..7 hi and 8..15 mid of the
+// token slots, then lo in columns 0..7.  The K range (kq steps of 32) is
+// split over the workgroup's NW waves; each wave's partial tiles go to
+// part[wave][tile][product][column][row], and mfma_rows_sum adds them in a
+// fixed order.
+typedef __bf16 bt_bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int kMTiles = 3;   // 16-row tiles (kBSlots <= 48)
+constexpr int kMSteps = 8;   // K steps of 32 per wave (K <= 32 * kMSteps * waves)
+static_assert(kBSlots <= 16 * kMTiles, "a workgroup's rows must fit the tiles");
+
+// The A fragments of this wave: row row[t] (a valid row of the workgroup for
+// every lane) of tile t, K steps w * spw + s, elements 8 (lane / 16) .. + 7;
+// a tile whose row is not wanted (want[t] false) reads nothing (zeros).
+template <int NW>
+__device__ __forceinline__ void mfma_rows_load(u32x4 (&fa)[kMTiles][kMSteps], const char* base, size_t rowb,
+                                               const int (&row)[kMTiles], const bool (&want)[kMTiles], int kq,
+                                               int wv, int lane) {
+  const int spw = (kq + NW - 1) / NW;
+#pragma unroll
+  for (int t = 0; t < kMTiles; ++t) {
+    const char* rp = base + (size_t)row[t] * rowb + (size_t)(8 * (lane >> 4)) * sizeof(bf16_t);
+#pragma unroll
+    for (int s = 0; s < kMSteps; ++s) {
+      const int ks = min(wv * spw + min(s, spw - 1), kq - 1);  // steps past the range re-read a valid one (unused)
+      fa[t][s] = want[t] ? load16(rp + (size_t)ks * 64) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int BM, int NW>
+__device__ __forceinline__ void mfma_rows_products(const u32x4 (&fa)[kMTiles][kMSteps], const float* qs, int K,
+                                                   int kq, float (*part)[kMTiles][2][16][16], int wv, int lane) {
+  const int spw = (kq + NW - 1) / NW;
+  const int n = lane & 15, b = n & 7;
+  const bool second = n >= 8, live = b < BM;
+  f32x4 acc[kMTiles][2];
+#pragma unroll
+  for (int t = 0; t < kMTiles; ++t) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMSteps; ++s) {
+    const int ks = wv * spw + s;
+    if (s < spw && ks < kq) {
+      const float* src = qs + (size_t)(live ? b : 0) * K + 32 * ks + 8 * (lane >> 4);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+      const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      bt_bf16x8 b0, b1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = live ? v[j] : 0.f;
+        const __bf16 hi = (__bf16)x;
+        const float r1 = x - (float)hi;
+        const __bf16 mid = (__bf16)r1;
+        const __bf16 lo = (__bf16)(r1 - (float)mid);
+        b0[j] = second ? mid : hi;
+        b1[j] = second ? (__bf16)0.f : lo;
+      }
+#pragma unroll
+      for (int t = 0; t < kMTiles; ++t) {
+        const bt_bf16x8 af = __builtin_bit_cast(bt_bf16x8, fa[t][s]);
+        acc[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b0, acc[t][0], 0, 0, 0);
+        acc[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b1, acc[t][1], 0, 0, 0);
+      }
+    }
+  }
+  // result register i of lane l: row 4 (l / 16) + i, column l % 16
+#pragma unroll
+  for (int t = 0; t < kMTiles; ++t)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<f32x4*>(&part[wv][t][q][lane & 15][4 * (lane >> 4)]) = acc[t][q];
+}
+
+// Row j (< 48) of the product for token slot b: the waves' partials of the
+// three parts, in a fixed order.
+template <int NW>
+__device__ __forceinline__ float mfma_rows_sum(float (*part)[kMTiles][2][16][16], int j, int b) {
+  const int t = j >> 4, m = j & 15;
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += (part[w][t][0][b][m] + part[w][t][0][b + 8][m]) + part[w][t][1][b][m];
+  return s;
+}
+
+// The matrix-core paths take bf16 weights.
+template <typename W>
+constexpr bool kMatrixOk = std::is_same<W, bf16_t>::value;
+
 // ---------------------------------------------------------------- bpred
-template <typename W, int BM>
+// MF: the scores on the matrix cores (bf16 weights, r a multiple of 32 and at
+// most 32 kMSteps waves); otherwise on the vector units.
+template <typename W, int BM, bool MF>
 __global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
   constexpr int CN = Chunk<W>::N;
   extern __shared__ float qs[];  // [B][r]: q[:r] of every token (unscaled)
@@ -159,7 +259,12 @@ __global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) nv[u] = min(n0 + 4 * gi + u, n1 - 1);  // slots past the range: a valid row, not stored
   constexpr int kRound = 5;
+  constexpr int NW = kBThreads / 64;
+  __shared__ float part[NW][kMTiles][2][16][16];  // matrix-core partials
+  static_assert(!MF || std::is_same<W, bf16_t>::value, "matrix-core path: bf16 weights");
+  constexpr bool mf = MF;
   u32x4 raw[kRound][4];
+  u32x4 fa[kMTiles][kMSteps];
   auto issue = [&](int c0) {
 #pragma unroll
     for (int k = 0; k < kRound; ++k)
@@ -169,7 +274,18 @@ __global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
         raw[k][u] = load16(k1 + (size_t)nv[u] * rowb + (size_t)c * 16);
       }
   };
-  issue(l32);
+  if constexpr (mf) {
+    int row[kMTiles];
+    bool want[kMTiles];
+#pragma unroll
+    for (int t = 0; t < kMTiles; ++t) {
+      row[t] = min(n0 + 16 * t + (lane & 15), n1 - 1);
+      want[t] = true;
+    }
+    mfma_rows_load<NW>(fa, k1, rowb, row, want, r / 32, wv, lane);
+  } else {
+    issue(l32);
+  }
   // each token's RMS scale from the previous layer's per-workgroup sums of
   // squares (half-wave b, fixed order), and q[:r] of every token to LDS
   if (a.prenorm) {
@@ -197,13 +313,22 @@ __global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
 #pragma unroll
     for (int b = 0; b < BM; ++b)
       if (b < B) a.scale[b] = sc[b];
+  if constexpr (mf) {
+    mfma_rows_products<BM, NW>(fa, qs, r, r / 32, part, wv, lane);
+    __syncthreads();
+    const int nown = n1 - n0;
+    for (int i = tid; i < BM * kBSlots; i += kBThreads) {
+      const int b = i / kBSlots, j = i % kBSlots;
+      if (b < B && j < nown) hs[b][j] = mfma_rows_sum<NW>(part, j, b) * sc[b];
+    }
+  }
   float acc[4][BM];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int b = 0; b < BM; ++b) acc[u][b] = 0.f;
   const f32x4* q4 = reinterpret_cast<const f32x4*>(qs);  // r is a multiple of 4
-  for (int c0 = l32; c0 < CK; c0 += 32 * kRound) {
+  for (int c0 = l32; !mf && c0 < CK; c0 += 32 * kRound) {
     if (c0 != l32) issue(c0);
 #pragma unroll
     for (int k = 0; k < kRound; ++k) {
@@ -234,7 +359,7 @@ __global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
       }
     }
   }
-  {
+  if constexpr (!mf) {
     float flat[4 * BM];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -263,7 +388,9 @@ __global__ __launch_bounds__(kBThreads) void bpred(const BatchArgs a) {
 }
 
 // ---------------------------------------------------------------- bgate
-template <typename W, int BM>
+// MF: the K2 dots on the matrix cores (bf16 weights, d - r a multiple of 32
+// and at most 32 kMSteps waves); otherwise on the vector units.
+template <typename W, int BM, bool MF>
 __global__ __launch_bounds__(kBThreads) void bgate(const BatchArgs a) {
   constexpr int CN = Chunk<W>::N;
   extern __shared__ float qs[];  // [B][d - r]: q[r:] of every token, scaled
@@ -366,6 +493,47 @@ __global__ __launch_bounds__(kBThreads) void bgate(const BatchArgs a) {
 #pragma unroll
     for (int b = 0; b < BM; ++b)
       sm[u] |= (b < B && n0 + 4 * gi + u < n1 && hv[u][b] > th[b]) ? 1u << b : 0u;
+  }
+  constexpr int NW = kBThreads / 64;
+  // the K2 dots on the matrix cores (the rows of neurons no token selects
+  // read as zeros)
+  static_assert(!MF || std::is_same<W, bf16_t>::value, "matrix-core path: bf16 weights");
+  if constexpr (MF) {
+    __shared__ float part[NW][kMTiles][2][16][16];
+    const int wv = tid >> 6;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (l32 == 0) sel[4 * gi + u] = sm[u];
+    __syncthreads();
+    const int nown = n1 - n0;
+    int row[kMTiles];
+    bool want[kMTiles];
+#pragma unroll
+    for (int t = 0; t < kMTiles; ++t) {
+      const int j = 16 * t + (lane & 15);
+      row[t] = min(n0 + j, n1 - 1);
+      want[t] = j < nown && j < kBSlots && sel[j < kBSlots ? j : 0] != 0;
+    }
+    u32x4 fa[kMTiles][kMSteps];
+    mfma_rows_load<NW>(fa, k2, rowb, row, want, rc / 32, wv, lane);
+    mfma_rows_products<BM, NW>(fa, qs, rc, rc / 32, part, wv, lane);
+    __syncthreads();
+    // gated values of the owned neurons: C[n][b] (exact 0 for the tokens that
+    // do not select n)
+    for (int i = tid; i < BM * kBSlots; i += kBThreads) {
+      const int b = i / kBSlots, j = i % kBSlots;
+      if (b < B && j < nown) {
+        const int n = n0 + j;
+        const bool on = (sel[j] >> b) & 1u;
+        const float g = mfma_rows_sum<NW>(part, j, b);
+        a.C[(size_t)n * BM + b] = on ? gelu_tanh(a.H[(size_t)b * a.d_ff + n] - th[b]) * g : 0.f;
+      }
+    }
+    if (tid < 64) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(lane < kBSlots && sel[lane < kBSlots ? lane : 0] != 0);
+      if (lane == 0) a.umask[blockIdx.x] = m;
+    }
+    return;
   }
   float acc[4][BM];
 #pragma unroll
@@ -925,6 +1093,13 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
   a.C = (float*)(base + Lo.C);
   a.ssp = (float*)(base + Lo.ssp);
   float* ybuf = (float*)(base + Lo.ybuf);
+  // the predictor and K2 products on the matrix cores where the shapes allow
+  constexpr int kMaxK = 32 * kMSteps * (kBThreads / 64);
+  const bool mf1 = kMatrixOk<W> && s.r % 32 == 0 && s.r <= kMaxK;
+  // (the K2 dots: at eight token slots; with fewer, the extra barrier and the
+  // full-tile loads of the matrix-core form cost more than the vector units'
+  // products, measured)
+  const bool mf2 = kMatrixOk<W> && BM >= 8 && (s.d_model - s.r) % 32 == 0 && s.d_model - s.r <= kMaxK;
   for (int l = 0; l < n_layers; ++l) {
     a.k1t = layers[l].k1t;
     a.k2t = layers[l].k2t;
@@ -932,8 +1107,14 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
     a.yin = l == 0 ? q : ybuf;
     a.prenorm = l == 0 ? 0 : 1;
     a.yout = l == n_layers - 1 ? y : ybuf;
-    hipLaunchKernelGGL((bpred<W, BM>), dim3(G), dim3(kBThreads), lds1, st, a);
-    hipLaunchKernelGGL((bgate<W, BM>), dim3(G), dim3(kBThreads), lds2, st, a);
+    if (mf1)
+      hipLaunchKernelGGL((bpred<W, BM, kMatrixOk<W>>), dim3(G), dim3(kBThreads), lds1, st, a);
+    else
+      hipLaunchKernelGGL((bpred<W, BM, false>), dim3(G), dim3(kBThreads), lds1, st, a);
+    if (mf2)
+      hipLaunchKernelGGL((bgate<W, BM, kMatrixOk<W> && BM >= 8>), dim3(G), dim3(kBThreads), lds2, st, a);
+    else
+      hipLaunchKernelGGL((bgate<W, BM, false>), dim3(G), dim3(kBThreads), lds2, st, a);
     if (trace && (trace->counts || trace->idx || trace->theta || trace->q_in))
       hipLaunchKernelGGL(btrace, dim3((unsigned)B), dim3(256), 0, st, a, trace->counts, trace->idx,
                          trace->idx ? trace->cap : 0, trace->theta, trace->q_in, (int64_t)l, (int64_t)n_layers);
