@@ -72,6 +72,18 @@ int decode_limits(const spark_ffn_shape* s) {
   return SPARK_OK;
 }
 
+// Where a batched-decode workspace's layer-by-layer buffers start: after the
+// whole layout of the single-token persistent kernel when the shape takes
+// that kernel (a call with one token runs it), so that neither form's
+// tagged exchange words ever share memory with the other's plain values and
+// a stale value can never pass for a tag; else after the header alone.
+size_t batched_offset(const spark_ffn_shape* s) {
+  if (decode_limits(s) != SPARK_OK) return kBatchedHeader;
+  const size_t d = spark::decode_workspace_bytes(s->d_model, s->d_ff, spark::kDecodeMaxLayersPerLaunch + 1, 1,
+                                                 spark::decode_grid(s->d_ff));
+  return std::max(kBatchedHeader, (d + 255) / 256 * 256);
+}
+
 }  // namespace
 
 extern "C" {
@@ -197,14 +209,7 @@ int spark_ffn_decode_batched_workspace_size(const spark_ffn_shape* s, int64_t B,
   const int64_t wide = s->r > s->d_model - s->r ? s->r : s->d_model - s->r;
   const int64_t slots = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8;  // token slots of the kernels
   if (slots * wide * 4 > spark::kBatchMaxLds) return SPARK_EUNSUPPORTED;
-  // room for either form a call may take: the header of the single-token
-  // persistent kernel, then the layer-by-layer kernels' buffers; or that
-  // kernel's own layout (B = 1)
-  size_t need = kBatchedHeader + spark::decode_batched_workspace_bytes(s->d_model, s->d_ff, B > 0 ? B : 1);
-  if (decode_limits(s) == SPARK_OK)
-    need = std::max(need, spark::decode_workspace_bytes(s->d_model, s->d_ff, spark::kDecodeMaxLayersPerLaunch + 1, 1,
-                                                        spark::decode_grid(s->d_ff)));
-  *bytes = need;
+  *bytes = batched_offset(s) + spark::decode_batched_workspace_bytes(s->d_model, s->d_ff, B > 0 ? B : 1);
   return SPARK_OK;
 }
 
@@ -226,11 +231,11 @@ int spark_ffn_decode_batched(const spark_ffn_shape* s, const spark_ffn_weights* 
   if (B == 0) return SPARK_OK;
   const double z = spark_threshold_z(s->k, s->d_ff);
   // one token: the single-token persistent kernel; more: the layer-by-layer
-  // kernels (after the header the persistent kernel keeps)
+  // kernels (the header's tags and failure record shared with it)
   if (B == 1 && decode_limits(s) == SPARK_OK)
     return hip_status(spark::launch_decode(*s, layers, n_layers, q, 1, y, rms_eps, z, trace, ws, stream));
   return hip_status(spark::launch_decode_batched(*s, layers, n_layers, q, B, y, rms_eps, z, trace,
-                                                 (char*)ws + kBatchedHeader, stream));
+                                                 (char*)ws + batched_offset(s), (uint64_t*)ws, stream));
 }
 
 int spark_ffn_prefill_workspace_size(const spark_ffn_shape* s, int64_t T, size_t* bytes) {

@@ -10,25 +10,29 @@
 // with the tokens of the batch processed together instead of one after the
 // other.
 //
-// Per layer three kernels on the stream (a fourth writes the trace when one
-// is asked for):
-//   bpred: workgroup g owns 32 neurons; it reads their K1 rows once and forms
-//          the scores of all B tokens (q[:r] of every token in LDS, each
-//          token's RMS scale from its own sum of squares), and the per-token
-//          (mean, M2) of its 32 scores;
+// Per layer, on the stream (one more kernel writes the trace when one is
+// asked for):
+//   bpred: workgroup g owns up to 40 neurons; it reads their K1 rows once and
+//          forms the scores of all B tokens (q[:r] of every token in LDS, each
+//          token's RMS scale from the previous layer's sums of squares), and
+//          the per-token (mean, M2) of its scores;
 //   bgate: theta per token from all workgroups' (mean, M2) (two plain sums,
 //          fixed order), then per owned neuron the tokens that select it; the
 //          K2 row of a neuron selected by any token is read once and dotted
 //          with each selecting token's q[r:]; it writes the B gated values
 //          GELU(h - theta) * dot of its neurons (0 for the tokens that do not
 //          select them) and the mask of its neurons selected by any token;
-//   bv:    workgroup w owns a range of output columns; its threads share out
-//          the union of the selected sets, read each union neuron's V row
-//          segment once and accumulate it into the B outputs, then sum over
-//          threads in a fixed order.
+//   bfused: bpred and bgate in one launch whose workgroups exchange the
+//          (mean, M2) as tagged words while they run (bf16 weights, both
+//          products on the matrix cores, a grid the device holds at once);
+//   bv (one token) or bv2 + breduce (more): the union of the selected sets
+//          times V, each union neuron's V row segment read once for all the
+//          tokens, summed over slices in a fixed order, with each token's sum
+//          of squares for the next layer's RMS scale.
 #include <type_traits>
 
 #include "common.hpp"
+#include "exchange.hpp"
 #include "internal.hpp"
 
 namespace spark {
@@ -1000,11 +1004,246 @@ __global__ __launch_bounds__(256) void btrace(const BatchArgs a, int32_t* counts
   }
 }
 
+// ---------------------------------------------------------------- bfused
+// bpred and bgate as one kernel: a grid the device holds at once (one
+// workgroup per CU, checked on the host), the per-workgroup (mean, M2) of the
+// scores exchanged as tagged words (device-scope relaxed atomics, replicated
+// once per XCD; a reader accepts a word only with this launch's tag, taken
+// from the workspace header) instead of across a kernel boundary.  Both
+// products on the matrix cores (bf16 weights; r and d - r multiples of 32, at
+// most 32 kMSteps waves).  Every wait is bounded: on timeout the launch marks
+// the call failed in the header (as the single-token kernel does), writes NaN
+// gated values for its neurons and ends; workgroup 0 advances the header's
+// tag on every way out.
+constexpr int kXRow = 256;  // exchange words are word-major: word k of workgroup g at k * kXRow + g
+constexpr int kXRep = 8;    // replicas (one per XCD)
+
+// A failed call's layer: NaN gated values for the owned neurons, all marked
+// used (so the V product spreads NaN over every output), and the tag advanced.
+template <int BM>
+__device__ __forceinline__ void bfused_failed(const BatchArgs& a, uint64_t* hdr, int n0, int nown, uint32_t tag) {
+  for (int i = threadIdx.x; i < BM * kBSlots; i += kBThreads) {
+    const int b = i / kBSlots, j = i % kBSlots;
+    if (b < a.B && j < nown) a.C[(size_t)(n0 + j) * BM + b] = __builtin_nanf("");
+  }
+  if (threadIdx.x == 0) {
+    a.umask[blockIdx.x] = nown >= 64 ? ~0ull : (1ull << nown) - 1;
+    if (blockIdx.x == 0) __hip_atomic_store(hdr, (uint64_t)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int BM>
+__global__ __launch_bounds__(kBThreads) void bfused(const BatchArgs a, uint64_t* hdr, uint64_t* xs, int xs_stride,
+                                                      int layer) {
+  constexpr int NW = kBThreads / 64;
+  extern __shared__ float dyn[];  // q[:r] of every token slot (unscaled), then q[r:] (scaled)
+  __shared__ float red[BM];       // each token's RMS scale
+  __shared__ float hs[BM][kBSlots];
+  __shared__ float part[NW][kMTiles][2][16][16];
+  __shared__ float th[BM];
+  __shared__ uint32_t sel[kBSlots];
+  __shared__ uint32_t s_tag, s_spin, s_poison;
+  __shared__ uint64_t s_fmark;
+  __shared__ int s_fail;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int gi = tid >> 5, l32 = tid & 31;
+  const int B = a.B, d = a.d_model, r = a.r, rc = d - r;
+  const int G = gridDim.x, w = blockIdx.x;
+  const int n0 = nfirst(w, a.d_ff, G), n1 = nfirst(w + 1, a.d_ff, G), nown = n1 - n0;
+  float* qs1 = dyn;
+  float* qs2 = dyn + (size_t)BM * r;
+  if (tid == 0) {
+    const uint32_t t0 = (uint32_t)get_word(hdr);
+    s_tag = t0 + 1;
+    // one failure mark per call (each layer of it advances the tag by one),
+    // so a call counts once however many of its layers time out
+    s_fmark = (uint64_t)(t0 + 1 - (uint32_t)layer);
+    // hdr[3], when nonzero, is the host-set test hook: it bounds every wait
+    // and makes the exchange wait for a tag no word carries
+    const uint64_t lim = get_word(hdr + 3);
+    s_spin = lim ? (uint32_t)lim : (1u << 22);
+    s_poison = lim ? 0x80000000u : 0u;
+    // an earlier layer of this call failed (that launch ended before this
+    // one began, so every workgroup reads the same): this layer fails too
+    s_fail = get_word(hdr + 1) == s_fmark ? 1 : 0;
+  }
+  // ---------------- the scores: K1 fragments first (they do not depend on the tokens)
+  u32x4 fa[kMTiles][kMSteps];
+  {
+    int row[kMTiles];
+    bool want[kMTiles];
+#pragma unroll
+    for (int t = 0; t < kMTiles; ++t) {
+      row[t] = min(n0 + 16 * t + (lane & 15), n1 - 1);
+      want[t] = true;
+    }
+    mfma_rows_load<NW>(fa, (const char*)a.k1t, (size_t)r * sizeof(bf16_t), row, want, r / 32, wv, lane);
+  }
+  // each token's RMS scale from the previous layer's per-segment sums of
+  // squares (half-wave b, fixed order)
+  if (gi < BM) {
+    const int b = gi;
+    float sc = 1.f;
+    if (a.prenorm && b < B) {
+      float ss = 0.f;
+      for (int w0 = l32; w0 < a.G3; w0 += 32 * 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = w0 + 32 * k < a.G3 ? a.ssp[(size_t)(w0 + 32 * k) * BM + b] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ss += v[k];
+      }
+      ss = half_sum(ss);
+      sc = 1.f / sqrtf(ss / (float)d + a.eps);
+    }
+    if (l32 == 0) red[b] = sc;
+  }
+  for (int i = B * r + tid; i < BM * r; i += kBThreads) qs1[i] = 0.f;  // empty token slots
+  for (int i = B * rc + tid; i < BM * rc; i += kBThreads) qs2[i] = 0.f;
+  load_tokens<BM, kBThreads>(a.yin, B, d, 0, r, qs1, nullptr, nullptr);
+  __syncthreads();
+  if (s_fail) {
+    bfused_failed<BM>(a, hdr, n0, nown, s_tag);
+    return;
+  }
+  load_tokens<BM, kBThreads>(a.yin, B, d, r, rc, qs2, red, nullptr);  // q[r:] scaled (used after the exchange)
+  if (w == 0 && tid < B) a.scale[tid] = red[tid];
+  mfma_rows_products<BM, NW>(fa, qs1, r, r / 32, part, wv, lane);
+  __syncthreads();
+  for (int i = tid; i < BM * kBSlots; i += kBThreads) {
+    const int b = i / kBSlots, j = i % kBSlots;
+    if (b < B && j < nown) {
+      const float h = mfma_rows_sum<NW>(part, j, b) * red[b];
+      hs[b][j] = h;
+      a.H[(size_t)b * a.d_ff + n0 + j] = h;
+    }
+  }
+  __syncthreads();
+  // ---------------- this workgroup's (mean, M2) per token, published
+  const uint32_t tag = s_tag;
+  for (int b = wv; b < B; b += NW) {
+    const bool own = lane < nown;
+    const float h = own ? hs[b][lane] : 0.f;
+    const float mean = wave_sum_dpp(h) / (float)nown;
+    const float dv = own ? h - mean : 0.f;
+    const float m2 = wave_sum_dpp(dv * dv);
+    if (lane < kXRep) {
+      uint64_t* dst = xs + (size_t)lane * xs_stride + (size_t)(2 * b) * kXRow + w;
+      put_tagged(dst, mean, tag);
+      put_tagged(dst + kXRow, m2, tag);
+    }
+  }
+  // ---------------- every workgroup's (mean, M2) of token gi (half-wave gi,
+  // workgroups l32 + 32 k), then theta (the mean, then the squared deviations
+  // about it, fixed order)
+  if (gi < B) {
+    const int b = gi;
+    const uint64_t* src = xs + (size_t)xcc_id() * xs_stride + (size_t)(2 * b) * kXRow;
+    constexpr int KG = 8;  // G <= 256
+    float mn[KG], m2v[KG], nn[KG];
+    uint32_t need = 0;
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const int g = l32 + 32 * k;
+      need |= g < G ? 3u << (2 * k) : 0u;
+      nn[k] = g < G ? (float)(nfirst(g + 1, a.d_ff, G) - nfirst(g, a.d_ff, G)) : 0.f;
+      mn[k] = m2v[k] = 0.f;
+    }
+    const uint32_t want_tag = tag ^ s_poison, spin_limit = s_spin;
+    bool ok = true;
+    for (uint32_t spin = 0; need; ++spin) {
+      uint64_t x[2 * KG];
+#pragma unroll
+      for (int k = 0; k < KG; ++k)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          x[2 * k + q] = ((need >> (2 * k + q)) & 1) ? get_word(src + (size_t)q * kXRow + l32 + 32 * k) : 0;
+#pragma unroll
+      for (int k = 0; k < KG; ++k)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          if (((need >> (2 * k + q)) & 1) && (uint32_t)(x[2 * k + q] >> 32) == want_tag) {
+            const float v = __uint_as_float((uint32_t)x[2 * k + q]);
+            if (q == 0)
+              mn[k] = v;
+            else
+              m2v[k] = v;
+            need &= ~(1u << (2 * k + q));
+          }
+      if (!need) break;
+      if (spin > spin_limit || ((spin & 1023) == 1023 && get_word(hdr + 1) == s_fmark)) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    float s1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < KG; ++k) s1 += nn[k] * mn[k];
+    const float mu = half_sum(s1) / (float)a.d_ff;
+    float s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const float dm = mn[k] - mu;
+      s2 += nn[k] > 0.f ? m2v[k] + nn[k] * dm * dm : 0.f;
+    }
+    s2 = half_sum(s2);
+    if (l32 == 0) th[b] = mu + sqrtf(s2 / (float)a.d_ff) * a.z;
+    if (!ok) {
+      s_fail = 1;
+      raise_failure(hdr, s_fmark);
+    }
+  }
+  __syncthreads();
+  if (s_fail) {
+    bfused_failed<BM>(a, hdr, n0, nown, tag);
+    return;
+  }
+  if (w == 0 && tid < B) a.theta[tid] = th[tid];
+  // ---------------- the tokens selecting each owned neuron
+  if (tid < kBSlots) {
+    uint32_t m = 0;
+    for (int b = 0; b < B; ++b) m |= (tid < nown && hs[b][tid] > th[b]) ? 1u << b : 0u;
+    sel[tid] = m;
+  }
+  __syncthreads();
+  // ---------------- the K2 dots of the selected neurons on the matrix cores
+  {
+    int row[kMTiles];
+    bool want[kMTiles];
+#pragma unroll
+    for (int t = 0; t < kMTiles; ++t) {
+      const int j = 16 * t + (lane & 15);
+      row[t] = min(n0 + j, n1 - 1);
+      want[t] = j < nown && j < kBSlots && sel[j < kBSlots ? j : 0] != 0;
+    }
+    mfma_rows_load<NW>(fa, (const char*)a.k2t, (size_t)rc * sizeof(bf16_t), row, want, rc / 32, wv, lane);
+    mfma_rows_products<BM, NW>(fa, qs2, rc, rc / 32, part, wv, lane);
+  }
+  __syncthreads();
+  for (int i = tid; i < BM * kBSlots; i += kBThreads) {
+    const int b = i / kBSlots, j = i % kBSlots;
+    if (b < B && j < nown) {
+      const bool on = (sel[j] >> b) & 1u;
+      const float g = mfma_rows_sum<NW>(part, j, b);
+      a.C[(size_t)(n0 + j) * BM + b] = on ? gelu_tanh(hs[b][j] - th[b]) * g : 0.f;
+    }
+  }
+  if (tid < 64) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(lane < kBSlots && sel[lane < kBSlots ? lane : 0] != 0);
+    if (lane == 0) a.umask[w] = m;
+  }
+  // every workgroup has read the header before publishing, and workgroup 0
+  // gets here only after every workgroup published
+  if (w == 0 && tid == 0) __hip_atomic_store(hdr, (uint64_t)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------- host side
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct BatchLayout {
-  size_t H, P, scale, theta, umask, C, ybuf, ssp, P2, total;
+  size_t H, P, scale, theta, umask, C, ybuf, ssp, P2, X, total;
+  int xs_stride;  // words between the exchange replicas of bfused
 };
 
 // Workgroups of bpred and bgate: one per CU, more when a CU's share of the
@@ -1026,6 +1265,11 @@ static BatchLayout batch_layout(int64_t d_model, int64_t d_ff, int64_t B) {
     off += round_up(bytes, 256);
     return o;
   };
+  // the tagged exchange words first: their place does not depend on B, so
+  // calls with any batch size on one workspace only ever leave tagged words
+  // (or zeros) there
+  L.xs_stride = (int)round_up((size_t)2 * kBatchMax * kXRow + 64, 512);  // replicas 4 KB+ apart
+  L.X = take((size_t)kXRep * L.xs_stride * 8);
   L.H = take((size_t)B * d_ff * 4);
   L.P = take((size_t)G * B * 2 * 4);
   L.scale = take((size_t)B * 4);
@@ -1051,7 +1295,7 @@ size_t decode_batched_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t B) 
 template <typename W, int BM>
 static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_weights* layers, int n_layers,
                                    const float* q, int64_t B, float* y, float eps, double z,
-                                   const spark_ffn_trace* trace, void* ws, hipStream_t st) {
+                                   const spark_ffn_trace* trace, void* ws, uint64_t* hdr, hipStream_t st) {
   constexpr int CN = Chunk<W>::N;
   const BatchLayout Lo = batch_layout(s.d_model, s.d_ff, B);
   char* base = (char*)ws;
@@ -1100,6 +1344,20 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
   // full-tile loads of the matrix-core form cost more than the vector units'
   // products, measured)
   const bool mf2 = kMatrixOk<W> && BM >= 8 && (s.d_model - s.r) % 32 == 0 && s.d_model - s.r <= kMaxK;
+  // both products on the matrix cores in one kernel per layer, when the device
+  // holds the whole grid at once (its workgroups exchange the statistics
+  // while they run)
+  bool fused = false;
+  const size_t ldsf = (size_t)BM * s.d_model * 4;
+  if (kMatrixOk<W> && mf1 && (s.d_model - s.r) % 32 == 0 && s.d_model - s.r <= kMaxK && G <= kXRow) {
+    int per_cu = 0;
+    if (hipFuncSetAttribute((const void*)bfused<BM>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsf) ==
+            hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bfused<BM>, kBThreads, ldsf) == hipSuccess &&
+        (int64_t)per_cu * device_cu_count() >= G)
+      fused = true;
+    (void)hipGetLastError();
+  }
   for (int l = 0; l < n_layers; ++l) {
     a.k1t = layers[l].k1t;
     a.k2t = layers[l].k2t;
@@ -1107,14 +1365,19 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
     a.yin = l == 0 ? q : ybuf;
     a.prenorm = l == 0 ? 0 : 1;
     a.yout = l == n_layers - 1 ? y : ybuf;
-    if (mf1)
-      hipLaunchKernelGGL((bpred<W, BM, kMatrixOk<W>>), dim3(G), dim3(kBThreads), lds1, st, a);
-    else
-      hipLaunchKernelGGL((bpred<W, BM, false>), dim3(G), dim3(kBThreads), lds1, st, a);
-    if (mf2)
-      hipLaunchKernelGGL((bgate<W, BM, kMatrixOk<W> && BM >= 8>), dim3(G), dim3(kBThreads), lds2, st, a);
-    else
-      hipLaunchKernelGGL((bgate<W, BM, false>), dim3(G), dim3(kBThreads), lds2, st, a);
+    if (fused) {
+      hipLaunchKernelGGL((bfused<BM>), dim3(G), dim3(kBThreads), ldsf, st, a, hdr, (uint64_t*)(base + Lo.X),
+                         Lo.xs_stride, l);
+    } else {
+      if (mf1)
+        hipLaunchKernelGGL((bpred<W, BM, kMatrixOk<W>>), dim3(G), dim3(kBThreads), lds1, st, a);
+      else
+        hipLaunchKernelGGL((bpred<W, BM, false>), dim3(G), dim3(kBThreads), lds1, st, a);
+      if (mf2)
+        hipLaunchKernelGGL((bgate<W, BM, kMatrixOk<W> && BM >= 8>), dim3(G), dim3(kBThreads), lds2, st, a);
+      else
+        hipLaunchKernelGGL((bgate<W, BM, false>), dim3(G), dim3(kBThreads), lds2, st, a);
+    }
     if (trace && (trace->counts || trace->idx || trace->theta || trace->q_in))
       hipLaunchKernelGGL(btrace, dim3((unsigned)B), dim3(256), 0, st, a, trace->counts, trace->idx,
                          trace->idx ? trace->cap : 0, trace->theta, trace->q_in, (int64_t)l, (int64_t)n_layers);
@@ -1137,19 +1400,20 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
 template <typename W>
 static hipError_t launch_batched_w(const spark_ffn_shape& s, const spark_ffn_weights* layers, int n_layers,
                                    const float* q, int64_t B, float* y, float eps, double z,
-                                   const spark_ffn_trace* trace, void* ws, hipStream_t st) {
-  if (B <= 1) return launch_batched_t<W, 1>(s, layers, n_layers, q, B, y, eps, z, trace, ws, st);
-  if (B <= 2) return launch_batched_t<W, 2>(s, layers, n_layers, q, B, y, eps, z, trace, ws, st);
-  if (B <= 4) return launch_batched_t<W, 4>(s, layers, n_layers, q, B, y, eps, z, trace, ws, st);
-  return launch_batched_t<W, 8>(s, layers, n_layers, q, B, y, eps, z, trace, ws, st);
+                                   const spark_ffn_trace* trace, void* ws, uint64_t* hdr, hipStream_t st) {
+  if (B <= 1) return launch_batched_t<W, 1>(s, layers, n_layers, q, B, y, eps, z, trace, ws, hdr, st);
+  if (B <= 2) return launch_batched_t<W, 2>(s, layers, n_layers, q, B, y, eps, z, trace, ws, hdr, st);
+  if (B <= 4) return launch_batched_t<W, 4>(s, layers, n_layers, q, B, y, eps, z, trace, ws, hdr, st);
+  return launch_batched_t<W, 8>(s, layers, n_layers, q, B, y, eps, z, trace, ws, hdr, st);
 }
 
 hipError_t launch_decode_batched(const spark_ffn_shape& s, const spark_ffn_weights* layers, int n_layers,
                                  const float* q, int64_t B, float* y, float eps, double z,
-                                 const spark_ffn_trace* trace, void* ws, hipStream_t st) {
+                                 const spark_ffn_trace* trace, void* ws, uint64_t* hdr, hipStream_t st) {
   if (B == 0) return hipSuccess;
-  if (s.wdtype == SPARK_BF16) return launch_batched_w<bf16_t>(s, layers, n_layers, q, B, y, eps, z, trace, ws, st);
-  return launch_batched_w<float>(s, layers, n_layers, q, B, y, eps, z, trace, ws, st);
+  if (s.wdtype == SPARK_BF16)
+    return launch_batched_w<bf16_t>(s, layers, n_layers, q, B, y, eps, z, trace, ws, hdr, st);
+  return launch_batched_w<float>(s, layers, n_layers, q, B, y, eps, z, trace, ws, hdr, st);
 }
 
 }  // namespace spark

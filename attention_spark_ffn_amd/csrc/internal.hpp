@@ -46,9 +46,11 @@ hipError_t launch_decode_noalloc(const spark_ffn_shape& s, const spark_ffn_weigh
 constexpr int kBatchMax = 8;          // tokens per batch
 constexpr int kBatchMaxLds = 65536;   // bytes of q held in LDS per kernel (slots x max(r, d_model - r) x 4)
 size_t decode_batched_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t B);
+// ws: the buffers after the workspace header; hdr: the header (exchange tags,
+// failure record), used by the fused predictor-and-gate kernel.
 hipError_t launch_decode_batched(const spark_ffn_shape& s, const spark_ffn_weights* layers, int n_layers,
                                  const float* q, int64_t B, float* y, float eps, double z,
-                                 const spark_ffn_trace* trace, void* ws, hipStream_t st);
+                                 const spark_ffn_trace* trace, void* ws, uint64_t* hdr, hipStream_t st);
 
 // ---------------------------------------------------------------- prefill
 size_t prefill_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t T);

@@ -197,9 +197,12 @@ int64_t spark_ffn_decode_tags(int n_layers, int64_t T);
  * FFN" and "Statistical Top-k"); results equal spark_ffn_decode's up to the
  * order of fp32 sums.
  * Forms, chosen per call: B = 1 (within spark_ffn_decode's limits) runs the
- * single-token persistent kernel; larger batches run per layer the predictor
- * kernel, the gate kernel and the V product (plus one kernel when a trace is
- * asked for).
+ * single-token persistent kernel; larger batches run per layer one kernel for
+ * the predictor and the gate, whose workgroups exchange the score statistics
+ * while they run (bf16 weights, r and d_model - r multiples of 32 and at most
+ * 1280, d_ff at most 256 x 40, and a grid the device holds at once), else a
+ * predictor kernel and a gate kernel; then the V product (plus one kernel
+ * when a trace is asked for).
  * Requires 0 <= B <= 8, d_model <= 8192, d_ff <= 65536,
  * P * max(r, d_model - r) * 4 <= 65536 with P = B rounded up to a power of
  * two, q and y 16-byte aligned, and the weight conditions of
@@ -207,11 +210,12 @@ int64_t spark_ffn_decode_tags(int n_layers, int64_t T);
  * 256-byte aligned, at least 256 bytes) must be zero-filled before its first
  * use and then handed unchanged to later calls: like spark_ffn_decode's it
  * carries the exchange tags (one call uses spark_ffn_decode_tags(n_layers, 1)
- * of them; zero it again before 2^32 - 1 are used) and the failure record at
- * byte offsets 16 (failed calls) and 24 (test hook, keep 0), both used by the
- * single-token kernel (B = 1): a call whose exchange wait times out (a grid
- * the device could not keep running) returns SPARK_OK with NaN in y and
- * counts itself at offset 16.  Calls that overlap on one workspace race.
+ * of them or fewer; zero it again before 2^32 - 1 are used) and the failure
+ * record at byte offsets 16 (failed calls) and 24 (test hook, keep 0), both
+ * used by the forms that exchange data while they run: a call whose exchange
+ * wait times out (a grid the device could not keep running) returns SPARK_OK
+ * with NaN in y and counts itself once at offset 16.  Calls that overlap on
+ * one workspace race.
  */
 int spark_ffn_decode_batched(const spark_ffn_shape *s, const spark_ffn_weights *layers, int n_layers,
                              const float *q, int64_t B, float *y, float rms_eps, const spark_ffn_trace *trace,

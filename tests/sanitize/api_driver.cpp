@@ -53,7 +53,7 @@ size_t decode_batched_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t B) 
   return (size_t)(d_model + d_ff) * B * 8;
 }
 hipError_t launch_decode_batched(const spark_ffn_shape&, const spark_ffn_weights*, int, const float*, int64_t, float*,
-                                 float, double, const spark_ffn_trace*, void*, hipStream_t) {
+                                 float, double, const spark_ffn_trace*, void*, uint64_t*, hipStream_t) {
   ++launches;
   return hipSuccess;
 }

@@ -151,6 +151,37 @@ def test_batched_one_token_failure_path_and_recovery():
     assert ws.failures() == 2
 
 
+def test_batched_fused_failure_path_and_recovery():
+    """Four tokens on bf16 weights run the fused predictor-and-gate kernel,
+    whose workgroups exchange their score statistics while they run: its
+    failure path driven from the host through the workspace's test hook ends
+    with every kernel exiting, counts one failed call for three failed layers,
+    leaves NaN in y and raises in the checked wrapper; with the hook cleared
+    the next calls on the same workspace match a fresh workspace bit for bit."""
+    layers_np = [synth.ffn_layer(31, l, 2304, 9216, 1152, "bf16") for l in range(3)]
+    layers = [tuple(to_dev(a) for a in lw) for lw in layers_np]
+    q = torch.from_numpy(synth.queries(31, 4, 2304)).to(DEV)
+    nbytes = 1 << 24
+    good = sf.spark_ffn_decode_batched(q, layers, 737, 1152, ws=torch.zeros(nbytes, dtype=torch.uint8, device=DEV))
+    ws = sf.TaggedWorkspace(torch.zeros(nbytes, dtype=torch.uint8, device=DEV))
+    first = sf.spark_ffn_decode_batched(q, layers, 737, 1152, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first, good) and ws.failures() == 0
+    ws.buf[24:32].view(torch.int64).fill_(1)
+    with pytest.raises(RuntimeError, match="timed out"):
+        sf.spark_ffn_decode_batched(q, layers, 737, 1152, ws=ws)
+    assert ws.failures() == 1
+    y = sf.spark_ffn_decode_batched(q, layers, 737, 1152, ws=ws, check=False)
+    torch.cuda.synchronize()
+    assert ws.new_failures() == 1 and ws.failures() == 2 and bool(torch.isnan(y).all())
+    ws.buf[24:32].view(torch.int64).fill_(0)
+    for _ in range(2):
+        again = sf.spark_ffn_decode_batched(q, layers, 737, 1152, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again, good)
+    assert ws.failures() == 2
+
+
 def test_batched_repeated_calls_share_workspace():
     """Calls with different batch sizes on the one cached workspace (a batch of
     one carries exchange tags in it, the others only use the space after its
