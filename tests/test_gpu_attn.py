@@ -71,6 +71,9 @@ def test_attn_deterministic():
 @pytest.mark.parametrize("Hq,Hkv,n,hd,r,ka", [
     (16, 1, 3000, 128, 64, 200),     # 16 query heads per KV head (two register groups of 8)
     (2, 1, 150000, 64, 32, 256),     # 586 chunks of 256 tokens
+    (2, 1, 3000, 512, 256, 4096),    # every token attended, more than one LDS batch, hd 512
+    (4, 2, 20000, 320, 160, 4000),   # ~4000 selected: two LDS batches; hd 320
+    (2, 2, 5000, 264, 128, 8000),    # every token attended, more than the list capacity of 4096
 ])
 def test_attn_wide_groups_and_long_context(Hq, Hkv, n, hd, r, ka):
     run_attn(Hq, Hkv, n, hd, r, ka, n + Hq, scale=0.5)
