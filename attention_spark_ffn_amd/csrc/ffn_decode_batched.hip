@@ -1016,6 +1016,8 @@ __global__ __launch_bounds__(256) void btrace(const BatchArgs a, int32_t* counts
 // gated values for its neurons and ends; workgroup 0 advances the header's
 // tag on every way out.
 constexpr int kXRow = 256;  // exchange words are word-major: word k of workgroup g at k * kXRow + g
+// bfused loads q[:r] and q[r:] as one 16-byte piece per thread and token
+static_assert(4 * kBThreads >= 32 * kMSteps * (kBThreads / 64), "r and d - r up to the products' K must fit");
 constexpr int kXRep = 8;    // replicas (one per XCD)
 
 // A failed call's layer: NaN gated values for the owned neurons, all marked
@@ -1067,7 +1069,22 @@ __global__ __launch_bounds__(kBThreads) void bfused(const BatchArgs a, uint64_t*
     // one began, so every workgroup reads the same): this layer fails too
     s_fail = get_word(hdr + 1) == s_fmark ? 1 : 0;
   }
-  // ---------------- the scores: K1 fragments first (they do not depend on the tokens)
+  // ---------------- the scores.  The small loads first (the previous layer's
+  // sums of squares, q[:r] of every token: one 16-byte piece per thread and
+  // token, r <= 4 kBThreads), then the K1 fragments, so that waiting for the
+  // small ones does not wait for the fragments.
+  const bool pre = a.prenorm && gi < B;
+  float ssv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int g3 = l32 + 32 * k;
+    ssv[k] = pre && g3 < a.G3 ? a.ssp[(size_t)g3 * BM + gi] : 0.f;
+  }
+  const bool qin = 4 * tid < r;
+  f32x4 xq[BM];
+#pragma unroll
+  for (int b = 0; b < BM; ++b)
+    xq[b] = b < B && qin ? *reinterpret_cast<const f32x4*>(a.yin + (size_t)b * d + 4 * tid) : f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 fa[kMTiles][kMSteps];
   {
     int row[kMTiles];
@@ -1079,34 +1096,29 @@ __global__ __launch_bounds__(kBThreads) void bfused(const BatchArgs a, uint64_t*
     }
     mfma_rows_load<NW>(fa, (const char*)a.k1t, (size_t)r * sizeof(bf16_t), row, want, r / 32, wv, lane);
   }
-  // each token's RMS scale from the previous layer's per-segment sums of
-  // squares (half-wave b, fixed order)
+  // each token's RMS scale (half-wave b, fixed order)
   if (gi < BM) {
-    const int b = gi;
     float sc = 1.f;
-    if (a.prenorm && b < B) {
+    if (pre) {
       float ss = 0.f;
-      for (int w0 = l32; w0 < a.G3; w0 += 32 * 8) {
-        float v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = w0 + 32 * k < a.G3 ? a.ssp[(size_t)(w0 + 32 * k) * BM + b] : 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) ss += v[k];
-      }
+      for (int k = 0; k < 8; ++k) ss += ssv[k];
+      for (int g3 = l32 + 256; g3 < a.G3; g3 += 32) ss += a.ssp[(size_t)g3 * BM + gi];  // more than 256 segments
       ss = half_sum(ss);
       sc = 1.f / sqrtf(ss / (float)d + a.eps);
     }
-    if (l32 == 0) red[b] = sc;
+    if (l32 == 0) red[gi] = sc;
   }
-  for (int i = B * r + tid; i < BM * r; i += kBThreads) qs1[i] = 0.f;  // empty token slots
-  for (int i = B * rc + tid; i < BM * rc; i += kBThreads) qs2[i] = 0.f;
-  load_tokens<BM, kBThreads>(a.yin, B, d, 0, r, qs1, nullptr, nullptr);
+  // q[:r] unscaled (the scale goes on the sums); empty token slots zero
+  if (qin) {
+#pragma unroll
+    for (int b = 0; b < BM; ++b) *reinterpret_cast<f32x4*>(qs1 + (size_t)b * r + 4 * tid) = xq[b];
+  }
   __syncthreads();
   if (s_fail) {
     bfused_failed<BM>(a, hdr, n0, nown, s_tag);
     return;
   }
-  load_tokens<BM, kBThreads>(a.yin, B, d, r, rc, qs2, red, nullptr);  // q[r:] scaled (used after the exchange)
   if (w == 0 && tid < B) a.scale[tid] = red[tid];
   mfma_rows_products<BM, NW>(fa, qs1, r, r / 32, part, wv, lane);
   __syncthreads();
@@ -1131,6 +1143,20 @@ __global__ __launch_bounds__(kBThreads) void bfused(const BatchArgs a, uint64_t*
       uint64_t* dst = xs + (size_t)lane * xs_stride + (size_t)(2 * b) * kXRow + w;
       put_tagged(dst, mean, tag);
       put_tagged(dst + kXRow, m2, tag);
+    }
+  }
+  // q[r:] of every token, scaled (used after the exchange; the barrier after
+  // it orders these LDS writes before the K2 products)
+  {
+    const bool kin = 4 * tid < rc;
+    f32x4 xk[BM];
+#pragma unroll
+    for (int b = 0; b < BM; ++b)
+      xk[b] = b < B && kin ? *reinterpret_cast<const f32x4*>(a.yin + (size_t)b * d + r + 4 * tid)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (kin) {
+#pragma unroll
+      for (int b = 0; b < BM; ++b) *reinterpret_cast<f32x4*>(qs2 + (size_t)b * rc + 4 * tid) = xk[b] * red[b];
     }
   }
   // ---------------- every workgroup's (mean, M2) of token gi (half-wave gi,
