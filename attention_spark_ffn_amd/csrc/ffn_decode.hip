@@ -19,12 +19,16 @@
 //     statistics exchange, the K2 gather-dot, the V rows, and the exchanges of
 //     the layer output.
 // Per layer three grid-wide exchanges (A: per-workgroup (mean, M2) of the
-// predictor scores -> theta; B: per-workgroup partial y -> column owners;
-// C: owned columns of y -> every workgroup) move 64-bit words that carry the
-// value and a 32-bit tag.  Writers store them with device-scope relaxed
-// atomics (coherent across the eight XCD L2 caches); readers poll until the
-// tag of the exchange appears, so no cross-XCD fence is needed.  Exchanges A
-// and C are replicated once per XCD so each replica has 32 readers.
+// predictor scores -> theta; B: per-workgroup selected list, a 64-bit mask
+// and the gated values -> every workgroup; C: owned columns of y -> every
+// workgroup) move 64-bit words that carry the value and a 32-bit tag.
+// Writers store them with device-scope relaxed atomics (coherent across the
+// eight XCD L2 caches); readers poll until the tag of the exchange appears,
+// so no cross-XCD fence is needed.  Every record is replicated once per XCD
+// so each replica has 32 readers.  In exchange B only the two mask words are
+// polled: the entries are stored before them and read once the mask is seen
+// (an entry still without its tag is polled), which keeps the polling
+// traffic of 256 readers to two words per record.
 // Every wait is bounded: on timeout the kernel records a failure in the
 // workspace header (the failed call's mark and a count of failed calls), the
 // workgroups write NaN over the output columns they own and leave, and
@@ -86,9 +90,6 @@ struct DecShared {
   float g[kDecodeMaxNeuronsPerWG];   // K2^T q[r:] of the owned neurons (candidates, then misses)
   int cnt[256];                      // selected count of every workgroup
   int off[256];                      // exclusive prefix of cnt
-  union {
-    float stage[256][kRecEntries];   // record entries as gathered, before placement
-  } t;
   float colpart[4][16];              // per-wave sums of the owned columns
   float wred[8];
   float theta;
@@ -113,6 +114,17 @@ __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
 // First neuron of workgroup g (g * d_ff < 2^32 under the decode limits).
 __device__ __forceinline__ int own_first(int g, int d_ff, int G) {
   return (int)((uint32_t)g * (uint32_t)d_ff / (uint32_t)G);
+}
+
+// Output columns owned by workgroup wg: the workgroups of one XCD
+// (wg = x + 8j) own one contiguous range, so each V row segment is read once
+// per XCD.  Ranges are whole 16-byte chunks of a V row (cn elements each).
+__device__ __forceinline__ void col_range(int wg, int G, int d_model, int cn, int& c0, int& ncol) {
+  const int o = (G % 8 == 0) ? (wg & 7) * (G / 8) + (wg >> 3) : wg;
+  const int vch = d_model / cn;  // 16-byte chunks per V row
+  const int ch0 = (int)((int64_t)o * vch / G);
+  c0 = ch0 * cn;
+  ncol = ((int)((int64_t)(o + 1) * vch / G) - ch0) * cn;
 }
 
 // Both roles execute exactly the same sequence of workgroup barriers:
@@ -326,14 +338,15 @@ __device__ __forceinline__ float k2_dot_row16(const char* row, const float* qr, 
 }
 
 // This thread's share of the V product: the selected neurons of one record
-// (workgroup gg's), NCH owned 16-byte chunks of each V row.  The first kSpecE
-// entries take their gated values from registers and all their loads are
-// issued before any is used; later entries (a record with more selected
-// neurons) are read one at a time.  Returns false if an overflow entry never
-// appeared.
+// (workgroup gg's, whose selection mask Mg is known), NCH owned 16-byte
+// chunks of each V row.  The loads of the first kSpecE entries' gated values
+// and of their V chunks are all issued before any is used (one memory round
+// trip); every entry word carries the exchange tag, and one that is not yet
+// visible is polled again.  Later entries (a record with more selected
+// neurons) are read one at a time.  Returns false if an entry never appeared.
 template <typename W, int NCH>
 __device__ __forceinline__ bool v_record(const DecodeParams& p, const DecShared& S, const char* vbase, size_t vrow,
-                                         uint64_t Mg, int nb, const float (&cspec)[kSpecE], int gg, uint32_t tagB,
+                                         uint64_t Mg, int nb, const uint64_t* rp, int gg, uint32_t tagB,
                                          float (&acc)[2 * Chunk<W>::N]) {
   constexpr int CN = Chunk<W>::N;
   const int n = __builtin_popcountll(Mg);
@@ -344,12 +357,27 @@ __device__ __forceinline__ bool v_record(const DecodeParams& p, const DecShared&
     jv[e] = mm ? __builtin_ctzll(mm) : 0;
     mm &= mm - 1;
   }
+  uint64_t ew[kSpecE];
+#pragma unroll
+  for (int e = 0; e < kSpecE; ++e) ew[e] = e < n ? get_word(rp + (size_t)(2 + e) * kRecRow) : 0;
   u32x4 raw[kSpecE][NCH];
 #pragma unroll
   for (int e = 0; e < kSpecE; ++e)
     if (e < n)
 #pragma unroll
       for (int hh = 0; hh < NCH; ++hh) raw[e][hh] = load16(vbase + (size_t)(nb + jv[e]) * vrow + hh * 16);
+  bool ok = true;
+  float cv[kSpecE];
+#pragma unroll
+  for (int e = 0; e < kSpecE; ++e) {
+    cv[e] = __uint_as_float((uint32_t)ew[e]);
+    if (e < n && (uint32_t)(ew[e] >> 32) != tagB) {  // not yet visible: poll it
+      const uint64_t* ep[1] = {rp + (size_t)(2 + e) * kRecRow};
+      float v1[1];
+      ok = ok && gather_tagged<1>(ep, tagB, v1, p.hdr, S.fmark, S.spin_limit);
+      cv[e] = ok ? v1[0] : 0.f;
+    }
+  }
 #pragma unroll
   for (int e = 0; e < kSpecE; ++e)
     if (e < n)
@@ -358,27 +386,21 @@ __device__ __forceinline__ bool v_record(const DecodeParams& p, const DecShared&
         float wf[CN];
         Chunk<W>::widen(raw[e][hh], wf);
 #pragma unroll
-        for (int i = 0; i < CN; ++i) acc[hh * CN + i] += cspec[e] * wf[i];
+        for (int i = 0; i < CN; ++i) acc[hh * CN + i] += cv[e] * wf[i];
       }
-  bool ok = true;
-  for (int e = kSpecE; e < n; ++e) {
+  for (int e = kSpecE; e < n && ok; ++e) {
     const int j = __builtin_ctzll(mm);
     mm &= mm - 1;
-    float cv;
-    if (e < kRecEntries) {
-      cv = S.t.stage[gg][e];
-    } else {
-      const uint64_t* op[1] = {p.ovf + (size_t)gg * kOvfWords + (e - kRecEntries)};
-      float ov[1];
-      ok = ok && gather_tagged<1>(op, tagB, ov, p.hdr, S.fmark, S.spin_limit);
-      cv = ok ? ov[0] : 0.f;
-    }
+    const uint64_t* ep[1] = {e < kRecEntries ? rp + (size_t)(2 + e) * kRecRow
+                                             : p.ovf + (size_t)gg * kOvfWords + (e - kRecEntries)};
+    float v1[1];
+    ok = gather_tagged<1>(ep, tagB, v1, p.hdr, S.fmark, S.spin_limit);
 #pragma unroll
     for (int hh = 0; hh < NCH; ++hh) {
       float wf[CN];
       Chunk<W>::widen(load16(vbase + (size_t)(nb + j) * vrow + hh * 16), wf);
 #pragma unroll
-      for (int i = 0; i < CN; ++i) acc[hh * CN + i] += cv * wf[i];
+      for (int i = 0; i < CN; ++i) acc[hh * CN + i] += v1[0] * wf[i];
     }
   }
   return ok;
@@ -545,6 +567,9 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
             put_tagged(p.ovf + (size_t)w * kOvfWords + (e - kRecEntries), cval, tagB);
           }
         }
+        // the mask words are the sentinel the readers poll (stored after the
+        // entries; a reader that still finds an entry without its tag polls
+        // that entry)
         if (lane < 2 * kRep) {
           const int rp = lane >> 1;
           put_tagged_u32(p.rec + (size_t)rp * p.rec_stride + (size_t)(lane & 1) * kRecRow + w,
@@ -555,73 +580,18 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
 
       // ---------------- exchange B: every workgroup's record (one thread each).
       // Records are word-major, so one load instruction of a wave reads the
-      // same word of 64 records from a few cache lines.  One polling loop
-      // takes the two mask words and the first kSpecE entries; entries past
-      // those (a record with more selected neurons) are read afterwards.
+      // same word of 64 records from a few cache lines.  Only the two mask
+      // words (stored after the entries) are polled; the entries are read
+      // once, together with their V rows, in v_record.
       bool okB = true;
       uint64_t Mg = 0;
-      float cspec[kSpecE];  // this thread's record: its first kSpecE gated values
-      {
-        const int gg = tid;
-        const bool has = gg < G;
-        const uint64_t* rp = fresh(p.rec + (size_t)g.rep * p.rec_stride) + (has ? gg : 0);
-        constexpr int NW = 2 + kSpecE;
-        float val[NW];
-        bool got[NW];
-#pragma unroll
-        for (int k = 0; k < NW; ++k) {
-          got[k] = !has;
-          val[k] = 0.f;
-        }
-        int n = has ? -1 : 0;  // entries announced by the masks (-1: not seen yet)
-        // two polling rounds in flight (see gather_tagged2)
-        uint64_t ra[NW], rb[NW];
-        auto issue = [&](uint64_t (&r)[NW]) {
-#pragma unroll
-          for (int k = 0; k < NW; ++k) r[k] = get_word(rp + (size_t)k * kRecRow);
-        };
-        auto check = [&](const uint64_t (&r)[NW]) {
-#pragma unroll
-          for (int k = 0; k < NW; ++k) {
-            if (!got[k] && (uint32_t)(r[k] >> 32) == tagB) {
-              val[k] = __uint_as_float((uint32_t)r[k]);
-              got[k] = true;
-            }
-          }
-          if (n < 0 && got[0] && got[1])
-            n = __builtin_popcountll(((uint64_t)__float_as_uint(val[1]) << 32) | __float_as_uint(val[0]));
-          bool all = got[0] && got[1];
-#pragma unroll
-          for (int k = 2; k < NW; ++k) all = all && (got[k] || (n >= 0 && k - 2 >= n));
-          return all;
-        };
-        issue(ra);
-        for (uint32_t spin = 0;; spin += 2) {
-          issue(rb);
-          if (check(ra)) break;
-          issue(ra);
-          if (check(rb)) break;
-          if (spin > S.spin_limit || ((spin & 1022) == 1022 && get_word(p.hdr + 1) == S.fmark)) {
-            okB = false;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        if (has && okB) Mg = ((uint64_t)__float_as_uint(val[1]) << 32) | __float_as_uint(val[0]);
-#pragma unroll
-        for (int k = 0; k < kSpecE; ++k) cspec[k] = val[2 + k];
-        if (okB && n > kSpecE) {
-          constexpr int NR = kRecEntries - kSpecE;
-          const uint64_t* pe[NR];
-#pragma unroll
-          for (int k = 0; k < NR; ++k) pe[k] = kSpecE + k < n ? rp + (size_t)(2 + kSpecE + k) * kRecRow : nullptr;
-          float ev[NR];
-          okB = gather_tagged<NR>(pe, tagB, ev, p.hdr, S.fmark, S.spin_limit);
-#pragma unroll
-          for (int k = 0; k < NR; ++k)
-            if (kSpecE + k < n) S.t.stage[gg][kSpecE + k] = ev[k];
-        }
-        if (has) S.cnt[gg] = okB ? __builtin_popcountll(Mg) : 0;
+      const uint64_t* recp = fresh(p.rec + (size_t)g.rep * p.rec_stride) + (tid < G ? tid : 0);
+      if (tid < G) {
+        const uint64_t* mp[2] = {recp, recp + kRecRow};
+        float mv[2];
+        okB = gather_tagged2<2>(mp, tagB, mv, p.hdr, S.fmark, S.spin_limit);
+        if (okB) Mg = ((uint64_t)__float_as_uint(mv[1]) << 32) | __float_as_uint(mv[0]);
+        S.cnt[tid] = okB ? __builtin_popcountll(Mg) : 0;
       }
       if (!okB) S.fail = 1;
 
@@ -636,9 +606,9 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         bool okV = true;
         if (tid < G && okB) {
           if (g.nch > 1)
-            okV = v_record<W, 2>(p, S, vbase, vrow, Mg, nb_rec, cspec, tid, tagB, acc);
+            okV = v_record<W, 2>(p, S, vbase, vrow, Mg, nb_rec, recp, tid, tagB, acc);
           else
-            okV = v_record<W, 1>(p, S, vbase, vrow, Mg, nb_rec, cspec, tid, tagB, acc);
+            okV = v_record<W, 1>(p, S, vbase, vrow, Mg, nb_rec, recp, tid, tagB, acc);
         }
         if (!okV) S.fail = 1;
         int col;
@@ -766,14 +736,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
   g.T = p.T;
   g.n0 = own_first(g.w, g.d_ff, g.G);
   g.nown = own_first(g.w + 1, g.d_ff, g.G) - g.n0;
-  // column owner index: the workgroups of one XCD (w = x + 8j) own one
-  // contiguous range of columns, so each V row segment is read once per XCD
-  const int o = (g.G % 8 == 0) ? (g.w & 7) * (g.G / 8) + (g.w >> 3) : g.w;
-  const int vch = g.d_model / CN;  // 16-byte chunks per V row
-  g.ch0 = (int)((int64_t)o * vch / g.G);
-  g.nch = (int)((int64_t)(o + 1) * vch / g.G) - g.ch0;
-  g.c0 = g.ch0 * CN;
-  g.ncol = g.nch * CN;
+  col_range(g.w, g.G, g.d_model, CN, g.c0, g.ncol);
+  g.ch0 = g.c0 / CN;
+  g.nch = g.ncol / CN;
   g.CK = g.r / CN;
   g.K2C = (g.d_model - g.r) / CN;
   g.TC = g.nown * g.CK;
