@@ -93,11 +93,12 @@ struct DecShared {
   float colpart[4][16];              // per-wave sums of the owned columns
   float wred[8];
   float theta;
-  uint64_t candmask;
   int ntot, fail;
   uint32_t tag0;
   uint32_t spin_limit;  // polling rounds a wait may take
   uint32_t poison;      // XORed into the tag exchange A waits for (nonzero: the test hook's forced failure)
+  uint32_t aflag;       // layer key (token * layers + layer + 1) whose theta is in S.theta
+  uint32_t dotcnt;      // candidate K2 dot waves done (3 per layer)
   uint64_t fmark;       // tag0 + 1: the failure mark of this call
 };
 
@@ -129,10 +130,32 @@ __device__ __forceinline__ void col_range(int wg, int G, int d_model, int cn, in
 
 // Both roles execute exactly the same sequence of workgroup barriers:
 //   per token:  1 (input loaded) [+2 when the input needs normalising]
-//   per layer:  2 per K1 tile, then A, S, [T1, T2: workgroup 0, when a
-//               trace is asked for], V, and either Y (last layer) or C;
-//               the failure flag is read after A, V and C.
+//   per layer:  2 per K1 tile, then E, [T1, T2: workgroup 0, when a trace
+//               is asked for], V, and either Y (last layer) or C; the
+//               failure flag is read after E, V and C.
+// Inside a layer the waves also signal each other through LDS flags (theta
+// known, candidate K2 dots done), which the waves that wait on them poll
+// with a bound.
 __device__ __forceinline__ void bar() { __syncthreads(); }
+
+// Wait (bounded) until the LDS word *w reaches v; false on timeout.
+__device__ __forceinline__ bool lds_wait_ge(const uint32_t* w, uint32_t v) {
+  bool ok = true;
+  for (uint32_t sp = 0; __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < v; ++sp) {
+    if (sp > (1u << 22)) {
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  return ok;
+}
+// Publish v in the LDS word *w after this wave's earlier LDS writes.
+__device__ __forceinline__ void lds_signal(uint32_t* w, uint32_t v) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 
 
@@ -286,10 +309,11 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
         reduce_tile(g, S, tile, lane, wv, qs);
         bar();
       }
-      bar();  // A
-      if (S.fail) return;
+      // the next slab streams from the moment theta is known
+      lds_wait_ge(&S.aflag, (uint32_t)(t * g.L + l + 1));
       prefetch_part(t, l, 0, kDecMaxC);
-      bar();  // S
+      bar();  // E
+      if (S.fail) return;
       if (trace_here) {
         bar();  // T1
         bar();  // T2
@@ -467,6 +491,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
 
       const bool own = lane < g.nown;
       const float hj = own ? S.h[lane] : 0.f;
+      const uint32_t lkey = (uint32_t)(t * g.L + l + 1);  // this layer's value of the LDS flags
       if (wv == 0) {
         // ---------------- exchange A: per-workgroup (mean, M2) -> theta
         const float mean_w = wave_sum_dpp(hj) / (float)g.nown;
@@ -503,10 +528,24 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           s2 += ngk[k] > 0.f ? vals[2 * k + 1] + ngk[k] * d * d : 0.f;
         }
         const float m2 = wave_sum_dpp(s2);
-        if (lane == 0) S.theta = mu + sqrtf(m2 / (float)g.d_ff) * p.z;
+        const float theta = mu + sqrtf(m2 / (float)g.d_ff) * p.z;
         if (__builtin_amdgcn_ballot_w64(!ok) != 0 && lane == 0) {
           S.fail = 1;
           raise_failure(p.hdr, S.fmark);
+        }
+        if (lane == 0) {
+          S.theta = theta;
+          lds_signal(&S.aflag, lkey);
+        }
+        // ---------------- the selection mask goes out as soon as theta is
+        // known; it is the word the readers of exchange B poll, and the gated
+        // values follow from wave 1 once the candidates' K2 dots are done (a
+        // reader that finds an entry without its tag polls it)
+        const uint64_t M = __builtin_amdgcn_ballot_w64(own && hj > theta);
+        if (lane < 2 * kRep) {
+          const int rp = lane >> 1;
+          put_tagged_u32(p.rec + (size_t)rp * p.rec_stride + (size_t)(lane & 1) * kRecRow + w,
+                         (lane & 1) ? (uint32_t)(M >> 32) : (uint32_t)M, tagB);
         }
       } else {
         // ---------------- waves 1..3, meanwhile: K2 dots of the top candidates.
@@ -519,7 +558,6 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         }
         const bool isc = own && rank < kCand;
         const uint64_t cmask = __builtin_amdgcn_ballot_w64(isc);
-        if (wv == 1 && lane == 0) S.candmask = cmask;
         const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cmask, 0));
         // this wave's candidates: positions wv-1, wv+2, wv+5, wv+8, one per
         // row of 16 lanes
@@ -537,69 +575,68 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
                                           lane & 15);
           if ((lane & 15) == 0 && jm >= 0) S.g[jm] = d * qs;
         }
-      }
-      bar();  // A
-      if (S.fail) {
-        fail_out();
-        return;
-      }
-      const float theta = S.theta;
-
-      // ---------------- selection, gated values, publish the record
-      if (wv == 0) {
-        const bool on = own && hj > theta;
-        const uint64_t M = __builtin_amdgcn_ballot_w64(on);
-        uint64_t miss = M & ~S.candmask;
-        while (miss) {  // selected neurons outside the candidates (rare)
-          const int j = __builtin_ctzll(miss);
-          miss &= miss - 1;
-          const float d = k2_dot<W>(k2base + (size_t)j * k2row, S.q + g.r, g.K2C, lane);
-          if (lane == 0) S.g[j] = d * qs;
+        if (lane == 0) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __hip_atomic_fetch_add(&S.dotcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        const float cval = on ? gelu_tanh(hj - theta) * S.g[lane < 64 ? lane : 0] : 0.f;
-        const int e = __builtin_amdgcn_mbcnt_hi((uint32_t)(M >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)M, 0));
-        if (on) {
-          if (e < kRecEntries) {
+        if (wv == 1) {
+          // ---------------- gated values of the selected neurons, published
+          // once theta and every candidate's K2 dot are known
+          const bool okw = lds_wait_ge(&S.dotcnt, 3 * lkey) && lds_wait_ge(&S.aflag, lkey);
+          if (!okw && lane == 0) S.fail = 1;
+          const float theta = S.theta;
+          const bool on = own && hj > theta;
+          const uint64_t M = __builtin_amdgcn_ballot_w64(on);
+          uint64_t miss = M & ~cmask;
+          while (miss) {  // selected neurons outside the candidates (rare)
+            const int j = __builtin_ctzll(miss);
+            miss &= miss - 1;
+            const float d = k2_dot<W>(k2base + (size_t)j * k2row, S.q + g.r, g.K2C, lane);
+            if (lane == 0) S.g[j] = d * qs;
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          const float cval = on ? gelu_tanh(hj - theta) * S.g[lane < 64 ? lane : 0] : 0.f;
+          const int e = __builtin_amdgcn_mbcnt_hi((uint32_t)(M >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)M, 0));
+          if (on) {
+            if (e < kRecEntries) {
 #pragma unroll
-            for (int rp = 0; rp < kRep; ++rp)
-              put_tagged(p.rec + (size_t)rp * p.rec_stride + (size_t)(2 + e) * kRecRow + w, cval, tagB);
-          } else {
-            put_tagged(p.ovf + (size_t)w * kOvfWords + (e - kRecEntries), cval, tagB);
+              for (int rp = 0; rp < kRep; ++rp)
+                put_tagged(p.rec + (size_t)rp * p.rec_stride + (size_t)(2 + e) * kRecRow + w, cval, tagB);
+            } else {
+              put_tagged(p.ovf + (size_t)w * kOvfWords + (e - kRecEntries), cval, tagB);
+            }
           }
         }
-        // the mask words are the sentinel the readers poll (stored after the
-        // entries; a reader that still finds an entry without its tag polls
-        // that entry)
-        if (lane < 2 * kRep) {
-          const int rp = lane >> 1;
-          put_tagged_u32(p.rec + (size_t)rp * p.rec_stride + (size_t)(lane & 1) * kRecRow + w,
-                         (lane & 1) ? (uint32_t)(M >> 32) : (uint32_t)M, tagB);
-        }
       }
-      bar();  // S
-
-      // ---------------- exchange B: every workgroup's record (one thread each).
-      // Records are word-major, so one load instruction of a wave reads the
-      // same word of 64 records from a few cache lines.  Only the two mask
-      // words (stored after the entries) are polled; the entries are read
-      // once, together with their V rows, in v_record.
+      // ---------------- exchange B: every workgroup's selection mask (thread
+      // tid polls record tid's two mask words; records are word-major, so one
+      // load instruction of a wave reads the same word of 64 records from a
+      // few cache lines).  The entries are read once, with their V rows, in
+      // v_record.
       bool okB = true;
       uint64_t Mg = 0;
-      const uint64_t* recp = fresh(p.rec + (size_t)g.rep * p.rec_stride) + (tid < G ? tid : 0);
       if (tid < G) {
-        const uint64_t* mp[2] = {recp, recp + kRecRow};
+        const uint64_t* recm = fresh(p.rec + (size_t)g.rep * p.rec_stride) + tid;
+        const uint64_t* mp[2] = {recm, recm + kRecRow};
         float mv[2];
         okB = gather_tagged2<2>(mp, tagB, mv, p.hdr, S.fmark, S.spin_limit);
         if (okB) Mg = ((uint64_t)__float_as_uint(mv[1]) << 32) | __float_as_uint(mv[0]);
         S.cnt[tid] = okB ? __builtin_popcountll(Mg) : 0;
       }
       if (!okB) S.fail = 1;
+      bar();  // E
+      if (S.fail) {
+        fail_out();
+        return;
+      }
+      const float theta = S.theta;
 
       // ---------------- V: the owned columns of y.  Thread gg takes the
       // selected neurons of record gg; column sums then run over lanes and
       // waves in a fixed order.
       {
         const char* vbase = (const char*)tab_v[l] + (size_t)g.ch0 * 16;
+        const uint64_t* recp = fresh(p.rec + (size_t)g.rep * p.rec_stride) + (tid < G ? tid : 0);
         float acc[2 * CN];
 #pragma unroll
         for (int i = 0; i < 2 * CN; ++i) acc[i] = 0.f;
@@ -756,6 +793,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
     S.spin_limit = lim ? (uint32_t)lim : p.spin_limit;
     S.poison = lim ? 0x80000000u : 0u;
     S.fail = 0;
+    S.aflag = 0;
+    S.dotcnt = 0;
   }
   __syncthreads();
   if (threadIdx.x < kWorkers) {
