@@ -130,9 +130,9 @@ __device__ __forceinline__ void col_range(int wg, int G, int d_model, int cn, in
 
 // Both roles execute exactly the same sequence of workgroup barriers:
 //   per token:  1 (input loaded) [+2 when the input needs normalising]
-//   per layer:  2 per K1 tile, then E, [T1, T2: workgroup 0, when a trace
-//               is asked for], V, and either Y (last layer) or C; the
-//               failure flag is read after E, V and C.
+//   per layer:  2 per K1 tile, then [T1, T2: workgroup 0, when a trace is
+//               asked for], V, and either Y (last layer) or C; the failure
+//               flag is read after V and C.
 // Inside a layer the waves also signal each other through LDS flags (theta
 // known, candidate K2 dots done), which the waves that wait on them poll
 // with a bound.
@@ -198,7 +198,7 @@ __device__ __forceinline__ void reduce_tile(const DecGeo& g, DecShared& S, int t
 
 // ---------------------------------------------------------------- streamer role
 template <typename W>
-__device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1, const DecGeo& g, DecShared& S) {
+__device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1, const void* const* tab_v, const DecGeo& g, DecShared& S) {
   constexpr int CN = Chunk<W>::N;
   const int sid = threadIdx.x - kWorkers, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int TILE = kStreamers * kDecMaxC;
@@ -242,6 +242,7 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
   const bool qreg = g.ntile == 1 && (kStreamers * kQPer) % g.CK == 0;
   const bool trace_here = g.w == 0 && (p.tr_idx || p.tr_counts || p.tr_theta);
   load_tile(0, 0);
+  uint32_t vsink = 0;  // the V touches' loaded words (never used)
   float qs = 1.f;  // scale of the q held in LDS (its RMS normalisation, applied to the products)
   for (int t = 0; t < g.T; ++t) {
     qs = 1.f;
@@ -279,6 +280,7 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
           S.u.part[c < g.TC ? c : TILE] = acc;
           if (m % 3 == 2) __builtin_amdgcn_sched_barrier(0);  // keep few chunks' conversions live
         }
+        asm volatile("" :: "v"(vsink));  // keeps the V touches (complete long before this point)
         bar();
         reduce_tile(g, S, 0, lane, wv, qs);
         bar();
@@ -312,8 +314,23 @@ __device__ void decode_streamer(const DecodeParams& p, const void* const* tab_k1
       // the next slab streams from the moment theta is known
       lds_wait_ge(&S.aflag, (uint32_t)(t * g.L + l + 1));
       prefetch_part(t, l, 0, kDecMaxC);
-      bar();  // E
-      if (S.fail) return;
+      // ... and the V rows of this workgroup's selected neurons are touched
+      // (one 4-byte load per 128-byte line), so that the column owners of
+      // every XCD find them in the caches when the selection lists arrive
+      {
+        const float th = S.theta;
+        const bool on = lane < g.nown && S.h[lane < 64 ? lane : 0] > th;
+        uint64_t M = __builtin_amdgcn_ballot_w64(on);
+        const int sw = wv - 4;
+        for (int k = 0; M; ++k) {
+          const int j = __builtin_ctzll(M);
+          M &= M - 1;
+          if ((k & 3) != sw) continue;
+          const char* row = (const char*)tab_v[l] + (size_t)(g.n0 + j) * (size_t)g.d_model * sizeof(W);
+          const int lines = (g.d_model * (int)sizeof(W) + 127) / 128;
+          for (int c = lane; c < lines; c += 64) vsink ^= *reinterpret_cast<const uint32_t*>(row + (size_t)c * 128);
+        }
+      }
       if (trace_here) {
         bar();  // T1
         bar();  // T2
@@ -624,12 +641,6 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         S.cnt[tid] = okB ? __builtin_popcountll(Mg) : 0;
       }
       if (!okB) S.fail = 1;
-      bar();  // E
-      if (S.fail) {
-        fail_out();
-        return;
-      }
-      const float theta = S.theta;
 
       // ---------------- V: the owned columns of y.  Thread gg takes the
       // selected neurons of record gg; column sums then run over lanes and
@@ -694,7 +705,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         }
         if (tid == 0) {
           if (p.tr_counts) p.tr_counts[trow] = S.ntot;
-          if (p.tr_theta) p.tr_theta[trow] = theta;
+          if (p.tr_theta) p.tr_theta[trow] = S.theta;
         }
       }
       bar();  // V
@@ -807,7 +818,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
       __hip_atomic_store(p.hdr, (uint64_t)(S.tag0 + (uint32_t)g.T * (uint32_t)(3 * g.L - 1)), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    decode_streamer<W>(p, kp->k1t, g, S);
+    decode_streamer<W>(p, kp->k1t, kp->v, g, S);
   }
 }
 
