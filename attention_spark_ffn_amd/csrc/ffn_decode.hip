@@ -46,7 +46,7 @@ constexpr int kDecMaxC = 21;   // K1 chunks (16 B) held per streamer thread (a 3
 constexpr int kStreamers = 256;
 constexpr int kWorkers = 256;
 constexpr int kRep = 8;        // replicas of every broadcast record (one per XCD)
-constexpr int kCand = 12;      // owned neurons whose K2 dot is formed before theta is known
+constexpr int kCand = 10;      // owned neurons whose K2 dot is formed before theta is known
 constexpr int kRecWords = 16;  // selected-list record: 2 mask words + 14 entries
 constexpr int kRecEntries = kRecWords - 2;
 constexpr int kRecRow = 256;   // records are word-major: word k of workgroup w at k * kRecRow + w
@@ -576,9 +576,10 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         const bool isc = own && rank < kCand;
         const uint64_t cmask = __builtin_amdgcn_ballot_w64(isc);
         const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cmask, 0));
-        // this wave's candidates: positions wv-1, wv+2, wv+5, wv+8, one per
-        // row of 16 lanes
-        static_assert(kCand == 12, "three waves of four 16-lane rows");
+        // this wave's candidates: positions wv-1, wv+2, wv+5, wv+8 (those below
+        // kCand), one per row of 16 lanes; a row without a candidate repeats
+        // the wave's first row (its loads hit the caches) and stores nothing
+        static_assert(kCand <= 12, "three waves of four 16-lane rows");
         int jsel[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
