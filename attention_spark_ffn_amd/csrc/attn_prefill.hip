@@ -308,8 +308,10 @@ struct FusedLds {
   static_assert(2 * 32 * K1S * 2 == 1024 * J1 && 2 * 32 * K2S * 2 == 1024 * J2 && 2 * HD * 64 == 1024 * JV,
                 "regions are whole jobs");
   static_assert(O_BYTES <= BUF_BYTES, "output staging fits one tile buffer");
-  static_assert(R == RC, "the score and gate chains run side by side");
+  static_assert(R == RC && K1S == K2S, "the score and gate chains of a wave pair have one shape");
 };
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // Raw buffer descriptor over `bytes` bytes from p (stride 0; word 3 as the
 // gfx9 raw buffers take it): offsets at or past `bytes` read as zeros.
@@ -532,18 +534,19 @@ __global__ __launch_bounds__(kMomentThreads) void attn_prefill_moments(const Fus
 }
 
 // Pass 2: gated weights and O.  Eight waves: for each row set and key parity
-// two waves compute the same score and gate tiles on the matrix cores, each
-// turns half of them (one 16-key half of the tile) into gated weights, the
-// two swap their halves through LDS, and each accumulates O for half of the
-// hd output dimensions (O needs every key of the tile).  Key and V^T tiles go
+// a pair of waves shares each tile: the lower one forms the scores on the
+// matrix cores and from them the selection and e^(s - M), the upper one the
+// gate products and their softplus; the two swap these (fp16, through LDS),
+// both form the gated weights of the whole tile, and each accumulates O for
+// half of the hd output dimensions (O needs every key of the tile).  Key and V^T tiles go
 // straight from memory to LDS (buffer loads with the LDS destination, 16 bytes
 // per lane; keys past the end of a head read as zeros), double-buffered: the
 // loads of step s + 1 are in flight while step s computes.
 template <int R, int RC>
 __global__ __launch_bounds__(kFusedThreads2) void attn_prefill_fused(const FusedArgs a) {
   using L = FusedLds<R, RC>;
-  constexpr int HD = L::HD, NB2 = HD / 64, KA = R / 16, KB = RC / 16;
-  constexpr int K1S = L::K1S, K2S = L::K2S, OS = L::OS;
+  constexpr int HD = L::HD, NB2 = HD / 64, KA = R / 16;
+  constexpr int K1S = L::K1S, OS = L::OS;
   constexpr int J1 = L::J1, J2 = L::J2, JV = L::JV;  // 1 KB load jobs per step
   constexpr int NW = kFusedThreads2 / 64;
   constexpr float kL2E = 1.4426950408889634f;
@@ -551,7 +554,7 @@ __global__ __launch_bounds__(kFusedThreads2) void attn_prefill_fused(const Fused
   // known not to alias the reads of the other
   __shared__ alignas(16) char buf0[L::BUF_BYTES];
   __shared__ alignas(16) char buf1[L::BUF_BYTES];
-  __shared__ alignas(16) bf16_t xch[NW][64 * 8];  // per wave: its half of the gated weights
+  __shared__ alignas(16) _Float16 xch[NW][64 * 16];  // per wave: e^(s - M) (lower) or the gates (upper)
   __shared__ float lc[2][2][2][32][2];            // [parity][half][row set][query]: l, count
   float* const om = reinterpret_cast<float*>(buf0);
 
@@ -599,12 +602,9 @@ __global__ __launch_bounds__(kFusedThreads2) void attn_prefill_fused(const Fused
         if (wv + NW * i < JV) load_lds16(rv, buf + L::V_OFF + 1024 * (wv + NW * i), (uint32_t)(ov[i] + svt));
     };
 
-    bf16x8 qa[KA], qg[KB];
-    {
-      const bf16_t* qrow = a.q + ((size_t)min(tq, T - 1) * Hq + h) * HD + 8 * hl;
-      load_qfrag(qa, qrow);
-      load_qfrag(qg, qrow + R);
-    }
+    // the lower wave of a pair holds q[:r] (scores), the upper one q[r:] (gates)
+    bf16x8 qf[KA];
+    load_qfrag(qf, a.q + ((size_t)min(tq, T - 1) * Hq + h) * HD + (half ? R : 0) + 8 * hl);
     float th = INFINITY, mxs = 0.f;
     if (live && tq < T) {
       th = a.rth[(size_t)h * T + tq];
@@ -625,64 +625,75 @@ __global__ __launch_bounds__(kFusedThreads2) void attn_prefill_fused(const Fused
       const int kt = F.tile<2>(s, par);
       const bool act = live && kt >= 0 && kt <= diag;
       if (act) {
-        // the upper-half wave reads key rows col ^ 16: its registers 0..7 then
-        // hold keys 16 + 8 hl + j, the lower-half wave's keys 8 hl + j
-        const int krow = col ^ (16 * half);
-        const bf16_t* k1t = reinterpret_cast<const bf16_t*>(cur) + par * 32 * K1S + krow * K1S + 8 * hl;
-        const bf16_t* k2t = reinterpret_cast<const bf16_t*>(cur + L::K2_OFF) + par * 32 * K2S + krow * K2S + 8 * hl;
-        // S^T and G^T chains interleaved; fragments read in groups of four
-        f32x16 sc, gc;
+        // S^T (lower wave) or G^T (upper wave) of the tile: register i of lane
+        // half hl holds key 16 (i / 8) + 8 hl + i % 8; fragments read in pairs
+        const bf16_t* kt_ = reinterpret_cast<const bf16_t*>(cur + (half ? L::K2_OFF : 0)) + par * 32 * K1S +
+                            col * K1S + 8 * hl;
+        // (one accumulation chain in K order: the order of tile_scores in the
+        // moments pass, so both passes form the same scores bit for bit)
+        f32x16 acc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = gc[i] = 0.f;
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
         for (int k0 = 0; k0 < KA; k0 += 2) {
-          bf16x8 f1[2], f2[2];
+          bf16x8 f[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            f1[u] = *reinterpret_cast<const bf16x8*>(k1t + 16 * (k0 + u));
-            f2[u] = *reinterpret_cast<const bf16x8*>(k2t + 16 * (k0 + u));
-          }
+          for (int u = 0; u < 2; ++u) f[u] = *reinterpret_cast<const bf16x8*>(kt_ + 16 * (k0 + u));
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[u], qa[k0 + u], sc, 0, 0, 0);
-            gc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2[u], qg[k0 + u], gc, 0, 0, 0);
-          }
+          for (int u = 0; u < 2; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[u], qf[k0 + u], acc, 0, 0, 0);
         }
-        // this wave's half of the tile: registers 0..7, keys 16 half + 8 hl + j
-        auto weights = [&](auto dc) {
-          constexpr bool DIAG = decltype(dc)::value;
-          bf16x8 pw;
-          uint32_t bits = 0;
+        f16x8 hv[2];
+        if (half == 0) {
+          auto exps = [&](auto dc) {
+            constexpr bool DIAG = decltype(dc)::value;
+            uint32_t bits = 0;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const bool sel = (!DIAG || 32 * kt + 16 * half + 8 * hl + j <= tq) && sc[j] > th;
-            const float e = sel ? __builtin_amdgcn_exp2f(fmaf(sc[j], kL2E, -mxs)) : 0.f;
-            lsum += e;
-            cnt += sel ? 1 : 0;
-            bits |= sel ? 1u << j : 0u;
-            pw[j] = (__bf16)(e * softplus_gate(gc[j]));
-          }
-          *reinterpret_cast<bf16x8*>(&xch[wv][8 * lane]) = pw;
-          // keys 32 kt + 16 half + 8 hl + j: byte 4 kt + 2 half + hl of the row's bitmask
-          if (a.sel && tq < T) a.sel[((size_t)tq * Hq + h) * a.selb + 4 * kt + 2 * half + hl] = (uint8_t)bits;
-        };
-        if (kt < diag)
-          weights(std::integral_constant<bool, false>{});
-        else
-          weights(std::integral_constant<bool, true>{});
+            for (int i = 0; i < 16; ++i) {
+              const int key = 32 * kt + 16 * (i >> 3) + 8 * hl + (i & 7);
+              const bool sel = (!DIAG || key <= tq) && acc[i] > th;
+              const float e = sel ? __builtin_amdgcn_exp2f(fmaf(acc[i], kL2E, -mxs)) : 0.f;
+              lsum += e;
+              cnt += sel ? 1 : 0;
+              bits |= sel ? 1u << i : 0u;
+              hv[i >> 3][i & 7] = (_Float16)e;
+            }
+            // keys 32 kt + 16 u + 8 hl + j: byte 4 kt + 2 u + hl of the row's bitmask
+            if (a.sel && tq < T) {
+              uint8_t* sb = a.sel + ((size_t)tq * Hq + h) * a.selb + 4 * kt + hl;
+              sb[0] = (uint8_t)(bits & 0xFFu);
+              sb[2] = (uint8_t)(bits >> 8);
+            }
+          };
+          if (kt < diag)
+            exps(std::integral_constant<bool, false>{});
+          else
+            exps(std::integral_constant<bool, true>{});
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) hv[i >> 3][i & 7] = (_Float16)softplus_gate(acc[i]);
+        }
+        *reinterpret_cast<f16x8*>(&xch[wv][16 * lane]) = hv[0];
+        *reinterpret_cast<f16x8*>(&xch[wv][16 * lane + 8]) = hv[1];
       }
-      __syncthreads();  // both halves of every tile are in LDS
+      __syncthreads();  // both halves of every pair are in LDS
       if (act) {
-        const bf16x8 pp = *reinterpret_cast<const bf16x8*>(&xch[partner][8 * lane]);
-        const bf16x8 p0 = half ? pp : *reinterpret_cast<const bf16x8*>(&xch[wv][8 * lane]);
-        const bf16x8 p1 = half ? *reinterpret_cast<const bf16x8*>(&xch[wv][8 * lane]) : pp;
+        // gated weights of the whole tile, the same in both waves of the pair
+        // (the product of the same two fp16 values)
+        bf16x8 pw[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f16x8 x = *reinterpret_cast<const f16x8*>(&xch[wv][16 * lane + 8 * u]);
+          const f16x8 y = *reinterpret_cast<const f16x8*>(&xch[partner][16 * lane + 8 * u]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pw[u][j] = (__bf16)((float)x[j] * (float)y[j]);
+        }
         const char* vtt = cur + L::V_OFF + par * HD * 64 + half * (HD / 2) * 64;
 #pragma unroll
         for (int b = 0; b < NB2; ++b) {
           oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *reinterpret_cast<const bf16x8*>(vtt + b * 2048 + vfrag0), p0, oacc[b], 0, 0, 0);
+              *reinterpret_cast<const bf16x8*>(vtt + b * 2048 + vfrag0), pw[0], oacc[b], 0, 0, 0);
           oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *reinterpret_cast<const bf16x8*>(vtt + b * 2048 + vfrag1), p1, oacc[b], 0, 0, 0);
+              *reinterpret_cast<const bf16x8*>(vtt + b * 2048 + vfrag1), pw[1], oacc[b], 0, 0, 0);
         }
       }
     };
