@@ -822,8 +822,19 @@ __device__ __forceinline__ void octet_colsum(float (&v)[NV], int lane) {
   octet_step<8, NV / 4, NV>(v, lane);
 }
 
-template <typename W, int BM>
-__global__ __launch_bounds__(kBv2Threads) void bv2(const BatchArgs a, int G2, int S, float* __restrict__ P2) {
+// FOLD (the launches whose predictor-and-gate kernel is bfused): no breduce.
+// Each workgroup publishes its slice sums as tagged words at
+// X2[block x S + slice][token][column of the block] (the layer's tag, which
+// bfused has just stored in the workspace header), and the block's last slice
+// -- dispatched after the others, so it only ever waits on workgroups already
+// started -- adds the S slices in the same fixed order as breduce, writes y
+// and each token's sum of squares over the block's columns to ssp[block].
+// Every wait is bounded; on timeout the call is marked failed and the block's
+// outputs are NaN.
+constexpr int kFoldCols = 64;  // columns of a column block (eight 16-byte bf16 chunks)
+template <typename W, int BM, bool FOLD>
+__global__ __launch_bounds__(kBv2Threads) void bv2(const BatchArgs a, int G2, int S, float* __restrict__ P2,
+                                                   uint64_t* hdr, uint64_t* X2, int layer) {
   constexpr int CN = Chunk<W>::N;
   constexpr int NV = BM * CN < 8 ? 8 : BM * CN;  // accumulators per lane (padded to eight)
   constexpr int NWV = kBv2Threads / 64;
@@ -927,12 +938,105 @@ __global__ __launch_bounds__(kBv2Threads) void bv2(const BatchArgs a, int G2, in
 #pragma unroll
   for (int j = 0; j < NV / 8; ++j) part[wv][c][(lane >> 3) * (NV / 8) + j] = acc[j];
   __syncthreads();
-  for (int t = tid; t < 8 * NV; t += kBv2Threads) {
-    const int cc = t / NV, idx = t % NV, b = idx / CN, i = idx % CN, gcc = cb * 8 + cc;
-    float sum = 0.f;
+  if constexpr (!FOLD) {
+    for (int t = tid; t < 8 * NV; t += kBv2Threads) {
+      const int cc = t / NV, idx = t % NV, b = idx / CN, i = idx % CN, gcc = cb * 8 + cc;
+      float sum = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < NWV; ++w2) sum += part[w2][cc][idx];
-    if (b < B && gcc < nchunks) P2[((size_t)sp * B + b) * d + (size_t)gcc * CN + i] = sum;
+      for (int w2 = 0; w2 < NWV; ++w2) sum += part[w2][cc][idx];
+      if (b < B && gcc < nchunks) P2[((size_t)sp * B + b) * d + (size_t)gcc * CN + i] = sum;
+    }
+  } else {
+    static_assert(!FOLD || 8 * CN == kFoldCols, "the folded reduction takes 16-byte chunks of eight bf16 values");
+    __shared__ float own[BM * kFoldCols];
+    __shared__ uint32_t s_tag, s_spin;
+    __shared__ uint64_t s_fmark;
+    if (tid == 0) {
+      s_tag = (uint32_t)get_word(hdr);
+      s_fmark = (uint64_t)(s_tag - (uint32_t)layer);
+      const uint64_t lim = get_word(hdr + 3);  // the host-set test hook bounds every wait
+      s_spin = lim ? (uint32_t)lim : (1u << 22);
+    }
+    __syncthreads();
+    const uint32_t tag = s_tag;
+    const bool red = sp == S - 1;
+    uint64_t* mine = X2 + (size_t)blockIdx.x * (BM * kFoldCols);
+    for (int t = tid; t < 8 * NV; t += kBv2Threads) {
+      const int cc = t / NV, idx = t % NV, b = idx / CN, i = idx % CN;
+      float sum = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NWV; ++w2) sum += part[w2][cc][idx];
+      if (b < B) {
+        if (red)
+          own[b * kFoldCols + cc * CN + i] = sum;
+        else
+          put_tagged(mine + b * kFoldCols + cc * CN + i, sum, tag);
+      }
+    }
+    if (!red) return;
+    __syncthreads();
+    // output o = token b (o / 64), column o % 64 of the block; a thread takes
+    // o = tid + 256 j (j < NO), so each wave's sums of squares belong to one
+    // token per j.  The words of up to KP slices of all a thread's outputs
+    // are polled in one round.
+    constexpr int NO = (BM * kFoldCols + kBv2Threads - 1) / kBv2Threads;
+    constexpr int KP = 16;
+    const uint64_t* blk = X2 + (size_t)cb * S * (BM * kFoldCols);
+    float y[NO];
+    bool okall = true;
+#pragma unroll
+    for (int j = 0; j < NO; ++j) y[j] = 0.f;
+    const size_t sstride = (size_t)BM * kFoldCols;  // words between the slices of a block
+    static_assert(NO * KP <= 32, "one pending bit per polled word");
+    for (int s0 = 0; s0 < S - 1 && okall; s0 += KP) {
+      // bit j KP + k: slice s0 + k of output j still without the layer's tag
+      uint32_t pend = 0;
+#pragma unroll
+      for (int j = 0; j < NO; ++j) {
+        const int o = tid + kBv2Threads * j;
+        if (o < BM * kFoldCols && o / kFoldCols < B)
+#pragma unroll
+          for (int k = 0; k < KP; ++k)
+            if (s0 + k < S - 1) pend |= 1u << (j * KP + k);
+      }
+      const uint32_t want = pend;
+      uint32_t v[NO * KP];
+      for (uint32_t spin = 0; pend; ++spin) {
+        uint64_t wvv[NO * KP];
+#pragma unroll
+        for (int i = 0; i < NO * KP; ++i)
+          if ((pend >> i) & 1u)
+            wvv[i] = get_word(blk + (size_t)(s0 + i % KP) * sstride + tid + kBv2Threads * (i / KP));
+#pragma unroll
+        for (int i = 0; i < NO * KP; ++i)
+          if (((pend >> i) & 1u) && (uint32_t)(wvv[i] >> 32) == tag) {
+            v[i] = (uint32_t)wvv[i];
+            pend &= ~(1u << i);
+          }
+        if (!pend) break;
+        if (spin > s_spin || ((spin & 1023) == 1023 && get_word(hdr + 1) == s_fmark)) {
+          okall = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int i = 0; i < NO * KP; ++i)  // slices in ascending order, as breduce
+        if ((want >> i) & 1u) y[i / KP] += __uint_as_float(v[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+      const int o = tid + kBv2Threads * j;
+      const int b = o / kFoldCols, gcol = cb * kFoldCols + o % kFoldCols;
+      const bool valid = o < BM * kFoldCols && b < B;
+      float yo = valid ? y[j] + own[o] : 0.f;
+      if (!okall) yo = __builtin_nanf("");
+      if (valid && gcol < d) a.yout[(size_t)b * d + gcol] = yo;
+      float ss = valid && gcol < d ? yo * yo : 0.f;
+      ss = wave_sum_dpp(ss);
+      if (lane == 0 && valid) a.ssp[(size_t)cb * BM + b] = ss;
+    }
+    if (!okall) raise_failure(hdr, s_fmark);
   }
 }
 
@@ -1268,7 +1372,7 @@ __global__ __launch_bounds__(kBThreads) void bfused(const BatchArgs a, uint64_t*
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct BatchLayout {
-  size_t H, P, scale, theta, umask, C, ybuf, ssp, P2, X, total;
+  size_t H, P, scale, theta, umask, C, ybuf, ssp, P2, X, X2, total;
   int xs_stride;  // words between the exchange replicas of bfused
 };
 
@@ -1280,6 +1384,17 @@ static int batch_groups(int64_t d_ff) {
   if (G > d_ff / 4) G = d_ff / 4 > 0 ? d_ff / 4 : 1;
   if ((d_ff + G - 1) / G > kBSlots) G = (d_ff + kBSlots - 1) / kBSlots;
   return (int)G;
+}
+
+// bv2 workgroups (column blocks x slices) whose slice sums the folded
+// reduction can hold: about two per CU plus one block's worth of rounding
+// (bfused shapes have d_model <= 2 x 1280, at most 40 column blocks).  The
+// area is sized without B or d_model, so it sits at the same place for every
+// call on a workspace and holds only tagged words.
+static int fold_blocks_cap() {
+  int cus = device_cu_count();
+  if (cus < 1) cus = 256;
+  return 2 * cus + 64;
 }
 
 static BatchLayout batch_layout(int64_t d_model, int64_t d_ff, int64_t B) {
@@ -1296,6 +1411,7 @@ static BatchLayout batch_layout(int64_t d_model, int64_t d_ff, int64_t B) {
   // (or zeros) there
   L.xs_stride = (int)round_up((size_t)2 * kBatchMax * kXRow + 64, 512);  // replicas 4 KB+ apart
   L.X = take((size_t)kXRep * L.xs_stride * 8);
+  L.X2 = take((size_t)fold_blocks_cap() * kBatchMax * kFoldCols * 8);
   L.H = take((size_t)B * d_ff * 4);
   L.P = take((size_t)G * B * 2 * 4);
   L.scale = take((size_t)B * 4);
@@ -1334,8 +1450,29 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
   constexpr bool kSmall = BM <= 1;
   const int nblocks = (nchunks + 7) / 8;      // bv2 column blocks (128-byte lines)
   const int S = bv2_slices(s.d_model, CN);    // bv2 union slices per block
+  // both products on the matrix cores in one kernel per layer, when the device
+  // holds the whole grid at once (its workgroups exchange the statistics
+  // while they run)
+  constexpr int kMaxK = 32 * kMSteps * (kBThreads / 64);
+  const bool mf1 = kMatrixOk<W> && s.r % 32 == 0 && s.r <= kMaxK;
+  bool fused = false;
+  const size_t ldsf = (size_t)BM * s.d_model * 4;
+  if (kMatrixOk<W> && mf1 && (s.d_model - s.r) % 32 == 0 && s.d_model - s.r <= kMaxK && G <= kXRow) {
+    int per_cu = 0;
+    if (hipFuncSetAttribute((const void*)bfused<BM>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsf) ==
+            hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bfused<BM>, kBThreads, ldsf) == hipSuccess &&
+        (int64_t)per_cu * device_cu_count() >= G)
+      fused = true;
+    (void)hipGetLastError();
+  }
+  // with bfused (which advances the header's tag every layer) and two or more
+  // tokens, bv2 reduces its slices itself: no breduce launch
+  const bool fold = !kSmall && fused && 8 * CN == kFoldCols && nblocks * S <= fold_blocks_cap();
   int G3;
-  if (kSmall) {
+  if (fold) {
+    G3 = nblocks;
+  } else if (kSmall) {
     G3 = device_cu_count();
     if (G3 < 1) G3 = 256;
     if (G3 > nchunks) G3 = nchunks;
@@ -1364,26 +1501,10 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
   a.ssp = (float*)(base + Lo.ssp);
   float* ybuf = (float*)(base + Lo.ybuf);
   // the predictor and K2 products on the matrix cores where the shapes allow
-  constexpr int kMaxK = 32 * kMSteps * (kBThreads / 64);
-  const bool mf1 = kMatrixOk<W> && s.r % 32 == 0 && s.r <= kMaxK;
   // (the K2 dots: at eight token slots; with fewer, the extra barrier and the
   // full-tile loads of the matrix-core form cost more than the vector units'
   // products, measured)
   const bool mf2 = kMatrixOk<W> && BM >= 8 && (s.d_model - s.r) % 32 == 0 && s.d_model - s.r <= kMaxK;
-  // both products on the matrix cores in one kernel per layer, when the device
-  // holds the whole grid at once (its workgroups exchange the statistics
-  // while they run)
-  bool fused = false;
-  const size_t ldsf = (size_t)BM * s.d_model * 4;
-  if (kMatrixOk<W> && mf1 && (s.d_model - s.r) % 32 == 0 && s.d_model - s.r <= kMaxK && G <= kXRow) {
-    int per_cu = 0;
-    if (hipFuncSetAttribute((const void*)bfused<BM>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsf) ==
-            hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bfused<BM>, kBThreads, ldsf) == hipSuccess &&
-        (int64_t)per_cu * device_cu_count() >= G)
-      fused = true;
-    (void)hipGetLastError();
-  }
   for (int l = 0; l < n_layers; ++l) {
     a.k1t = layers[l].k1t;
     a.k2t = layers[l].k2t;
@@ -1412,10 +1533,20 @@ static hipError_t launch_batched_t(const spark_ffn_shape& s, const spark_ffn_wei
     if constexpr (kSmall) {
       hipLaunchKernelGGL((bv<W, BM>), dim3(G3), dim3(kBvThreads), 0, st, a, G);
     } else {
-      hipLaunchKernelGGL((bv2<W, BM>), dim3((unsigned)(nblocks * S)), dim3(kBv2Threads), 0, st, a, G, S,
-                         (float*)(base + Lo.P2));
-      hipLaunchKernelGGL((breduce<BM>), dim3((unsigned)G3, (unsigned)B), dim3(64), 0, st, a, S,
-                         (const float*)(base + Lo.P2));
+      bool folded = false;
+      if constexpr (kMatrixOk<W>) {
+        if (fold) {
+          hipLaunchKernelGGL((bv2<W, BM, true>), dim3((unsigned)(nblocks * S)), dim3(kBv2Threads), 0, st, a, G, S,
+                             (float*)nullptr, hdr, (uint64_t*)(base + Lo.X2), l);
+          folded = true;
+        }
+      }
+      if (!folded) {
+        hipLaunchKernelGGL((bv2<W, BM, false>), dim3((unsigned)(nblocks * S)), dim3(kBv2Threads), 0, st, a, G, S,
+                           (float*)(base + Lo.P2), (uint64_t*)nullptr, (uint64_t*)nullptr, l);
+        hipLaunchKernelGGL((breduce<BM>), dim3((unsigned)G3, (unsigned)B), dim3(64), 0, st, a, S,
+                           (const float*)(base + Lo.P2));
+      }
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
