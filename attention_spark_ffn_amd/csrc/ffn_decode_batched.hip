@@ -779,7 +779,9 @@ __global__ __launch_bounds__(kBvThreads) void bv(const BatchArgs a, int G2) {
 // ---------------------------------------------------------------- bv2 + breduce (two or more tokens)
 // The V product by (column block, union slice): workgroup (cb, sp) takes the
 // 128-byte line cb of every V row it needs (eight 16-byte chunks) and the
-// union entries [sp U / S, (sp + 1) U / S).  Eight lanes read one row's line
+// union neurons of the predictor workgroups [sp G / S, (sp + 1) G / S) (their
+// masks only, placed by prefix counts: no search over the whole union).
+// Eight lanes read one row's line
 // together (lane l: row l / 8 of the wave's eight rows, chunk l % 8), so a
 // wave's load instruction covers eight whole lines, and each V row is read by
 // one workgroup per line instead of one per 16-byte chunk.  The slice sums go
@@ -787,7 +789,7 @@ __global__ __launch_bounds__(kBvThreads) void bv(const BatchArgs a, int G2) {
 // each token's sum of squares for the next layer's RMS scale.
 constexpr int kBv2Threads = 256;
 constexpr int kBv2Round = 4;      // rows per lane in flight
-constexpr int kBv2Rows = 1024;    // union entries whose neurons are resolved into LDS at a time
+constexpr int kBv2Rows = 2048;    // union entries whose neurons are resolved into LDS at a time (32 masks)
 
 // Slices per column block: about two workgroups per CU over the whole grid.
 static int bv2_slices(int64_t d_model, int cn) {
@@ -838,40 +840,18 @@ __global__ __launch_bounds__(kBv2Threads) void bv2(const BatchArgs a, int G2, in
   constexpr int CN = Chunk<W>::N;
   constexpr int NV = BM * CN < 8 ? 8 : BM * CN;  // accumulators per lane (padded to eight)
   constexpr int NWV = kBv2Threads / 64;
-  constexpr int WPT = 2048 / kBv2Threads;  // mask words per thread in the prefix count
-  __shared__ uint64_t um[2048];
-  __shared__ int pre[2049];
-  __shared__ int wtot[NWV];
+  constexpr int kGrp = kBv2Rows / 64;  // predictor workgroups (64-bit masks) resolved into LDS at a time
+  __shared__ uint64_t um[kGrp];
+  __shared__ int pre[kGrp];
+  __shared__ int s_ns;
   __shared__ int rows[kBv2Rows];
   __shared__ float part[NWV][8][NV];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int B = a.B, d = a.d_model, nchunks = d / CN;
   const int cb = blockIdx.x / S, sp = blockIdx.x % S;
-  // union masks and their exclusive prefix counts (thread t: words WPT t ..)
-  int cnt8 = 0;
-  uint64_t w8[WPT];
-#pragma unroll
-  for (int k = 0; k < WPT; ++k) {
-    const int g = WPT * tid + k;
-    w8[k] = g < G2 ? a.umask[g] : 0ull;
-    cnt8 += __builtin_popcountll(w8[k]);
-  }
-  const int incl = wave_incl_scan_dpp(cnt8);
-  if (lane == 63) wtot[wv] = incl;
-  __syncthreads();
-  int run = incl - cnt8;
-  for (int w2 = 0; w2 < wv; ++w2) run += wtot[w2];
-#pragma unroll
-  for (int k = 0; k < WPT; ++k) {
-    const int g = WPT * tid + k;
-    um[g] = w8[k];
-    pre[g] = run;
-    run += __builtin_popcountll(w8[k]);
-  }
-  if (tid == kBv2Threads - 1) pre[2048] = run;
-  __syncthreads();
-  const int U = pre[2048];
-  const int e0 = (int)((int64_t)sp * U / S), e1 = (int)((int64_t)(sp + 1) * U / S);
+  // this slice: the union neurons of predictor workgroups [g0, g1), in
+  // ascending order (each workgroup owns a contiguous neuron range)
+  const int g0 = (int)((int64_t)sp * G2 / S), g1 = (int)((int64_t)(sp + 1) * G2 / S);
   // this lane: row rl of each group of eight, chunk c of the block's line
   const int rl = lane >> 3, c = lane & 7, gc = cb * 8 + c;
   const size_t rowb = (size_t)d * sizeof(W);
@@ -879,23 +859,30 @@ __global__ __launch_bounds__(kBv2Threads) void bv2(const BatchArgs a, int G2, in
   float acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-  for (int s0 = e0; s0 < e1; s0 += kBv2Rows) {
-    const int ns = min(kBv2Rows, e1 - s0);
-    // neuron of each entry: the workgroup g holding it (last g with pre[g] <= e),
-    // then the (e - pre[g])-th set bit of its mask
-    __syncthreads();  // the previous sub-slice's rows are read
-    for (int i = tid; i < ns; i += kBv2Threads) {
-      const int e = s0 + i;
-      int lo = 0, hi = G2 - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= e) lo = mid; else hi = mid - 1;
+  for (int gg0 = g0; gg0 < g1; gg0 += kGrp) {
+    const int ng = min(kGrp, g1 - gg0);
+    __syncthreads();  // the previous group's rows are read
+    if (wv == 0) {  // the group's masks and their exclusive prefix counts
+      const uint64_t m = lane < ng ? a.umask[gg0 + lane] : 0ull;
+      const int cnt = __builtin_popcountll(m);
+      const int incl = wave_incl_scan_dpp(cnt);
+      if (lane < kGrp) {
+        um[lane] = m;
+        pre[lane] = incl - cnt;
       }
-      uint64_t w = um[lo];
-      for (int k = e - pre[lo]; k > 0; --k) w &= w - 1;
-      rows[i] = nfirst(lo, a.d_ff, G2) + __builtin_ctzll(w);
+      if (lane == 63) s_ns = incl;
     }
     __syncthreads();
+    // neuron j of workgroup gg0 + w goes to the place of its rank among the
+    // group's selected neurons
+    for (int p = tid; p < ng * 64; p += kBv2Threads) {
+      const int w = p >> 6, j = p & 63;
+      const uint64_t m = um[w];
+      if ((m >> j) & 1ull)
+        rows[pre[w] + __builtin_popcountll(m & ((1ull << j) - 1ull))] = nfirst(gg0 + w, a.d_ff, G2) + j;
+    }
+    __syncthreads();
+    const int ns = s_ns;
     // rows (k NWV + wv) 8 + rl of each pass; a slot past the sub-slice repeats
     // row 0 (in bounds) with weight zero, so a pass has no branches
     for (int p0 = 0; p0 < ns; p0 += kBv2Round * NWV * 8) {
