@@ -24,8 +24,10 @@
 // workgroup) move 64-bit words that carry the value and a 32-bit tag.
 // Writers store them with device-scope relaxed atomics (coherent across the
 // eight XCD L2 caches); readers poll until the tag of the exchange appears,
-// so no cross-XCD fence is needed.  Every record is replicated once per XCD
-// so each replica has 32 readers.  In exchange B only the two mask words are
+// so no cross-XCD fence is needed.  Every record is written to several
+// copies, each read by a fixed share of the workgroups (16 copies of the
+// statistics, 2 of the selection records, one per XCD of the layer output:
+// measured).  In exchange B only the two mask words are
 // polled: the entries are stored before them and read once the mask is seen
 // (an entry still without its tag is polled), which keeps the polling
 // traffic of 256 readers to two words per record.
@@ -45,7 +47,13 @@ namespace spark {
 constexpr int kDecMaxC = 21;   // K1 chunks (16 B) held per streamer thread (a 36 x 1152 bf16 slab)
 constexpr int kStreamers = 256;
 constexpr int kWorkers = 256;
-constexpr int kRep = 8;        // replicas of every broadcast record (one per XCD)
+// Copies of the broadcast records of each exchange; workgroup w reads copy
+// (x + 8 ((w / 8) % 2)) % kRep* with x its XCD (measured: statistics 16
+// copies, 16 readers each; selection records 2, written fastest; the layer
+// output one per XCD)
+constexpr int kRepA = 16;      // statistics
+constexpr int kRepB = 2;       // selection records
+constexpr int kRepC = 8;       // layer output
 constexpr int kCand = 10;      // owned neurons whose K2 dot is formed before theta is known
 constexpr int kRecWords = 16;  // selected-list record: 2 mask words + 14 entries
 constexpr int kRecEntries = kRecWords - 2;
@@ -72,10 +80,10 @@ struct DecodeParams {
   int64_t tr_cap;
   uint64_t* hdr;    // [0]: tag before the next call, [1]: mark (tag0 + 1) of the last failed call, [2]: failed
                     // calls, [3]: bound of every wait when nonzero (test hook)
-  uint64_t* stats;  // kRep x stats_stride: means of all workgroups, then their M2 (kRecRow apart)
-  uint64_t* rec;    // kRep x rec_stride: selected-list record per workgroup
+  uint64_t* stats;  // kRepA x stats_stride: means of all workgroups, then their M2 (kRecRow apart)
+  uint64_t* rec;    // kRepB x rec_stride: selected-list record per workgroup
   uint64_t* ovf;    // G x kOvfWords: list entries past the record
-  uint64_t* ycol;   // kRep x ycol_stride: owned columns of y
+  uint64_t* ycol;   // kRepC x ycol_stride: owned columns of y
   int stats_stride, rec_stride, ycol_stride;
   uint32_t spin_limit;
 };
@@ -514,14 +522,14 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         const float mean_w = wave_sum_dpp(hj) / (float)g.nown;
         const float dv = own ? hj - mean_w : 0.f;
         const float m2_w = wave_sum_dpp(dv * dv);
-        if (lane < kRep) {
+        if (lane < kRepA) {
           uint64_t* dst = p.stats + (size_t)lane * p.stats_stride + w;
           put_tagged(dst, mean_w, tagA);
           put_tagged(dst + kRecRow, m2_w, tagA);
         }
         // every record's two words in one polling loop: the means of all
         // workgroups are contiguous, then their M2 values
-        const uint64_t* src = fresh(p.stats + (size_t)g.rep * p.stats_stride);
+        const uint64_t* src = fresh(p.stats + (size_t)(g.rep % kRepA) * p.stats_stride);
         constexpr int KA = 8;  // 4 records (G <= 256) x 2 words per lane
         const uint64_t* pa[KA];
 #pragma unroll
@@ -559,7 +567,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
         // values follow from wave 1 once the candidates' K2 dots are done (a
         // reader that finds an entry without its tag polls it)
         const uint64_t M = __builtin_amdgcn_ballot_w64(own && hj > theta);
-        if (lane < 2 * kRep) {
+        if (lane < 2 * kRepB) {
           const int rp = lane >> 1;
           put_tagged_u32(p.rec + (size_t)rp * p.rec_stride + (size_t)(lane & 1) * kRecRow + w,
                          (lane & 1) ? (uint32_t)(M >> 32) : (uint32_t)M, tagB);
@@ -618,7 +626,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
           if (on) {
             if (e < kRecEntries) {
 #pragma unroll
-              for (int rp = 0; rp < kRep; ++rp)
+              for (int rp = 0; rp < kRepB; ++rp)
                 put_tagged(p.rec + (size_t)rp * p.rec_stride + (size_t)(2 + e) * kRecRow + w, cval, tagB);
             } else {
               put_tagged(p.ovf + (size_t)w * kOvfWords + (e - kRecEntries), cval, tagB);
@@ -634,7 +642,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       bool okB = true;
       uint64_t Mg = 0;
       if (tid < G) {
-        const uint64_t* recm = fresh(p.rec + (size_t)g.rep * p.rec_stride) + tid;
+        const uint64_t* recm = fresh(p.rec + (size_t)(g.rep % kRepB) * p.rec_stride) + tid;
         const uint64_t* mp[2] = {recm, recm + kRecRow};
         float mv[2];
         okB = gather_tagged2<2>(mp, tagB, mv, p.hdr, S.fmark, S.spin_limit);
@@ -648,7 +656,7 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       // waves in a fixed order.
       {
         const char* vbase = (const char*)tab_v[l] + (size_t)g.ch0 * 16;
-        const uint64_t* recp = fresh(p.rec + (size_t)g.rep * p.rec_stride) + (tid < G ? tid : 0);
+        const uint64_t* recp = fresh(p.rec + (size_t)(g.rep % kRepB) * p.rec_stride) + (tid < G ? tid : 0);
         float acc[2 * CN];
 #pragma unroll
         for (int i = 0; i < 2 * CN; ++i) acc[i] = 0.f;
@@ -729,10 +737,10 @@ __device__ void decode_worker(const DecodeParams& p, const void* const* tab_k2, 
       {
         if (tid < g.ncol)
 #pragma unroll
-          for (int rp = 0; rp < kRep; ++rp) put_tagged(p.ycol + (size_t)rp * p.ycol_stride + g.c0 + tid, ymine, tagC);
+          for (int rp = 0; rp < kRepC; ++rp) put_tagged(p.ycol + (size_t)rp * p.ycol_stride + g.c0 + tid, ymine, tagC);
         bool okC = true;
         float ss = 0.f;
-        const uint64_t* src = fresh(p.ycol + (size_t)g.rep * p.ycol_stride);
+        const uint64_t* src = fresh(p.ycol + (size_t)(g.rep % kRepC) * p.ycol_stride);
         constexpr int KC = 9;
         for (int c00 = 0; okC && c00 < d_model; c00 += kWorkers * KC) {
           const uint64_t* ptrs[KC];
@@ -792,7 +800,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
   g.K2C = (g.d_model - g.r) / CN;
   g.TC = g.nown * g.CK;
   g.ntile = (g.TC + kStreamers * kDecMaxC - 1) / (kStreamers * kDecMaxC);
-  g.rep = xcc_id();
+  g.rep = xcc_id() + 8 * ((g.w >> 3) & 1);
   if (threadIdx.x == 0) {
     S.tag0 = (uint32_t)get_word(p.hdr);
     S.fmark = (uint64_t)S.tag0 + 1;
@@ -840,13 +848,13 @@ static DecodeLayout decode_layout(int64_t d_model, int64_t T, int grid, int n_la
   L.hdr = off;
   off += 256;
   L.stats = off;
-  off += round_up((size_t)kRep * L.stats_stride * 8, 256);
+  off += round_up((size_t)kRepA * L.stats_stride * 8, 256);
   L.rec = off;
-  off += round_up((size_t)kRep * L.rec_stride * 8, 256);
+  off += round_up((size_t)kRepB * L.rec_stride * 8, 256);
   L.ovf = off;
   off += round_up((size_t)grid * kOvfWords * 8, 256);
   L.ycol = off;
-  off += round_up((size_t)kRep * L.ycol_stride * 8, 256);
+  off += round_up((size_t)kRepC * L.ycol_stride * 8, 256);
   L.qbuf = off;
   if (n_layers > kDecodeMaxLayersPerLaunch) off += 2 * round_up((size_t)T * d_model * 4, 256);
   L.total = off;
