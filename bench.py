@@ -114,6 +114,27 @@ def _time_ms(torch, fn, reps=20, warm=3):
     return float(np.median(ts))
 
 
+def _time_b2b_ms(torch, fns, n=20, reps=5, warm=2):
+    """Per-call time in ms on the GPU timeline: n calls issued back to back
+    (cycling through fns) between two HIP events, median over reps.  Unlike
+    _time_ms, the host-side setup of each call (argument marshalling, the
+    first launch) overlaps the GPU work of the previous calls."""
+    for i in range(warm):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fns[i % len(fns)]()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / n)
+    return float(np.median(ts))
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -231,7 +252,10 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
     bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
     layer = tuple(bf(a) for a in lw)
     Q = bf(synth.queries(seed, T, D_MODEL, "bf16"))
-    ms = _time_ms(torch, lambda: sf.spark_ffn_prefill(Q, layer, K, R), reps=10)
+    ms_one = _time_ms(torch, lambda: sf.spark_ffn_prefill(Q, layer, K, R), reps=10)
+    # back to back (each call writes ~420 MB of workspace, which turns the
+    # memory-side cache over by itself)
+    ms = _time_b2b_ms(torch, [lambda: sf.spark_ffn_prefill(Q, layer, K, R)], n=10, reps=5)
     _, ptr = sf.spark_ffn_prefill(Q, layer, K, R, trace=True, cap=1)
     nsel = float(ptr["counts"].double().sum().item())
     flops = 2.0 * T * R * D_FF
@@ -241,7 +265,8 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
     # the gathered form (only the selected K2 and V rows read, per token)
     gath_ms = _time_ms(torch, lambda: sf.spark_ffn_prefill(Q, layer, K, R, gathered=True), reps=5)
     # the predictor product alone (its own entry point), HIP events
-    pred_ms = _time_ms(torch, lambda: sf.spark_ffn_prefill_scores(Q, layer, R), reps=50)
+    pred_ms_one = _time_ms(torch, lambda: sf.spark_ffn_prefill_scores(Q, layer, R), reps=50)
+    pred_ms = _time_b2b_ms(torch, [lambda: sf.spark_ffn_prefill_scores(Q, layer, R)], n=20, reps=5)
     Qr = Q[:, :R].contiguous()
     K1 = layer[0].t().contiguous()  # [r][d_ff]
     ref_ms = _time_ms(torch, lambda: torch.mm(Qr, K1), reps=10)
@@ -250,13 +275,15 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
     # contribute exact zeros): scores, gated K2 values, and C V
     dense = 2.0 * T * D_FF * (R + (D_MODEL - R) + D_MODEL)
     res["prefill"] = {"workload": "4096 tokens, one 2304 x 9216 layer (r 1152, k 737), bf16", "ms": ms,
+                      "ms_one_call": ms_one,
                       "tokens_per_s": T / ms * 1e3, "us_per_token": ms * 1e3 / T, "mean_selected": nsel / T,
                       "method_gflop": method / 1e9, "dense_products_gflop": dense / 1e9,
                       "roofline": {"bound": "mfma", "achieved": method / ms / 1e9, "peak": MFMA_BF16_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": method / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
                                    "note": "the method's FLOPs (2 T r d_ff + 2 sum_t |S_t| (d_model - r + d_model)) "
-                                           "over the whole call"},
-                      "predictor_gemm": {"us": pred_ms * 1e3, "gflop": flops / 1e9,
+                                           "over the whole call (calls back to back; 'ms_one_call' is one call "
+                                           "timed alone, host-side setup included)"},
+                      "predictor_gemm": {"us": pred_ms * 1e3, "us_one_call": pred_ms_one * 1e3, "gflop": flops / 1e9,
                                          "roofline": {"bound": "mfma", "achieved": flops / pred_ms / 1e9,
                                                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                                       "frac": flops / pred_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}},
@@ -283,14 +310,26 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
         ws = torch.zeros(need.value, dtype=torch.uint8, device=dev)  # zero-filled before its first use
         o2 = torch.empty((8, 256), device=dev)
         c2 = torch.empty(8, dtype=torch.int32, device=dev)
-        call = lambda: L.spark_attn_decode(*[sf._p(a) for a in args], 8, 4, n, 256, 128, 256, sf._p(o2), sf._p(c2),
-                                           None, 0, None, sf._p(ws), need.value, sf._stream(dev))
-        ms = _time_ms(torch, call, reps=50)
+        mk = lambda kv: (lambda: L.spark_attn_decode(*[sf._p(a) for a in [args[0]] + kv], 8, 4, n, 256, 128, 256,
+                                                     sf._p(o2), sf._p(c2), None, 0, None, sf._p(ws), need.value,
+                                                     sf._stream(dev)))
+        ms = _time_ms(torch, mk(args[1:]), reps=50)
+        # back to back over copies of the cache whose total (> 512 MB) exceeds
+        # the memory-side cache, so every call reads its cache from HBM
+        cache_bytes = sum(a.numel() * 2 for a in args[1:])
+        ncopy = max(2, -(-(512 << 20) // cache_bytes))
+        copies = [[a.clone() for a in args[1:]] for _ in range(ncopy)]
+        ms_b2b = _time_b2b_ms(torch, [mk(kv) for kv in copies], n=max(20, 2 * ncopy), reps=7)
+        del copies
+        torch.cuda.empty_cache()
         c = cnt.double().sum().item()
         moved = 4 * n * 128 * 2 + c * (128 + 256) * 2 + 8 * 256 * 2
-        att[str(n)] = {"us": ms * 1e3, "mean_attended": c / 8, "algorithmic_bytes": moved,
-                       "roofline": {"bound": "hbm", "achieved": moved / ms / 1e6, "peak": HBM_PEAK_GBS,
-                                    "unit": "GB/s", "frac": moved / ms / 1e6 / HBM_PEAK_GBS}}
+        att[str(n)] = {"us": ms * 1e3, "us_back_to_back_cold": ms_b2b * 1e3, "cache_copies": ncopy,
+                       "mean_attended": c / 8, "algorithmic_bytes": moved,
+                       "roofline": {"bound": "hbm", "achieved": moved / ms_b2b / 1e6, "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": moved / ms_b2b / 1e6 / HBM_PEAK_GBS,
+                                    "note": "calls back to back over cache copies that do not fit the memory-side "
+                                            "cache; 'us' is one call timed alone, host-side setup included"}}
         if with_cpu:
             att[str(n)]["cpu_baseline"] = _oracle_rate(lambda: oracle.spark_attn_decode(qb, k1b, k2b, vb, 256), 1,
                                                        "steps/s", f"one decode step at n_ctx {n}")
@@ -300,15 +339,26 @@ def extra_workloads(torch, sf, synth, dev, seed, with_cpu):
     qp, k1p, k2p, vp = synth.attn_prefill_inputs(seed, Tp, 8, 4, 256, 128)
     pargs = [bf(a) for a in (qp, k1p, k2p, vp)]
     po, pc, _, _ = sf.spark_attn_prefill(*pargs, 256)
-    ms = _time_ms(torch, lambda: sf.spark_attn_prefill(*pargs, 256), reps=10)
+    ms_one = _time_ms(torch, lambda: sf.spark_attn_prefill(*pargs, 256), reps=10)
+    # back to back over copies of the inputs (> 512 MB in all: none is found in
+    # the memory-side cache)
+    in_bytes = sum(a.numel() * 2 for a in pargs)
+    ncopy = max(2, -(-(512 << 20) // in_bytes))
+    pcopies = [[a.clone() for a in pargs] for _ in range(ncopy)]
+    ms = _time_b2b_ms(torch, [(lambda c=c: sf.spark_attn_prefill(*c, 256)) for c in pcopies], n=2 * ncopy, reps=3)
+    del pcopies
+    torch.cuda.empty_cache()
     flops = 2.0 * 8 * (Tp * (Tp + 1) / 2) * (128 + 128 + 256)  # causal S, gated K2 scores, W V
     res["attention_prefill"] = {
         "workload": "4096-position prompt, Hq 8, Hkv 4, hd 256, r 128, k_attn 256, causal", "ms": ms,
+        "ms_one_call": ms_one, "input_copies": ncopy,
         "positions_per_s": Tp / ms * 1e3, "mean_attended": float(pc.double().mean().item()),
         "roofline": {"bound": "mfma", "achieved": flops / ms / 1e9, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
                      "note": "algorithmic causal products (scores, gate products, weights x V) over the "
-                             "whole call; the moments pass recomputes the scores and is not counted"}}
+                             "whole call (calls back to back over input copies; 'ms_one_call' is one call timed "
+                             "alone, host-side setup included); the moments pass recomputes the scores and is "
+                             "not counted"}}
     if with_cpu:
         qs, k1s, k2s, vs = synth.attn_prefill_inputs(seed, 512, 8, 4, 256, 128)
         res["attention_prefill"]["cpu_baseline"] = _oracle_rate(
