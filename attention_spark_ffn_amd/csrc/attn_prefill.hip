@@ -34,9 +34,7 @@ namespace spark {
 // Abramowitz and Stegun 26.2.23 (error below 4.5e-4) by Newton steps on
 // erfc(w / sqrt 2) / 2 = tt, which converge monotonically (the tail is convex
 // for w >= 0) and reach double precision in three.
-__global__ void z_table(int k, int T, float* __restrict__ z) {
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n > T) return;
+__device__ __forceinline__ void z_entry(int k, int n, float* __restrict__ z) {
   if (n <= k) {
     z[n] = 0.f;
     return;
@@ -53,6 +51,10 @@ __global__ void z_table(int k, int T, float* __restrict__ z) {
     w += (0.5 * erfc(w * 0.7071067811865476) - tt) / pdf;
   }
   z[n] = (float)(upper ? w : -w);
+}
+__global__ void z_table(int k, int T, float* __restrict__ z) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n <= T) z_entry(k, n, z);
 }
 
 // Fixed-order sum / max over the 256 threads.
@@ -754,10 +756,18 @@ __global__ __launch_bounds__(kFusedThreads2) void attn_prefill_fused(const Fused
 
 // vt[g][c][j] = v[g][j][c] for j < T and 0 for T <= j < LT, all KV heads in
 // one launch: 64 x 64 tiles through LDS, 16-byte loads and stores.
+// The last z-slice of the grid (blockIdx.z == Hkv) fills the threshold table
+// z[0..T] instead (z_table's entries; the grid has at least 4 LT >= T + 1
+// threads per slice), so the fused path needs no launch of its own for it.
 __global__ __launch_bounds__(256) void transpose_v(const bf16_t* __restrict__ v, int T, int HD, int LT,
-                                                   bf16_t* __restrict__ vt) {
+                                                   bf16_t* __restrict__ vt, int Hkv, int k, float* __restrict__ z) {
   __shared__ bf16_t tile[64][72];  // [key][dim]
   const int g = blockIdx.z, j0 = blockIdx.x * 64, c0 = blockIdx.y * 64, tid = threadIdx.x;
+  if (g == Hkv) {
+    const int n = (blockIdx.y * gridDim.x + blockIdx.x) * 256 + tid;
+    if (n <= T) z_entry(k, n, z);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int e = tid + 256 * i, key = e >> 3, cc = e & 7;
@@ -866,12 +876,11 @@ static hipError_t attn_prefill_main(const void* q, const void* k1, const void* k
   const int Ti = (int)T, H = (int)Hq, G = (int)(Hq / Hkv), D = (int)hd, R = (int)r, RC = (int)(hd - r);
   const int LT = (Ti + 7) & ~7;  // row stride of S, W and V^T: 16-byte aligned rows
   const bf16_t* Q = (const bf16_t*)q;
-  hipLaunchKernelGGL(z_table, dim3((unsigned)((T + 1 + 255) / 256)), dim3(256), 0, st, (int)k_attn, Ti, ztab);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if (attn_prefill_fused_ok(hd, r)) {
-    hipLaunchKernelGGL(transpose_v, dim3((unsigned)((LT + 63) / 64), (unsigned)((hd + 63) / 64), (unsigned)Hkv),
-                       dim3(256), 0, st, (const bf16_t*)v, Ti, D, LT, Vt);
+    // V^T for the fused kernel, and (one more grid slice) the threshold table
+    hipLaunchKernelGGL(transpose_v, dim3((unsigned)((LT + 63) / 64), (unsigned)((hd + 63) / 64), (unsigned)(Hkv + 1)),
+                       dim3(256), 0, st, (const bf16_t*)v, Ti, D, LT, Vt, (int)Hkv, (int)k_attn, ztab);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     FusedArgs a;
@@ -901,6 +910,10 @@ static hipError_t attn_prefill_main(const void* q, const void* k1, const void* k
       default: return launch_fused_t<128>(a, st);
     }
   }
+  // 0. the threshold table
+  hipLaunchKernelGGL(z_table, dim3((unsigned)((T + 1 + 255) / 256)), dim3(256), 0, st, (int)k_attn, Ti, ztab);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   // 1. scores
   {
     GemmArgs a = gemm_args(Q, H * D, (const bf16_t*)k1, R, S, LT, Ti, Ti, R);
