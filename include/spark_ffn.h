@@ -202,7 +202,9 @@ int64_t spark_ffn_decode_tags(int n_layers, int64_t T);
  * while they run (bf16 weights, r and d_model - r multiples of 32 and at most
  * 1280, d_ff at most 256 x 40, and a grid the device holds at once), else a
  * predictor kernel and a gate kernel; then the V product (plus one kernel
- * when a trace is asked for).
+ * when a trace is asked for).  After the exchanging kernel the V product sums
+ * its slices itself, through tagged words in the workspace under the same
+ * layer tag; otherwise one more kernel sums them.
  * Requires 0 <= B <= 8, d_model <= 8192, d_ff <= 65536,
  * P * max(r, d_model - r) * 4 <= 65536 with P = B rounded up to a power of
  * two, q and y 16-byte aligned, and the weight conditions of
