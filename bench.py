@@ -379,6 +379,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (scale for HBM byte counters)")
+    ap.add_argument("--predictor-gemm", type=int, default=0, metavar="N",
+                    help="only run the prefill predictor product (4096 x 1152 x 9216, bf16) N times "
+                         "(for matrix-core counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the decode path is a single-GPU kernel); got --gpus {args.gpus}",
@@ -399,6 +402,15 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4, "launches": 5}))
+        return
+    if args.predictor_gemm:
+        bf = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        layer = tuple(bf(x) for x in synth.ffn_layer(args.seed, 0, D_MODEL, D_FF, R, "bf16"))
+        Q = bf(synth.queries(args.seed, 4096, D_MODEL, "bf16"))
+        ms = _time_b2b_ms(torch, [lambda: sf.spark_ffn_prefill_scores(Q, layer, R)], n=args.predictor_gemm, reps=1)
+        flops = 2.0 * 4096 * R * D_FF
+        print(json.dumps({"predictor_gemm_us": ms * 1e3, "calls": args.predictor_gemm + 2, "gflop_per_call": flops / 1e9,
+                          "tflops": flops / ms / 1e9}))
         return
     t0 = time.perf_counter()
     layers_np = synth.ffn_stack(args.seed, LAYERS, D_MODEL, D_FF, R, "bf16", workers=16)
