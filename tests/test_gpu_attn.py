@@ -39,7 +39,7 @@ def run_attn(Hq, Hkv, n, hd, r, ka, seed, tol=2e-2, scale=None):
 
 @pytest.mark.parametrize("n", [4096, 32768])
 def test_attn_config(n):
-    """BASELINE's attention workload: 8 query heads on 4 KV heads, hd 256,
+    """The attention decode workload: 8 query heads on 4 KV heads, hd 256,
     r 128, k_attn 256, Q/K/V ~ N(0,1)/16 in bf16."""
     counts = run_attn(8, 4, n, 256, 128, 256, 0)
     assert np.all(np.abs(counts - 256) <= 256 * 0.5)

@@ -78,7 +78,7 @@ def run_stack(layers_np, q0, r, k, eps=1e-6, tol=1e-4, check_layers=None, fn=Non
 
 
 def test_decode_tiny_fp32_config():
-    """BASELINE's tiny Spark FFN layer: d_model 256, d_ff 1024, r 128, k 82, fp32, 16 tokens."""
+    """The tiny Spark FFN layer: d_model 256, d_ff 1024, r 128, k 82, fp32, 16 tokens."""
     layers = [synth.ffn_layer(0, 0, 256, 1024, 128, "f32")]
     q0 = synth.queries(0, 16, 256)
     run_stack(layers, q0, 128, 82, tol=1e-4)
@@ -98,7 +98,7 @@ def test_decode_shapes(dm, dff, r, k, L, T, dt):
 
 
 def test_decode_full_stack_config():
-    """BASELINE's decode workload: 26 layers of 2304 x 9216, r 1152, k 737, bf16
+    """The decode workload: 26 layers of 2304 x 9216, r 1152, k 737, bf16
     weights, fp32 q, RMS normalisation between layers; 2 tokens, every layer
     teacher-forced against the oracle, and the whole chain."""
     L = 26

@@ -35,7 +35,7 @@ def run_prefill(dm, dff, r, k, T, seed, sample=None, tol=2e-2, gathered=False):
 
 
 def test_prefill_config():
-    """BASELINE's prefill workload: 4096 tokens through one 2304 x 9216 layer
+    """The prefill workload: 4096 tokens through one 2304 x 9216 layer
     (r 1152, k 737), bf16; a sample of 96 tokens against the oracle, spread
     over every 128-row tile of the predictor GEMM."""
     T = 4096
